@@ -1,0 +1,165 @@
+/*
+ * moe_lora.h -- C ABI of the MI355X (gfx950) MoE-LoRA hot path.
+ *
+ * Two operations, both hand-written HIP kernels:
+ *
+ *   moe_lora_align  -- per LoRA slot, group the routed (token, k) pairs by
+ *                      expert and pad every group to block_m (vLLM PR #29257
+ *                      "Lora MoE Align Improvements", Purpose).
+ *   fused_moe_lora  -- Y[m,k,:] (+)= (X[m] A[s,l,e]^T) B[s,l,e]^T per slice s,
+ *                      with l = token_lora_mapping[m], e = topk_ids[m,k], the
+ *                      rank-r vector kept on chip, optional routed weight
+ *                      (prhub summary of vLLM PR #42290, implementation
+ *                      steps and key source fragment).
+ *
+ * Conventions for every call below:
+ *   - Pointers marked [device] are device (HBM) addresses; the caller owns
+ *     and allocates every buffer.  The library allocates no memory, keeps no
+ *     pointer after a call returns, and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it asynchronously; results are visible to later work on that stream.
+ *   - All index arrays are int32 (a type mismatch on token_lora_mapping was
+ *     flagged as undefined behaviour in the review of PR #29257).
+ *   - Arguments are validated on the host before any HIP call.  A negative
+ *     status means nothing was launched and no output was written.
+ *   - M = 0 is valid: moe_lora_align still writes every slot's metadata
+ *     (all slots empty), fused_moe_lora returns MOE_LORA_OK at once.
+ *   - Calls on different streams may overlap if their outputs are disjoint.
+ *
+ * Limits: 1 <= E <= 1024 (the expert limit asked for in the review of PR
+ * #29257), 1 <= L <= 1024, L*E <= 8192, block_m in {16, 32, 64, 128},
+ * 1 <= r <= 128 (the one-shot kernel's compile-time rank bound in the prhub
+ * summary of PR #42290, here an error code instead of an assert),
+ * M*topk + min(E, M*topk)*(block_m-1) < 2^31 and L * capacity < 2^31.
+ */
+#ifndef MOE_LORA_H
+#define MOE_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_LORA_API __attribute__((visibility("default")))
+#else
+#define MOE_LORA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_lora_status {
+    MOE_LORA_OK = 0,
+    MOE_LORA_ERR_INVALID = -1,     /* null pointer, negative size, bad flag,
+                                      misaligned pointer, K or Ns not % 8   */
+    MOE_LORA_ERR_UNSUPPORTED = -2, /* outside the limits listed above       */
+    MOE_LORA_ERR_WORKSPACE = -3,   /* align workspace smaller than needed   */
+    MOE_LORA_ERR_HIP = -4          /* a HIP launch or query failed          */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+MOE_LORA_API const char *moe_lora_status_string(int status);
+
+/*
+ * Row length `cap` of each slot in sorted_token_ids:
+ *     round_up(numel + min(E, numel) * (block_m - 1), block_m),
+ * numel = M * topk.  No slot can need more: each non-empty expert group adds
+ * at most block_m - 1 padding entries.  expert_ids rows hold cap / block_m
+ * entries.  Returns a negative status for invalid sizes.  Host only.
+ */
+MOE_LORA_API int64_t moe_lora_align_capacity(int64_t M, int32_t topk, int32_t E, int32_t block_m);
+
+/*
+ * Bytes of device workspace moe_lora_align needs for these sizes (0 when
+ * the single-workgroup path is taken).  Returns a negative status for
+ * invalid sizes.  Host only.
+ */
+MOE_LORA_API int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int32_t E,
+                                       int32_t L, int32_t block_m);
+
+/*
+ * moe_lora_align -- the align step (vLLM PR #29257, Purpose: an LDS variant
+ * for few experts and a global-memory variant for many; one routine serves
+ * the LoRA case and, with L = 1 and a zero mapping, the plain MoE case).
+ *
+ * Inputs  [device]:
+ *   topk_ids            int32 [M, topk]   expert of pair p = m*topk + k
+ *   token_lora_mapping  int32 [M]         slot of token m; -1 = no adapter
+ * Outputs [device]:
+ *   sorted_token_ids    int32 [L, cap]    slot l's row: for each expert e in
+ *                       ascending order, the pairs p with (l, e) in ascending
+ *                       p, then the sentinel numel = M*topk up to a multiple
+ *                       of block_m.  Entries from num_tokens_post_padded[l]
+ *                       to cap are not written.
+ *   expert_ids          int32 [L, cap/block_m]  expert of each block of
+ *                       block_m entries in that row (entries past the slot's
+ *                       blocks are not written).
+ *   num_tokens_post_padded int32 [L]      padded length of each slot's row.
+ *   lora_ids            int32 [L] or NULL the slots with at least one pair,
+ *                       ascending, then -1 (the active-slot list of vLLM PR
+ *                       #32005).
+ *   num_active_loras    int32 [1] or NULL how many slots are active.
+ *   workspace           [device] scratch of moe_lora_align_workspace_bytes()
+ *                       bytes (may be NULL when that is 0); contents on entry
+ *                       do not matter.
+ * Pairs whose slot is outside [0, L) (including -1) or whose expert is
+ * outside [0, E) are skipped; nothing traps on device.  The result does not
+ * depend on thread timing: the same inputs give the same bytes.
+ */
+MOE_LORA_API int moe_lora_align(const int32_t *topk_ids, const int32_t *token_lora_mapping,
+                   int64_t M, int32_t topk, int32_t E, int32_t L,
+                   int32_t block_m, int32_t *sorted_token_ids,
+                   int32_t *expert_ids, int32_t *num_tokens_post_padded,
+                   int32_t *lora_ids, int32_t *num_active_loras,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Kernel choice for fused_moe_lora. */
+enum moe_lora_variant {
+    MOE_LORA_VARIANT_AUTO = 0, /* chosen from the expected rows per block */
+    MOE_LORA_VARIANT_VALU = 1, /* vector loads + wavefront reductions     */
+    MOE_LORA_VARIANT_MFMA = 2  /* LDS-staged bf16 MFMA tiles              */
+};
+
+/*
+ * fused_moe_lora -- shrink and expand in one kernel, the rank-r vector
+ * never leaving the chip (prhub summary of vLLM PR #42290; slices and the
+ * routed weight as in the fused_moe_lora signature of the PR #32005 diff).
+ *
+ * For every valid pair p = m*topk + k in the align outputs, with its slot l
+ * (the row of sorted_token_ids it sits in) and expert e (its block's
+ * expert_ids entry), and every slice s < S:
+ *     v[j] = sum_t X[row, t] * A[s,l,e,j,t]      row = p if x_per_pair else m
+ *     d[n] = sum_j v[j] * B[s,l,e,n,j]           (fp32 accumulation)
+ *     d[n] *= topk_weights[p]                    if mul_routed_weight
+ *     Y[p, s*Ns+n] = bf16(add_inputs ? Y[p, s*Ns+n] + d[n] : d[n])  (RNE)
+ * Rows of pairs that are in no slot are not touched.
+ *
+ * Inputs  [device]:
+ *   x          bf16 [M, K], or [M*topk, K] when x_per_pair (w2-style input)
+ *   lora_a     bf16 [S, L, E, r, K]
+ *   lora_b     bf16 [S, L, E, Ns, r]
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded: as produced by
+ *              moe_lora_align for the same M, topk, E, L, block_m.
+ *   topk_weights fp32 [M, topk]; may be NULL when mul_routed_weight == 0.
+ * In/out [device]:
+ *   y          bf16 [M, topk, S*Ns]
+ * x, lora_a, lora_b and y must be 16-byte aligned; K and Ns multiples of 8.
+ * The grid covers only blocks of active slots: a workgroup finds its slot
+ * from num_tokens_post_padded, and the launch size depends on M alone, not
+ * on how many slots are active.  Results are deterministic (no atomics).
+ * `variant` is a moe_lora_variant; both kernels compute the same function.
+ */
+MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
+                   const uint16_t *lora_a, const uint16_t *lora_b,
+                   const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                   const int32_t *num_tokens_post_padded,
+                   const float *topk_weights, int32_t mul_routed_weight,
+                   int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, uint16_t *y, int32_t variant, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H */

@@ -1,0 +1,189 @@
+"""MI355X-native MoE-LoRA hot path: Python binding of libmoelora.so.
+
+The binding only marshals arguments: every step of the path runs in the HIP
+kernels behind the C ABI declared in include/moe_lora.h.  PyTorch provides
+device memory and the current stream.  If the library is not built the calls
+raise; there is no fallback implementation.
+
+    out = moe_lora_align(topk_ids, token_lora_mapping, E, L, block_m)
+    fused_moe_lora(x, lora_a, lora_b, out, topk_weights, y,
+                   mul_routed_weight=..., add_inputs=..., x_per_pair=...)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoelora.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+VARIANTS = {"auto": VARIANT_AUTO, "valu": VARIANT_VALU, "mfma": VARIANT_MFMA}
+
+# symbol -> (restype, argtypes); mirrors include/moe_lora.h
+_P = ctypes.c_void_p
+_I32, _I64 = ctypes.c_int32, ctypes.c_int64
+SIGNATURES = {
+    "moe_lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_lora_align_capacity": (_I64, [_I64, _I32, _I32, _I32]),
+    "moe_lora_align_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_lora_align": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                      _P, _P, _P, _I64, _P]),
+    "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                      _I32, _P]),
+}
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH) -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m moe_lora_adapter_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_lora_status_string(int(status)).decode()
+
+
+def align_capacity(M: int, topk: int, E: int, block_m: int) -> int:
+    v = lib().moe_lora_align_capacity(M, topk, E, block_m)
+    if v < 0:
+        raise MoeLoraError(v, "moe_lora_align_capacity")
+    return int(v)
+
+
+def align_workspace_bytes(M: int, topk: int, E: int, L: int, block_m: int) -> int:
+    v = lib().moe_lora_align_workspace_bytes(M, topk, E, L, block_m)
+    if v < 0:
+        raise MoeLoraError(v, "moe_lora_align_workspace_bytes")
+    return int(v)
+
+
+@dataclass
+class AlignOutput:
+    sorted_token_ids: "object"        # int32 [L, cap]
+    expert_ids: "object"              # int32 [L, cap // block_m]
+    num_tokens_post_padded: "object"  # int32 [L]
+    lora_ids: "object"                # int32 [L]
+    num_active_loras: "object"        # int32 [1]
+    block_m: int
+    cap: int
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def alloc_align_output(M, topk, E, L, block_m, device):
+    import torch
+    cap = align_capacity(M, topk, E, block_m)
+    i32 = dict(dtype=torch.int32, device=device)
+    return AlignOutput(torch.empty((L, cap), **i32), torch.empty((L, cap // block_m), **i32),
+                       torch.empty(L, **i32), torch.empty(L, **i32), torch.empty(1, **i32),
+                       block_m, cap)
+
+
+def moe_lora_align(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *,
+                   out: AlignOutput | None = None, workspace=None, stream=None) -> AlignOutput:
+    """Group the (token, k) pairs of every LoRA slot by expert; see moe_lora.h."""
+    import torch
+    dev = topk_ids.device
+    _check(topk_ids, "topk_ids", torch.int32, dev)
+    _check(token_lora_mapping, "token_lora_mapping", torch.int32, dev)
+    if topk_ids.dim() != 2 or token_lora_mapping.shape != (topk_ids.shape[0],):
+        raise ValueError("topk_ids must be [M, topk] and token_lora_mapping [M]")
+    M, topk = topk_ids.shape
+    if out is None:
+        out = alloc_align_output(M, topk, E, L, block_m, dev)
+    ws_bytes = align_workspace_bytes(M, topk, E, L, block_m)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = lib().moe_lora_align(
+        _dptr(topk_ids), _dptr(token_lora_mapping), M, topk, E, L, block_m,
+        _dptr(out.sorted_token_ids), _dptr(out.expert_ids), _dptr(out.num_tokens_post_padded),
+        _dptr(out.lora_ids), _dptr(out.num_active_loras), _dptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "moe_lora_align")
+    return out
+
+
+def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
+                   mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
+                   variant: str | int = "auto", stream=None):
+    """Y (+)= (X A^T) B^T per routed pair and slice, in place on y; see moe_lora.h."""
+    import torch
+    dev = y.device
+    _check(x, "x", torch.bfloat16, dev)
+    _check(lora_a, "lora_a", torch.bfloat16, dev)
+    _check(lora_b, "lora_b", torch.bfloat16, dev)
+    _check(y, "y", torch.bfloat16, dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, dev)
+    if lora_a.dim() != 5 or lora_b.dim() != 5 or y.dim() != 3:
+        raise ValueError("lora_a [S,L,E,r,K], lora_b [S,L,E,Ns,r], y [M,topk,S*Ns]")
+    S, L, E, r, K = lora_a.shape
+    Ns = lora_b.shape[3]
+    if tuple(lora_b.shape) != (S, L, E, Ns, r):
+        raise ValueError("lora_b shape does not match lora_a")
+    M, topk, N = y.shape
+    if N != S * Ns:
+        raise ValueError("y's last dim must be S*Ns")
+    rows = M * topk if x_per_pair else M
+    if tuple(x.shape) != (rows, K):
+        raise ValueError(f"x must be [{rows}, {K}]")
+    if topk_weights is not None and tuple(topk_weights.shape) != (M, topk):
+        raise ValueError("topk_weights must be [M, topk]")
+    if align.sorted_token_ids.shape[0] != L:
+        raise ValueError("align output was made for another L")
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    rc = lib().fused_moe_lora(
+        _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
+        _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
+        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
+        align.block_m, _dptr(y), v, _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "fused_moe_lora")
+    return y

@@ -1,0 +1,257 @@
+// Align step on gfx950: per LoRA slot, bucket the (token, k) pairs by expert,
+// pad each bucket to block_m, in canonical order (ascending pair index inside
+// a bucket, ascending expert per slot).
+//
+// The pages (vLLM PR #29257 "Lora MoE Align Improvements", Purpose) keep a
+// shared-memory variant for few experts and add a global-memory variant for
+// many.  Here the split is by problem size instead:
+//   * small problems: ONE workgroup does histogram, scan, layout and scatter
+//     with every table in LDS (one launch: decode batches are latency bound);
+//   * large problems: tiles of pairs over many workgroups; each tile keeps its
+//     per-wave histograms in LDS and only its per-key totals go to global
+//     memory, followed by a per-key scan over tiles, one layout workgroup and a
+//     tile scatter.
+// Both paths are deterministic: a pair's position is its group's start plus
+// the number of earlier pairs of the same group, found by wavefront votes on
+// the key bits (no atomics decide an order).
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mlr {
+
+constexpr int kLdsInts = 16384;  // 64 KiB of LDS per workgroup
+
+__device__ __forceinline__ int pair_key(const AlignParams& a, int p) {
+  const int m = p / a.topk;
+  const int l = a.mapping[m];
+  const int e = a.topk_ids[p];
+  return (unsigned(l) < unsigned(a.L) && unsigned(e) < unsigned(a.E)) ? l * a.E + e : -1;
+}
+
+// One wavefront counts pairs [s0, s1) into row[key] (LDS).
+__device__ void count_segment(const AlignParams& a, int s0, int s1, int* row) {
+  for (int base = s0; base < s1; base += kWave) {
+    const int p = base + lane_id();
+    if (p < s1) {
+      const int key = pair_key(a, p);
+      if (key >= 0) atomicAdd(&row[key], 1);
+    }
+  }
+}
+
+// One wavefront places pairs [s0, s1).  row[key] holds the position of the
+// next pair of that key; the lowest lane of each equal-key set advances it.
+__device__ void scatter_segment(const AlignParams& a, int s0, int s1, int* row) {
+  const int lane = lane_id();
+  for (int base = s0; base < s1; base += kWave) {
+    const int p = base + lane;
+    const int key = p < s1 ? pair_key(a, p) : -1;
+    const uint64_t valid = __ballot(key >= 0);
+    if (valid == 0) continue;
+    const uint64_t peers = match_key(key, valid, a.nbits);
+    if (key >= 0) {
+      const uint64_t below = peers & lanes_below(lane);
+      const int pos = row[key] + __popcll(below);
+      const int l = key / a.E;
+      a.sorted[l * a.cap + pos] = p;
+      if (below == 0) row[key] = pos + __popcll(peers);
+    }
+  }
+}
+
+// From per-key pair counts: padded group starts (within the slot) in off[],
+// slot starts in sb[0..L], and the outputs num_tokens_post_padded,
+// expert_ids, padding sentinels, lora_ids and num_active.  All threads of the
+// workgroup call it (barriers inside).  tot may live in LDS or global memory.
+__device__ void layout_groups(const AlignParams& a, const int* tot, int* off, int* sb,
+                              int* wtot) {
+  const int tid = threadIdx.x;
+  for (int key = tid; key < a.LE; key += blockDim.x) {
+    const int c = tot[key];
+    off[key] = (c + a.B - 1) / a.B * a.B;
+  }
+  __syncthreads();
+  const int total = block_excl_scan(off, a.LE, wtot);
+  for (int l = tid; l <= a.L; l += blockDim.x) sb[l] = l < a.L ? off[l * a.E] : total;
+  __syncthreads();
+  for (int key = tid; key < a.LE; key += blockDim.x) {
+    const int l = key / a.E, e = key - l * a.E;
+    const int o = off[key] - sb[l];
+    const int c = tot[key];
+    const int P = (c + a.B - 1) / a.B * a.B;
+    int32_t* srow = a.sorted + l * a.cap;
+    int32_t* erow = a.eids + l * a.nb;
+    for (int blk = o / a.B; blk < (o + P) / a.B; ++blk) erow[blk] = e;
+    for (int i = o + c; i < o + P; ++i) srow[i] = a.numel;
+  }
+  __syncthreads();
+  for (int key = tid; key < a.LE; key += blockDim.x) off[key] -= sb[key / a.E];
+  for (int l = tid; l < a.L; l += blockDim.x) a.ntpp[l] = sb[l + 1] - sb[l];
+  if (wave_id() == 0 && (a.lora_ids || a.nact)) {
+    const int lane = lane_id();
+    int run = 0;
+    for (int c0 = 0; c0 < a.L; c0 += kWave) {
+      const int l = c0 + lane;
+      const bool act = l < a.L && sb[l + 1] > sb[l];
+      const uint64_t mk = __ballot(act);
+      if (act && a.lora_ids) a.lora_ids[run + __popcll(mk & lanes_below(lane))] = l;
+      run += __popcll(mk);
+    }
+    if (a.lora_ids)
+      for (int i = run + lane; i < a.L; i += kWave) a.lora_ids[i] = -1;
+    if (a.nact && lane == 0) *a.nact = run;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- one workgroup
+__global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
+  extern __shared__ int smem[];
+  int* cnt = smem;                // [W][LE]: wave histograms, then positions
+  int* tot = cnt + a.W * a.LE;    // [LE]
+  int* off = tot + a.LE;          // [LE]
+  int* sb = off + a.LE;           // [L + 1]
+  int* wtot = sb + a.L + 1;       // [17]
+  const int tid = threadIdx.x, w = wave_id();
+  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int s0 = w * a.seg, s1 = min(a.numel, s0 + a.seg);
+  if (w < a.W) count_segment(a, s0, s1, cnt + w * a.LE);
+  __syncthreads();
+  for (int key = tid; key < a.LE; key += blockDim.x) {
+    int run = 0;
+    for (int q = 0; q < a.W; ++q) {
+      const int c = cnt[q * a.LE + key];
+      cnt[q * a.LE + key] = run;
+      run += c;
+    }
+    tot[key] = run;
+  }
+  __syncthreads();
+  layout_groups(a, tot, off, sb, wtot);
+  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] += off[i % a.LE];
+  __syncthreads();
+  if (w < a.W) scatter_segment(a, s0, s1, cnt + w * a.LE);
+}
+
+// ---------------------------------------------------------------- tiles
+__global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
+  extern __shared__ int smem[];
+  int* cnt = smem;  // [W][LE]
+  const int tid = threadIdx.x, w = wave_id(), t = blockIdx.x;
+  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
+  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE);
+  __syncthreads();
+  for (int key = tid; key < a.LE; key += blockDim.x) {
+    int sum = 0;
+    for (int q = 0; q < a.W; ++q) sum += cnt[q * a.LE + key];
+    a.tile_cnt[t * a.LE + key] = sum;
+  }
+}
+
+// Per key: exclusive prefix of the tile counts over tiles, and the total.
+__global__ void __launch_bounds__(256) align_tile_prefix_kernel(AlignParams a) {
+  const int key = blockIdx.x * blockDim.x + threadIdx.x;
+  if (key >= a.LE) return;
+  int run = 0;
+#pragma unroll 8
+  for (int t = 0; t < a.ntiles; ++t) {
+    int* c = a.tile_cnt + t * a.LE + key;
+    const int v = *c;
+    *c = run;
+    run += v;
+  }
+  a.key_tot[key] = run;
+}
+
+__global__ void __launch_bounds__(1024) align_meta_kernel(AlignParams a) {
+  extern __shared__ int smem[];
+  int* off = smem;            // [LE]
+  int* sb = off + a.LE;       // [L + 1]
+  int* wtot = sb + a.L + 1;   // [17]
+  layout_groups(a, a.key_tot, off, sb, wtot);
+  for (int key = threadIdx.x; key < a.LE; key += blockDim.x) a.key_off[key] = off[key];
+}
+
+__global__ void __launch_bounds__(1024) align_tile_scatter_kernel(AlignParams a) {
+  extern __shared__ int smem[];
+  int* cnt = smem;  // [W][LE]
+  const int tid = threadIdx.x, w = wave_id(), t = blockIdx.x;
+  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
+  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE);
+  __syncthreads();
+  for (int key = tid; key < a.LE; key += blockDim.x) {
+    int run = a.key_off[key] + a.tile_cnt[t * a.LE + key];
+    for (int q = 0; q < a.W; ++q) {
+      const int c = cnt[q * a.LE + key];
+      cnt[q * a.LE + key] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (s0 < s1) scatter_segment(a, s0, s1, cnt + w * a.LE);
+}
+
+// ---------------------------------------------------------------- host
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+AlignPlan plan_align(int64_t numel, int E, int L, int B) {
+  (void)B;
+  AlignPlan pl{};
+  const int64_t LE = int64_t(L) * E;
+  const int64_t fixed = 2 * LE + L + 1 + 17;
+  const int64_t wmax_single = (kLdsInts - fixed) / LE;
+  if (numel <= 4096 && wmax_single >= 1) {
+    pl.single = true;
+    int64_t W = std::min<int64_t>({16, std::max<int64_t>(1, cdiv(numel, kWave)), wmax_single});
+    int64_t seg = cdiv(std::max<int64_t>(numel, 1), W);
+    seg = cdiv(seg, kWave) * kWave;
+    W = std::max<int64_t>(1, cdiv(numel, seg));
+    pl.W = int(W);
+    pl.seg = int(seg);
+    pl.ntiles = 1;
+    const int64_t waves = std::min<int64_t>(16, std::max<int64_t>(W, cdiv(LE, kWave)));
+    pl.threads = int(waves * kWave);
+    pl.lds_bytes = size_t((W * LE + fixed) * 4);
+    pl.ws_bytes = 0;
+    return pl;
+  }
+  pl.single = false;
+  const int64_t W = std::min<int64_t>(16, kLdsInts / LE);
+  const int64_t max_tiles = std::max<int64_t>(1, std::min<int64_t>(1024, (int64_t(1) << 18) / LE));
+  int64_t ntiles = std::min<int64_t>(max_tiles, cdiv(numel, W * kWave));
+  ntiles = std::max<int64_t>(ntiles, 1);
+  int64_t seg = std::max<int64_t>(kWave, cdiv(cdiv(numel, ntiles * W), kWave) * kWave);
+  ntiles = std::max<int64_t>(1, cdiv(numel, W * seg));
+  pl.W = int(W);
+  pl.seg = int(seg);
+  pl.ntiles = int(ntiles);
+  pl.threads = int(W * kWave);
+  pl.lds_bytes = size_t(W * LE * 4);
+  pl.meta_lds_bytes = size_t((LE + L + 1 + 17) * 4);
+  pl.ws_bytes = (ntiles * LE + 2 * LE) * 4;
+  return pl;
+}
+
+hipError_t launch_align(const AlignPlan& pl, const AlignParams& a, hipStream_t st) {
+  if (pl.single) {
+    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(pl.threads), pl.lds_bytes, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(align_tile_count_kernel, dim3(pl.ntiles), dim3(pl.threads), pl.lds_bytes,
+                     st, a);
+  hipLaunchKernelGGL(align_tile_prefix_kernel, dim3(unsigned(cdiv(a.LE, 256))), dim3(256), 0,
+                     st, a);
+  hipLaunchKernelGGL(align_meta_kernel, dim3(1), dim3(1024), pl.meta_lds_bytes, st, a);
+  hipLaunchKernelGGL(align_tile_scatter_kernel, dim3(pl.ntiles), dim3(pl.threads),
+                     pl.lds_bytes, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mlr

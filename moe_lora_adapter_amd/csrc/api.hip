@@ -1,0 +1,192 @@
+// C ABI of the MoE-LoRA hot path: argument checks, sizing, dispatch.
+// Every check runs on the host before any HIP call; a failing check returns
+// a negative status with nothing launched and nothing written.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/moe_lora.h"
+#include "internal.h"
+
+using namespace mlr;
+
+namespace {
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxL = 1024;
+constexpr int64_t kMaxLE = 8192;
+constexpr int64_t kMaxRank = 128;
+constexpr int64_t kInt32Max = 2147483647;
+
+bool block_m_ok(int64_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared size checks of both calls.  On success fills numel and cap.
+int check_sizes(int64_t M, int64_t topk, int64_t E, int64_t L, int64_t block_m,
+                int64_t* numel_out, int64_t* cap_out) {
+  if (M < 0 || topk < 1 || E < 1 || L < 1) return MOE_LORA_ERR_INVALID;
+  if (E > kMaxE || L > kMaxL || L * E > kMaxLE || !block_m_ok(block_m))
+    return MOE_LORA_ERR_UNSUPPORTED;
+  if (topk > kInt32Max || M > kInt32Max / topk) return MOE_LORA_ERR_UNSUPPORTED;
+  const int64_t numel = M * topk;
+  const int64_t groups = std::min(E, numel);
+  const int64_t bound = numel + groups * (block_m - 1);
+  const int64_t cap = (bound + block_m - 1) / block_m * block_m;
+  if (bound + block_m >= kInt32Max || L * cap >= kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;
+  *numel_out = numel;
+  *cap_out = cap;
+  return MOE_LORA_OK;
+}
+
+int nbits_for(int64_t keys) {
+  int n = 0;
+  while ((int64_t(1) << n) < keys) ++n;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_lora_status_string(int status) {
+  switch (status) {
+    case MOE_LORA_OK: return "ok";
+    case MOE_LORA_ERR_INVALID: return "invalid argument";
+    case MOE_LORA_ERR_UNSUPPORTED: return "unsupported size or option";
+    case MOE_LORA_ERR_WORKSPACE: return "workspace too small";
+    case MOE_LORA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_lora_align_capacity(int64_t M, int32_t topk, int32_t E, int32_t block_m) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, 1, block_m, &numel, &cap);
+  return rc != MOE_LORA_OK ? rc : cap;
+}
+
+int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int32_t E, int32_t L,
+                                       int32_t block_m) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  return plan_align(numel, E, L, block_m).ws_bytes;
+}
+
+int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, int64_t M,
+                   int32_t topk, int32_t E, int32_t L, int32_t block_m,
+                   int32_t* sorted_token_ids, int32_t* expert_ids,
+                   int32_t* num_tokens_post_padded, int32_t* lora_ids,
+                   int32_t* num_active_loras, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  if (!topk_ids || !token_lora_mapping || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded || workspace_bytes < 0)
+    return MOE_LORA_ERR_INVALID;
+  // numel == 0 still launches: every slot's metadata is written (all empty)
+  const AlignPlan plan = plan_align(numel, E, L, block_m);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return MOE_LORA_ERR_WORKSPACE;
+  AlignParams a{};
+  a.topk_ids = topk_ids;
+  a.mapping = token_lora_mapping;
+  a.sorted = sorted_token_ids;
+  a.eids = expert_ids;
+  a.ntpp = num_tokens_post_padded;
+  a.lora_ids = lora_ids;
+  a.nact = num_active_loras;
+  a.numel = int32_t(numel);
+  a.topk = topk;
+  a.E = E;
+  a.L = L;
+  a.LE = L * E;
+  a.B = block_m;
+  a.nbits = nbits_for(int64_t(L) * E);
+  a.cap = int32_t(cap);
+  a.nb = int32_t(cap / block_m);
+  a.W = plan.W;
+  a.seg = plan.seg;
+  a.ntiles = plan.ntiles;
+  if (!plan.single) {
+    int32_t* ws = static_cast<int32_t*>(workspace);
+    a.tile_cnt = ws;
+    a.key_tot = ws + int64_t(plan.ntiles) * a.LE;
+    a.key_off = a.key_tot + a.LE;
+  }
+  const hipError_t err = launch_align(plan, a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                   const uint16_t* lora_b, const int32_t* sorted_token_ids,
+                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                   const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                   int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                   int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
+                   void* stream) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  if (K < 8 || Ns < 8 || S < 1 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
+  if ((x_per_pair != 0 && x_per_pair != 1) || (mul_routed_weight != 0 && mul_routed_weight != 1) ||
+      (add_inputs != 0 && add_inputs != 1) || variant < 0 || variant > 2)
+    return MOE_LORA_ERR_INVALID;
+  if (r > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
+  if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded || !y || (mul_routed_weight && !topk_weights))
+    return MOE_LORA_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y))
+    return MOE_LORA_ERR_INVALID;
+  const int64_t N = int64_t(S) * Ns;
+  if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_supported(r, block_m))
+    return MOE_LORA_ERR_UNSUPPORTED;
+  if (numel == 0) return MOE_LORA_OK;
+  const int64_t gmax = max_total_blocks(numel, int64_t(L) * E, block_m);
+  const int64_t units = gmax * S;
+  if (units * 64 > kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;
+
+  FusedParams p{};
+  p.x = x;
+  p.a = lora_a;
+  p.b = lora_b;
+  p.sorted = sorted_token_ids;
+  p.eids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.w = topk_weights;
+  p.y = y;
+  p.x_per_pair = x_per_pair;
+  p.mul = mul_routed_weight;
+  p.add = add_inputs;
+  p.numel = int32_t(numel);
+  p.topk = topk;
+  p.K = K;
+  p.Ns = Ns;
+  p.S = S;
+  p.E = E;
+  p.L = L;
+  p.r = r;
+  p.B = block_m;
+  p.N = int32_t(N);
+  p.cap = int32_t(cap);
+  p.nb = int32_t(cap / block_m);
+  p.units = int32_t(units);
+
+  bool use_mfma = false;
+  if (variant == MOE_LORA_VARIANT_MFMA) {
+    use_mfma = true;
+  } else if (variant == MOE_LORA_VARIANT_AUTO) {
+    // expected valid rows per block: pairs over the groups they can fill
+    const int64_t groups = std::min<int64_t>(numel, int64_t(L) * E);
+    const int64_t rows_per_group = numel / std::max<int64_t>(groups, 1);
+    use_mfma = mfma_supported(r, block_m) && rows_per_group >= 8;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
+  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+}  // extern "C"

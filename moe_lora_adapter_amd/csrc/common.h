@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlr {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, 32 CUs each
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return (uint64_t(1) << lane) - 1;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Mask of the lanes (among `active`) whose key equals this lane's key, found
+// by voting on each key bit in turn.  Keys are below 2^nbits.
+__device__ __forceinline__ uint64_t match_key(int key, uint64_t active, int nbits) {
+  uint64_t peers = active;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t ones = __ballot(bit);
+    peers &= bit ? ones : ~ones;
+  }
+  return peers;
+}
+
+// Exclusive prefix sum, in place, of a[0..n) held in LDS, by the whole
+// workgroup (blockDim.x a multiple of 64, at most 1024).  `wtot` is LDS
+// scratch of at least 17 ints.  Returns the total to every thread.  Contains
+// barriers: every thread of the block must call it.
+__device__ inline int block_excl_scan(int* a, int n, int* wtot) {
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int nw = blockDim.x / kWave;
+  int carry = 0;
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int i = base + tid;
+    const int v = i < n ? a[i] : 0;
+    const int incl = wave_incl_scan(v);
+    if (lane == kWave - 1) wtot[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int t = lane < nw ? wtot[lane] : 0;
+      const int ti = wave_incl_scan(t);
+      if (lane < nw) wtot[lane] = ti - t;
+      if (lane == nw - 1) wtot[16] = ti;
+    }
+    __syncthreads();
+    if (i < n) a[i] = carry + wtot[w] + incl - v;
+    carry += wtot[16];
+    __syncthreads();
+  }
+  return carry;
+}
+
+// bf16 <-> fp32.  Widening is exact (the bf16 bits are the upper half of the
+// binary32 value).  Narrowing rounds to nearest, ties to even, from the IEEE
+// definition; NaN stays a quiet NaN.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2 on gfx950).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// 8 bf16 x 8 bf16 dot product added onto acc.
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+  acc = dot2_bf16(a.x, b.x, acc);
+  acc = dot2_bf16(a.y, b.y, acc);
+  acc = dot2_bf16(a.z, b.z, acc);
+  acc = dot2_bf16(a.w, b.w, acc);
+  return acc;
+}
+
+}  // namespace mlr

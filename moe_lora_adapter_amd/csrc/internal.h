@@ -1,0 +1,69 @@
+// Host-side declarations shared by the translation units of libmoelora.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlr {
+
+// ---------------------------------------------------------------- align
+struct AlignParams {
+  const int32_t* topk_ids;
+  const int32_t* mapping;
+  int32_t* sorted;    // [L, cap]
+  int32_t* eids;      // [L, nb]
+  int32_t* ntpp;      // [L]
+  int32_t* lora_ids;  // [L] or null
+  int32_t* nact;      // [1] or null
+  int32_t* tile_cnt;  // [ntiles, LE]  (multi-workgroup path)
+  int32_t* key_tot;   // [LE]
+  int32_t* key_off;   // [LE]
+  int32_t numel, topk, E, L, LE, B, nbits;
+  int32_t cap, nb;
+  int32_t W;       // waves that own a pair segment, per workgroup
+  int32_t seg;     // pairs per wave segment (multiple of 64)
+  int32_t ntiles;  // workgroups of the tile kernels
+};
+
+struct AlignPlan {
+  bool single;       // one workgroup does everything
+  int W, seg, ntiles;
+  int threads;       // block size of the single / tile kernels
+  size_t lds_bytes;  // dynamic LDS of the single / tile kernels
+  size_t meta_lds_bytes;
+  int64_t ws_bytes;  // device workspace (0 for the single path)
+};
+
+AlignPlan plan_align(int64_t numel, int E, int L, int B);
+hipError_t launch_align(const AlignPlan& plan, const AlignParams& a, hipStream_t st);
+
+// ---------------------------------------------------------------- fused
+struct FusedParams {
+  const uint16_t* x;
+  const uint16_t* a;   // [S, L, E, r, K]
+  const uint16_t* b;   // [S, L, E, Ns, r]
+  const int32_t* sorted;
+  const int32_t* eids;
+  const int32_t* ntpp;
+  const float* w;      // [numel] or null
+  uint16_t* y;         // [numel, N]
+  int32_t x_per_pair, mul, add;
+  int32_t numel, topk, K, Ns, S, E, L, r, B, N;
+  int32_t cap, nb;
+  int32_t units;       // upper bound on blocks, times S
+  int32_t n_split;     // workgroups sharing one (block, slice)
+  int32_t nsz;         // output columns per split (multiple of 8)
+};
+
+// Upper bound on the number of blocks over all slots: every non-empty
+// (slot, expert) group adds at most block_m - 1 padding entries.
+inline int64_t max_total_blocks(int64_t numel, int64_t LE, int64_t B) {
+  const int64_t groups = numel < LE ? numel : LE;
+  return (numel + groups * (B - 1)) / B;
+}
+
+hipError_t launch_fused_valu(FusedParams p, hipStream_t st);
+hipError_t launch_fused_mfma(FusedParams p, hipStream_t st);
+bool mfma_supported(int r, int B);
+
+}  // namespace mlr

@@ -1,0 +1,152 @@
+"""The C ABI library on the host: it loads, exports every declared symbol,
+and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_lora_adapter_amd as mla
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_lora.h")
+
+V = ctypes.c_void_p
+P16 = V(16)  # a non-null, 16-byte aligned stand-in; never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_LORA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert set(names) == set(mla.SIGNATURES), names
+    lib = mla.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert mla.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert mla.status_string(st) not in ("ok", "unknown status")
+    assert mla.status_string(5) == "unknown status"
+
+
+def test_capacity_matches_oracle_and_bound():
+    o = oracle.load()
+    for M, topk, E, B in ((16, 2, 8, 16), (16, 4, 32, 16), (8192, 8, 128, 64),
+                          (0, 4, 32, 16), (3, 1, 2, 4 * 4), (65536, 8, 256, 64)):
+        assert mla.align_capacity(M, topk, E, B) == o.capacity(M, topk, E, B)
+
+
+def test_workspace_query():
+    assert mla.align_workspace_bytes(16, 4, 32, 6, 16) == 0          # one workgroup
+    assert mla.align_workspace_bytes(65536, 8, 256, 16, 64) > 0      # tiles
+    assert mla.align_workspace_bytes(0, 4, 32, 6, 16) == 0
+
+
+def align_call(**kw):
+    args = dict(topk_ids=P16, mapping=P16, M=16, topk=4, E=32, L=6, B=16, sorted=P16,
+                eids=P16, ntpp=P16, lora_ids=None, nact=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    a = args
+    return mla.lib().moe_lora_align(a["topk_ids"], a["mapping"], a["M"], a["topk"], a["E"],
+                                    a["L"], a["B"], a["sorted"], a["eids"], a["ntpp"],
+                                    a["lora_ids"], a["nact"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk_ids=None), mla.ERR_INVALID),
+    (dict(mapping=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(eids=None), mla.ERR_INVALID),
+    (dict(ntpp=None), mla.ERR_INVALID),
+    (dict(M=-1), mla.ERR_INVALID),
+    (dict(topk=0), mla.ERR_INVALID),
+    (dict(E=0), mla.ERR_INVALID),
+    (dict(L=0), mla.ERR_INVALID),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(L=1025, E=1), mla.ERR_UNSUPPORTED),
+    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
+    (dict(B=8), mla.ERR_UNSUPPORTED),
+    (dict(B=48), mla.ERR_UNSUPPORTED),
+    (dict(M=2 ** 31, topk=1), mla.ERR_UNSUPPORTED),
+    (dict(M=65536, topk=8, E=256, L=16, B=64), mla.ERR_WORKSPACE),
+    (dict(M=65536, topk=8, E=256, L=16, B=64, ws=P16, ws_bytes=100), mla.ERR_WORKSPACE),
+    (dict(ws_bytes=-1), mla.ERR_INVALID),
+])
+def test_align_rejects(kw, status):
+    assert align_call(**kw) == status
+
+
+def fused_call(**kw):
+    a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
+             add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
+             variant=0)
+    a.update(kw)
+    return mla.lib().fused_moe_lora(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"], a["eids"],
+                                    a["ntpp"], a["w"], a["mul"], a["add"], a["M"], a["topk"],
+                                    a["K"], a["Ns"], a["S"], a["E"], a["L"], a["r"], a["B"],
+                                    a["y"], a["variant"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.ERR_INVALID),
+    (dict(la=None), mla.ERR_INVALID),
+    (dict(lb=None), mla.ERR_INVALID),
+    (dict(y=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(mul=1, w=None), mla.ERR_INVALID),
+    (dict(mul=2), mla.ERR_INVALID),
+    (dict(add=-1), mla.ERR_INVALID),
+    (dict(xpp=3), mla.ERR_INVALID),
+    (dict(variant=7), mla.ERR_INVALID),
+    (dict(K=2884), mla.ERR_INVALID),
+    (dict(Ns=2881), mla.ERR_INVALID),
+    (dict(K=0), mla.ERR_INVALID),
+    (dict(S=0), mla.ERR_INVALID),
+    (dict(r=0), mla.ERR_INVALID),
+    (dict(r=129), mla.ERR_UNSUPPORTED),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(B=24), mla.ERR_UNSUPPORTED),
+    (dict(x=V(24)), mla.ERR_INVALID),
+    (dict(y=V(18)), mla.ERR_INVALID),
+    (dict(M=0), mla.OK),
+])
+def test_fused_rejects(kw, status):
+    assert fused_call(**kw) == status
+
+
+def test_binding_checks_dtypes_before_calling():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        mla.moe_lora_align(torch.zeros((4, 2), dtype=torch.int64), torch.zeros(4, dtype=torch.int32),
+                           8, 2, 16)
+    with pytest.raises(ValueError):
+        mla.moe_lora_align(torch.zeros((4, 2), dtype=torch.int32)[:, :1],
+                           torch.zeros(4, dtype=torch.int32), 8, 2, 16)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = mla._lib
+    try:
+        mla._lib = None
+        with pytest.raises(RuntimeError, match="no fallback"):
+            mla.lib(str(tmp_path / "nope.so"))
+    finally:
+        mla._lib = saved
+
+
+def test_product_package_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "moe_lora_adapter_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle.c" not in text, f

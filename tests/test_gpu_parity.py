@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Align outputs must match bit for bit.  Y must satisfy
+|gpu - oracle| <= 1e-2 * (1 + |oracle|) elementwise; rows of pairs in no slot
+must be bit-identical to the input.  Small workloads are compared in full;
+the full-size workloads are compared on sampled pairs that the oracle
+computes one by one, plus properties that hold at any size.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from moe_lora_adapter_amd import synth  # noqa: E402
+import gpu_helpers as gh  # noqa: E402
+
+SMALL = ["tiny"] + [f"oss20b_decode_w13_a{a}" for a in range(1, 7)] + \
+    ["oss120b_decode_w13", "oss120b_decode_w2"]
+LARGE = ["oss120b_prefill_w13", "oss120b_prefill_w2", "qwen3_prefill", "dense_qkv", "dense_o"]
+ALIGN_ALL = SMALL + LARGE + ["align_stress", "align_stress_neg"]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def _variants(s):
+    return ["valu"] + (["mfma"] if _mfma_ok(s) else [])
+
+
+def _mfma_ok(s):
+    import moe_lora_adapter_amd as mla
+    import ctypes
+    # probe with a zero-sized call: MOE_LORA_ERR_UNSUPPORTED means not available
+    rc = mla.lib().fused_moe_lora(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                  ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                  None, 0, 1, 0, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                  s.block_m, ctypes.c_void_p(16), 2, None)
+    return rc == 0
+
+
+# ------------------------------------------------------------------ align
+@pytest.mark.parametrize("name", ALIGN_ALL)
+def test_align_matches_oracle(orc, name):
+    s = synth.shape(name)
+    _log(f"align parity {name} M={s.M} topk={s.topk} E={s.E} L={s.L} B={s.block_m}")
+    c = synth.draw(s, with_tensors=False)
+    ref = orc.align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m)
+    gpu = gh.align_to_host(gh.run_align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m))
+    gh.assert_align_equal(gpu, ref, s.block_m)
+
+
+def _random_align_case(rng):
+    M = int(rng.choice([0, 1, 3, 64, 65, 1000, 4095, 4096, 4097, 9000, 20000]))
+    topk = int(rng.integers(1, 9))
+    E = int(rng.choice([1, 2, 7, 64, 129, 1024]))
+    L = int(rng.choice([1, 2, 5, 8]))
+    while L * E > 8192:
+        L //= 2
+    B = int(rng.choice([16, 32, 64, 128]))
+    topk_ids = rng.integers(-1, E + 1, size=(M, topk)).astype(np.int32)
+    mapping = rng.integers(-2, L + 1, size=M).astype(np.int32)
+    return topk_ids, mapping, E, L, B
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_align_edge_cases(orc, seed):
+    rng = np.random.default_rng(100 + seed)
+    topk_ids, mapping, E, L, B = _random_align_case(rng)
+    _log(f"align edge seed={seed} M={len(mapping)} topk={topk_ids.shape[1]} E={E} L={L} B={B}")
+    ref = orc.align(topk_ids, mapping, E, L, B)
+    gpu = gh.align_to_host(gh.run_align(topk_ids, mapping, E, L, B))
+    gh.assert_align_equal(gpu, ref, B)
+
+
+def test_align_max_experts_and_many_slots(orc):
+    rng = np.random.default_rng(7)
+    for (M, topk, E, L, B) in ((3000, 8, 1024, 8, 64), (500, 2, 2, 1024, 16),
+                               (40000, 4, 8, 1024, 128)):
+        _log(f"align limits M={M} topk={topk} E={E} L={L} B={B}")
+        topk_ids = rng.integers(0, E, size=(M, topk)).astype(np.int32)
+        mapping = rng.integers(-1, L, size=M).astype(np.int32)
+        ref = orc.align(topk_ids, mapping, E, L, B)
+        gpu = gh.align_to_host(gh.run_align(topk_ids, mapping, E, L, B))
+        gh.assert_align_equal(gpu, ref, B)
+
+
+def test_align_deterministic():
+    s = synth.shape("align_stress")
+    c = synth.draw(s, with_tensors=False)
+    a = gh.align_to_host(gh.run_align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m))
+    b = gh.align_to_host(gh.run_align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m))
+    for k in ("sorted_token_ids", "num_tokens_post_padded", "lora_ids"):
+        for l, n in enumerate(a["num_tokens_post_padded"]):
+            if k == "sorted_token_ids":
+                assert np.array_equal(a[k][l, :n], b[k][l, :n])
+        assert np.array_equal(a["num_tokens_post_padded"], b["num_tokens_post_padded"])
+
+
+# ------------------------------------------------------------------ fused, full compare
+def _full_compare(orc, s, variant):
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    y = dc.fused(variant=variant)
+    got = gh.bf16_host_f64(y).reshape(s.numel, s.N)
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+    gh.assert_fused_close(got, ref, f"{s.name}/{variant}/{s.dist}")
+    base = gh.bf16_host_f64(dc.y_in).reshape(s.numel, s.N)
+    inval = ~gh.valid_pairs(c)
+    assert np.array_equal(got[inval], base[inval]), "rows of unmapped pairs changed"
+    return c, dc, got, ref
+
+
+@pytest.mark.parametrize("dist", ["literal", "stress"])
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_fused_small_full(orc, name, dist, variant):
+    s = synth.shape(name, dist=dist)
+    if variant == "mfma" and not _mfma_ok(s):
+        pytest.skip("MFMA kernel not available for this shape")
+    _log(f"fused full {name} {dist} {variant}")
+    _full_compare(orc, s, variant)
+
+
+@pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a3"])
+def test_fused_overwrite_delta(orc, name):
+    """add_inputs = 0 writes the delta itself: checked elementwise and normwise."""
+    s = synth.shape(name, add=False)
+    for variant in _variants(s):
+        _log(f"fused overwrite {name} {variant}")
+        c, dc, got, ref = _full_compare(orc, s, variant)
+        v = gh.valid_pairs(c)
+        gh.assert_delta_close(got[v], ref[v], np.zeros_like(ref[v]), f"{name}/{variant}")
+
+
+# ------------------------------------------------------------------ fused, full size sampled
+def _sample_pairs(c, rng, n=384):
+    s = c.shape
+    v = np.nonzero(gh.valid_pairs(c))[0]
+    pick = rng.choice(v, size=min(n, len(v)), replace=False)
+    ends = np.array([v[0], v[-1]])
+    return np.unique(np.concatenate([pick, ends]))
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_fused_full_size_sampled(orc, name):
+    s = synth.shape(name)
+    _log(f"fused full-size {name}: drawing inputs")
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    align = dc.align()
+    pairs = _sample_pairs(c, np.random.default_rng(s.seed))
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair, pairs=pairs)
+    inval = torch.from_numpy(~gh.valid_pairs(c)).to(gh.DEV)
+    for variant in _variants(s):
+        _log(f"fused full-size {name} {variant}")
+        y = dc.fused(align=align, variant=variant)
+        yv = y.view(s.numel, s.N)
+        got = gh.bf16_host_f64(yv[torch.from_numpy(pairs).to(gh.DEV)])
+        gh.assert_fused_close(got, ref, f"{name}/{variant}")
+        same = (yv[inval].view(torch.int16) == dc.y_in.view(s.numel, s.N)[inval].view(torch.int16))
+        assert bool(same.all()), "rows of unmapped pairs changed"
+
+
+# ------------------------------------------------------------------ metamorphic, bit-exact
+@pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "oss120b_decode_w2"])
+def test_fused_metamorphic(name):
+    s = synth.shape(name, dist="stress")
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    align = dc.align()
+    for variant in _variants(s):
+        _log(f"fused metamorphic {name} {variant}")
+        zero_a = torch.zeros_like(dc.a)
+        y = dc.fused(align, variant, add=True, a=zero_a)
+        assert torch.equal(y.view(torch.int16), dc.y_in.view(torch.int16)), "zero adapter, add"
+        y = dc.fused(align, variant, add=False, a=zero_a)
+        valid = torch.from_numpy(gh.valid_pairs(c)).to(gh.DEV)
+        assert bool((y.view(s.numel, s.N)[valid].float() == 0).all()), "zero adapter, overwrite"
+        # routed weights of one equal no routed weight
+        ones = torch.ones_like(dc.w)
+        w_saved, dc.w = dc.w, ones
+        y1 = dc.fused(align, variant, mul=True)
+        dc.w = w_saved
+        y0 = dc.fused(align, variant, mul=False)
+        assert torch.equal(y1.view(torch.int16), y0.view(torch.int16)), "w = 1 vs no weight"
+        # doubling B doubles the overwritten delta exactly
+        d1 = dc.fused(align, variant, add=False).float()
+        d2 = dc.fused(align, variant, add=False, b=dc.b * 2).float()
+        assert torch.equal(d2, 2 * d1), "B -> 2B"
+        # add onto zeros equals overwrite
+        yz = dc.fused(align, variant, add=True, y=torch.zeros_like(dc.y_in))
+        yo = dc.fused(align, variant, add=False, y=torch.zeros_like(dc.y_in))
+        assert torch.equal(yz.view(torch.int16), yo.view(torch.int16)), "add onto 0"
+        # deterministic
+        ya = dc.fused(align, variant)
+        yb = dc.fused(align, variant)
+        assert torch.equal(ya.view(torch.int16), yb.view(torch.int16)), "run to run"
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+EDGE = [
+    dict(K=264, Ns=776, r=8, block_m=16),
+    dict(K=264, Ns=776, r=5, block_m=32),
+    dict(K=8, Ns=8, r=1, block_m=16),
+    dict(K=128, Ns=64, r=4, block_m=64),
+    dict(K=256, Ns=128, r=24, block_m=128),
+    dict(K=512, Ns=256, r=128, block_m=64),
+    dict(K=1032, Ns=136, r=64, block_m=16, S=3),
+    dict(K=256, Ns=128, r=16, block_m=64, M=300, E=4, topk=3, x_per_pair=True, mul=True),
+    dict(K=256, Ns=128, r=32, block_m=16, M=200, E=1024, topk=8, L=2, active=2),
+    dict(K=64, Ns=64, r=16, block_m=16, M=70, E=3, L=100, active=70, p_neg=0.1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(EDGE)))
+def test_fused_edge_shapes(orc, i):
+    s = synth.shape("tiny", dist="stress", seed=9000 + i, **EDGE[i])
+    for variant in _variants(s):
+        _log(f"fused edge {i} {EDGE[i]} {variant}")
+        _full_compare(orc, s, variant)
+
+
+def test_fused_duplicate_experts_in_token(orc):
+    s = synth.shape("tiny", dist="stress", seed=77, topk=4)
+    c = synth.draw(s)
+    c.topk_ids[:, 1] = c.topk_ids[:, 0]     # the same expert twice per token
+    c.topk_ids[::3, 3] = c.topk_ids[::3, 0]
+    dc = gh.DeviceCase(c)
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add)
+    for variant in _variants(s):
+        got = gh.bf16_host_f64(dc.fused(variant=variant)).reshape(s.numel, s.N)
+        gh.assert_fused_close(got, ref, f"duplicates/{variant}")
+
+
+def test_fused_no_mapped_token_and_empty_batch():
+    s = synth.shape("tiny", p_neg=1.0)
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    for variant in _variants(s):
+        y = dc.fused(variant=variant)
+        assert torch.equal(y.view(torch.int16), dc.y_in.view(torch.int16))
+    import moe_lora_adapter_amd as mla
+    s0 = synth.shape("tiny", M=0)
+    c0 = synth.draw(s0)
+    d0 = gh.DeviceCase(c0)
+    al = d0.align()
+    torch.cuda.synchronize()
+    assert int(al.num_active_loras.item()) == 0
+    assert bool((al.num_tokens_post_padded == 0).all())
+    mla.fused_moe_lora(d0.x, d0.a, d0.b, al, d0.w, d0.y_in, mul_routed_weight=True,
+                       add_inputs=True)
