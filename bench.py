@@ -1,0 +1,347 @@
+"""Benchmark of the MoE-LoRA hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: moe_lora_align, then
+fused_moe_lora, on seeded synthetic inputs already resident in HBM.  The
+default workload is the gpt-oss-20b-like decode w13 shape (M=16, K=2880,
+N=2x2880, E=32, topk=4, L=6 slots all active, r=64, BLOCK_M=16).
+
+Timing:
+  * value / ms_per_step: K steps captured in one HIP graph and replayed,
+    bracketed by synchronize on both sides.  Every input buffer is rotated
+    over enough copies that the touched bytes exceed 4x the 256 MB
+    Infinity Cache, so weights are read from HBM (``--warm`` disables this).
+  * roofline: the fused kernel's own duration from HIP events recorded on
+    its stream around each launch (work queued behind a short GPU sleep so
+    the events bracket back-to-back kernels), against the algorithmic bytes
+    it must move (weights of the active (slice, slot, expert) groups once,
+    the X rows it reads, the Y rows it reads and writes, routed weights and
+    block metadata).
+  * cpu_baseline: the CPU oracle (plain C, fp64) on the same inputs.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("fused MoE-LoRA µs/call + achieved HBM TB/s (decode) / MFMA % (prefill)")
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_lora_adapter_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------- algorithmic work
+def algorithmic_work(case):
+    """Bytes and flops the fused step must move / compute (see module doc)."""
+    s = case.shape
+    slot = np.repeat(case.token_lora_mapping, s.topk).astype(np.int64)
+    ex = case.topk_ids.reshape(-1).astype(np.int64)
+    valid = (slot >= 0) & (slot < s.L) & (ex >= 0) & (ex < s.E)
+    P = int(valid.sum())
+    keys = np.unique(slot[valid] * s.E + ex[valid])
+    groups = len(keys) * s.S
+    idx = np.nonzero(valid)[0]
+    xrows = len(np.unique(idx if s.x_per_pair else idx // s.topk))
+    cnt = np.bincount(slot[valid] * s.E + ex[valid], minlength=s.L * s.E)
+    padded = int((-(-cnt // s.block_m) * s.block_m).sum())
+    w_bytes = groups * (s.r * s.K + s.Ns * s.r) * 2
+    x_bytes = xrows * s.K * 2
+    y_bytes = P * s.S * s.Ns * 2 * (2 if s.add else 1)
+    meta = padded * 4 + (padded // s.block_m) * 4 + (P * 4 if s.mul else 0)
+    fused_bytes = w_bytes + x_bytes + y_bytes + meta
+    flops = 2.0 * P * s.S * s.r * (s.K + s.Ns)
+    align_bytes = s.numel * 4 + s.M * 4 + padded * 4 + (padded // s.block_m) * 4 + 2 * s.L * 4
+    return dict(valid_pairs=P, active_groups=len(keys), fused_bytes=int(fused_bytes),
+                weight_bytes=int(w_bytes), x_bytes=int(x_bytes), y_bytes=int(y_bytes),
+                meta_bytes=int(meta), fused_flops=flops, align_bytes=int(align_bytes))
+
+
+# ----------------------------------------------------------------- device inputs
+class DeviceSet:
+    """One copy of every buffer a step reads or writes."""
+
+    def __init__(self, case, dev, proto=None):
+        import torch
+        import moe_lora_adapter_amd as mla
+        s = case.shape
+        if proto is None:
+            t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+            self.topk_ids = torch.from_numpy(case.topk_ids).to(dev)
+            self.mapping = torch.from_numpy(case.token_lora_mapping).to(dev)
+            self.w = torch.from_numpy(case.topk_weights).to(dev)
+            self.x, self.a, self.b, self.y = t16(case.x), t16(case.lora_a), t16(case.lora_b), t16(case.y_in)
+        else:
+            for k in ("topk_ids", "mapping", "w", "x", "a", "b", "y"):
+                setattr(self, k, getattr(proto, k).clone())
+        self.align = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, dev)
+        ws = mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+
+
+def run_align(ds, s):
+    import moe_lora_adapter_amd as mla
+    mla.moe_lora_align(ds.topk_ids, ds.mapping, s.E, s.L, s.block_m, out=ds.align, workspace=ds.ws)
+
+
+def run_fused(ds, s, variant):
+    import moe_lora_adapter_amd as mla
+    mla.fused_moe_lora(ds.x, ds.a, ds.b, ds.align, ds.w, ds.y, mul_routed_weight=s.mul,
+                       add_inputs=s.add, x_per_pair=s.x_per_pair, variant=variant)
+
+
+def step(ds, s, variant):
+    run_align(ds, s)
+    run_fused(ds, s, variant)
+
+
+# ----------------------------------------------------------------- measurements
+def time_steps_graph(sets, s, variant, steps):
+    """Capture `steps` steps (rotating over the copies) in one graph; replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step(sets[0], s, variant)  # stream warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(sets[i % len(sets)], s, variant)
+    torch.cuda.synchronize()
+    g.replay()  # untimed replay: first-launch costs of the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_kernel_events(sets, s, variant, which, launches):
+    """Average duration of one kernel from events around each launch."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))   # ~50 ms: lets the launches queue up
+    for i in range(launches):
+        ds = sets[i % len(sets)]
+        if which == "fused":
+            run_align(ds, s)
+        evs[i][0].record()
+        if which == "fused":
+            run_fused(ds, s, variant)
+        else:
+            run_align(ds, s)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])  # us
+    return float(d.mean()), float(np.median(d))
+
+
+def cpu_baseline(case, budget_s):
+    import oracle
+    o = oracle.load()
+    s = case.shape
+    valid = np.nonzero((np.repeat(case.token_lora_mapping, s.topk) >= 0))[0]
+    t0 = time.perf_counter()
+    o.align(case.topk_ids, case.token_lora_mapping, s.E, s.L, s.block_m)
+    t_align = time.perf_counter() - t0
+    # time one pair first, then size a sample to the budget
+    probe = valid[:1]
+    t0 = time.perf_counter()
+    o.fused(case.x, case.lora_a, case.lora_b, case.topk_ids, case.token_lora_mapping,
+            case.topk_weights, case.y_in, s.mul, s.add, x_per_pair=s.x_per_pair, pairs=probe)
+    per_pair = max(time.perf_counter() - t0, 1e-6)
+    threads = o.num_threads()
+    n_full = len(valid)
+    reps, n_sample = 1, n_full
+    est_full = per_pair * n_full / max(1, min(threads, n_full))
+    if est_full > budget_s:
+        n_sample = max(threads, int(n_full * budget_s / est_full))
+    else:
+        reps = max(1, int(budget_s / max(est_full, 1e-3)))
+    sample = valid[np.linspace(0, n_full - 1, n_sample).astype(np.int64)] if n_sample < n_full else None
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        o.fused(case.x, case.lora_a, case.lora_b, case.topk_ids, case.token_lora_mapping,
+                case.topk_weights, case.y_in, s.mul, s.add, x_per_pair=s.x_per_pair, pairs=sample)
+        times.append(time.perf_counter() - t0)
+    t_fused = float(np.median(times)) * (n_full / n_sample)
+    if sample is None:
+        desc = f"whole step (align + fused over all {n_full} valid pairs), median of {reps} runs"
+    else:
+        desc = (f"align over all pairs + fused over {n_sample} of {n_full} valid pairs "
+                f"(evenly spaced), scaled to all pairs")
+    return {"value": round((t_align + t_fused) * 1e6, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle", "sample": desc,
+            "align_us": round(t_align * 1e6, 1), "fused_us": round(t_fused * 1e6, 1)}
+
+
+def copy_calibration(dev, mib=256, reps=5):
+    """Plain device copies of known size, for scaling rocprofv3 byte counters."""
+    import torch
+    a = torch.empty(mib * 2 ** 20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {mib} MiB")
+
+
+def load_traffic(kernel, workload):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None, None
+    if not rec or rec.get("src_sha") != kernel_sources_sha():
+        return None, rec
+    return rec.get("traffic_bytes_per_launch"), rec
+
+
+# ----------------------------------------------------------------- main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="oss20b_decode_w13_a6")
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--warm", action="store_true", help="no cache-defeating rotation")
+    ap.add_argument("--cold-bytes", type=float, default=4 * MALL_BYTES)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain 256 MiB device copies (rocprofv3 counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the hot path has no "
+              "cross-GPU step); run with --gpus 1", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: one process, one GPU", file=sys.stderr)
+        return 2
+
+    import torch
+    import moe_lora_adapter_amd as mla
+    from moe_lora_adapter_amd import synth
+
+    dev = torch.device("cuda:0")
+    mla.lib()
+    s = synth.shape(args.workload)
+    log(f"workload {s.name}: drawing inputs")
+    case = synth.draw(s)
+    work = algorithmic_work(case)
+    touched = work["fused_bytes"] + work["align_bytes"]
+    copies = 1 if args.warm else max(1, min(64, math.ceil(args.cold_bytes / touched)))
+    log(f"{copies} input copies (touched {touched / 1e6:.1f} MB each)")
+    sets = [DeviceSet(case, dev)]
+    for _ in range(copies - 1):
+        sets.append(DeviceSet(case, dev, proto=sets[0]))
+    variant = args.variant
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(sets[i % copies], s, variant)
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        copy_calibration(dev)
+
+    log(f"timing {args.steps} steps (one graph)")
+    sec_per_step = time_steps_graph(sets, s, variant, args.steps)
+    log("timing kernels with events")
+    fused_avg, fused_med = time_kernel_events(sets, s, variant, "fused", args.steps)
+    align_avg, align_med = time_kernel_events(sets, s, variant, "align", args.steps)
+
+    gbps = work["fused_bytes"] / (fused_avg * 1e-6) / 1e9
+    tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
+    kname = "fused_mfma_kernel" if _uses_mfma(s, variant) else "fused_valu_kernel"
+    traffic, _rec = load_traffic(kname, s.name)
+    out = {
+        "metric": METRIC,
+        "value": round(sec_per_step * 1e6, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; routing, adapter mapping and weights drawn, no dataset)",
+        "config": {"workload": s.name, "M": s.M, "K": s.K, "N": s.N, "slices": s.S, "E": s.E,
+                   "topk": s.topk, "L": s.L, "active_slots": s.active, "r": s.r,
+                   "block_m": s.block_m, "mul_routed_weight": s.mul, "add_inputs": s.add,
+                   "x_per_pair": s.x_per_pair, "step": "moe_lora_align + fused_moe_lora",
+                   "timing": "one HIP graph of K steps",
+                   "cache": ("warm" if args.warm else
+                             f"cold: {copies} rotated input copies, "
+                             f"{copies * touched / 2 ** 30:.2f} GiB touched")},
+        "roofline": {"bound": "hbm", "kernel": kname,
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": work["fused_bytes"],
+                     "kernel_us_avg": round(fused_avg, 3), "kernel_us_median": round(fused_med, 3)},
+        "fused_tflops": round(tflops, 3),
+        "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "align_kernel_us_avg": round(align_avg, 3),
+        "work": work,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _uses_mfma(s, variant):
+    if variant == "mfma":
+        return True
+    if variant == "valu":
+        return False
+    groups = min(s.numel, s.L * s.E)
+    return (s.numel // max(groups, 1)) >= 8 and _mfma_available(s)
+
+
+def _mfma_available(s):
+    import ctypes
+    import moe_lora_adapter_amd as mla
+    P = ctypes.c_void_p(16)
+    rc = mla.lib().fused_moe_lora(P, 0, P, P, P, P, P, None, 0, 1, 0, s.topk, s.K, s.Ns, s.S,
+                                  s.E, s.L, s.r, s.block_m, P, 2, None)
+    return rc == 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

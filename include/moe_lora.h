@@ -23,7 +23,8 @@
  *   - Arguments are validated on the host before any HIP call.  A negative
  *     status means nothing was launched and no output was written.
  *   - M = 0 is valid: moe_lora_align still writes every slot's metadata
- *     (all slots empty), fused_moe_lora returns MOE_LORA_OK at once.
+ *     (all slots empty), fused_moe_lora returns MOE_LORA_OK at once.  Arrays
+ *     of zero size may then be NULL.
  *   - Calls on different streams may overlap if their outputs are disjoint.
  *
  * Limits: 1 <= E <= 1024 (the expert limit asked for in the review of PR

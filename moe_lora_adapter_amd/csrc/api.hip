@@ -83,8 +83,10 @@ int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, i
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
   if (rc != MOE_LORA_OK) return rc;
-  if (!topk_ids || !token_lora_mapping || !sorted_token_ids || !expert_ids ||
-      !num_tokens_post_padded || workspace_bytes < 0)
+  // arrays of zero size (everything but num_tokens_post_padded when M == 0)
+  // may be null
+  if (!num_tokens_post_padded || workspace_bytes < 0) return MOE_LORA_ERR_INVALID;
+  if (numel > 0 && (!topk_ids || !token_lora_mapping || !sorted_token_ids || !expert_ids))
     return MOE_LORA_ERR_INVALID;
   // numel == 0 still launches: every slot's metadata is written (all empty)
   const AlignPlan plan = plan_align(numel, E, L, block_m);
@@ -135,16 +137,16 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
       (add_inputs != 0 && add_inputs != 1) || variant < 0 || variant > 2)
     return MOE_LORA_ERR_INVALID;
   if (r > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
+  const int64_t N = int64_t(S) * Ns;
+  if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_supported(r, block_m))
+    return MOE_LORA_ERR_UNSUPPORTED;
+  if (numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
   if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
       !num_tokens_post_padded || !y || (mul_routed_weight && !topk_weights))
     return MOE_LORA_ERR_INVALID;
   if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y))
     return MOE_LORA_ERR_INVALID;
-  const int64_t N = int64_t(S) * Ns;
-  if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
-  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_supported(r, block_m))
-    return MOE_LORA_ERR_UNSUPPORTED;
-  if (numel == 0) return MOE_LORA_OK;
   const int64_t gmax = max_total_blocks(numel, int64_t(L) * E, block_m);
   const int64_t units = gmax * S;
   if (units * 64 > kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;

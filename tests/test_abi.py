@@ -62,6 +62,7 @@ def align_call(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(topk_ids=None), mla.ERR_INVALID),
+    (dict(M=0, ntpp=None), mla.ERR_INVALID),
     (dict(mapping=None), mla.ERR_INVALID),
     (dict(sorted=None), mla.ERR_INVALID),
     (dict(eids=None), mla.ERR_INVALID),
@@ -117,6 +118,7 @@ def fused_call(**kw):
     (dict(x=V(24)), mla.ERR_INVALID),
     (dict(y=V(18)), mla.ERR_INVALID),
     (dict(M=0), mla.OK),
+    (dict(M=0, x=None, y=None, sorted=None, eids=None), mla.OK),
 ])
 def test_fused_rejects(kw, status):
     assert fused_call(**kw) == status

@@ -199,8 +199,8 @@ def test_fused_metamorphic(name):
         y0 = dc.fused(align, variant, mul=False)
         assert torch.equal(y1.view(torch.int16), y0.view(torch.int16)), "w = 1 vs no weight"
         # doubling B doubles the overwritten delta exactly
-        d1 = dc.fused(align, variant, add=False).float()
-        d2 = dc.fused(align, variant, add=False, b=dc.b * 2).float()
+        d1 = dc.fused(align, variant, add=False).view(s.numel, s.N)[valid].float()
+        d2 = dc.fused(align, variant, add=False, b=dc.b * 2).view(s.numel, s.N)[valid].float()
         assert torch.equal(d2, 2 * d1), "B -> 2B"
         # add onto zeros equals overwrite
         yz = dc.fused(align, variant, add=True, y=torch.zeros_like(dc.y_in))
@@ -265,3 +265,41 @@ def test_fused_no_mapped_token_and_empty_batch():
     assert bool((al.num_tokens_post_padded == 0).all())
     mla.fused_moe_lora(d0.x, d0.a, d0.b, al, d0.w, d0.y_in, mul_routed_weight=True,
                        add_inputs=True)
+
+
+# ------------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "qwen3_prefill"])
+def test_graph_replay_matches_eager(name):
+    """align + fused captured in a HIP graph: every replay equals the eager run."""
+    import moe_lora_adapter_amd as mla
+    s = synth.shape(name, dist="stress")
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    variants = _variants(s)
+    eager = {v: dc.fused(variant=v) for v in variants}
+    al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
+    ws = torch.empty(max(16, mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)),
+                     dtype=torch.uint8, device=gh.DEV)
+    for v in variants:
+        _log(f"graph replay {name} {v}")
+        y = dc.y_in.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            mla.moe_lora_align(dc.topk_ids, dc.mapping, s.E, s.L, s.block_m, out=al, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            mla.moe_lora_align(dc.topk_ids, dc.mapping, s.E, s.L, s.block_m, out=al, workspace=ws)
+            mla.fused_moe_lora(dc.x, dc.a, dc.b, al, dc.w, y, mul_routed_weight=s.mul,
+                               add_inputs=s.add, x_per_pair=s.x_per_pair, variant=v)
+        for rep in range(3):
+            y.copy_(dc.y_in)                       # eager work between replays
+            al.sorted_token_ids.fill_(-7)
+            al.num_tokens_post_padded.fill_(-7)
+            al.expert_ids.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), eager[v].view(torch.int16)), f"replay {rep}"
