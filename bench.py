@@ -10,9 +10,9 @@ Timing:
     bracketed by synchronize on both sides.  Every input buffer is rotated
     over enough copies that the touched bytes exceed 4x the 256 MB
     Infinity Cache, so weights are read from HBM (``--warm`` disables this).
-  * roofline: the fused kernel's own duration from HIP events recorded on
-    its stream around each launch (work queued behind a short GPU sleep so
-    the events bracket back-to-back kernels), against the algorithmic bytes
+  * roofline: the fused kernel's own duration from HIP events on its stream
+    around K back-to-back launches (queued behind a short GPU sleep so they
+    run back to back), against the algorithmic bytes
     it must move (weights of the active (slice, slot, expert) groups once,
     the X rows it reads, the Y rows it reads and writes, routed weights and
     block metadata).
@@ -145,25 +145,25 @@ def time_steps_graph(sets, s, variant, steps):
 
 
 def time_kernel_events(sets, s, variant, which, launches):
-    """Average duration of one kernel from events around each launch."""
+    """Average duration of one kernel: `launches` back-to-back launches of it
+    between one pair of HIP events on its stream, queued behind a short GPU
+    sleep so the launches run back to back.  The align outputs of every copy
+    are already in place from earlier steps, so fused launches need no align
+    in between."""
     import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(2.4e9 * 0.05))   # ~50 ms: lets the launches queue up
+    e0.record()
     for i in range(launches):
         ds = sets[i % len(sets)]
-        if which == "fused":
-            run_align(ds, s)
-        evs[i][0].record()
         if which == "fused":
             run_fused(ds, s, variant)
         else:
             run_align(ds, s)
-        evs[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    d = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])  # us
-    return float(d.mean()), float(np.median(d))
+    return e0.elapsed_time(e1) * 1e3 / launches
 
 
 def cpu_baseline(case, budget_s):
@@ -280,8 +280,8 @@ def main(argv=None):
     log(f"timing {args.steps} steps (one graph)")
     sec_per_step = time_steps_graph(sets, s, variant, args.steps)
     log("timing kernels with events")
-    fused_avg, fused_med = time_kernel_events(sets, s, variant, "fused", args.steps)
-    align_avg, align_med = time_kernel_events(sets, s, variant, "align", args.steps)
+    fused_avg = time_kernel_events(sets, s, variant, "fused", args.steps)
+    align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
 
     gbps = work["fused_bytes"] / (fused_avg * 1e-6) / 1e9
     tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
@@ -312,7 +312,7 @@ def main(argv=None):
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": work["fused_bytes"],
-                     "kernel_us_avg": round(fused_avg, 3), "kernel_us_median": round(fused_med, 3)},
+                     "kernel_us_avg": round(fused_avg, 3)},
         "fused_tflops": round(tflops, 3),
         "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
         "align_kernel_us_avg": round(align_avg, 3),

@@ -10,7 +10,10 @@ constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, 32 CUs each
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// Wavefront index within the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return (uint64_t(1) << lane) - 1;

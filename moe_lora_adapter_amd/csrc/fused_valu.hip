@@ -1,23 +1,31 @@
 // Fused shrink + expand with vector loads and wavefront reductions (the
 // decode-sized path).  One workgroup handles one (block, slice, column split):
 //
-//   shrink  v[i][j] = sum_t X[row_i][t] A[j][t]   -- lanes walk K in 16-byte
-//           chunks (coalesced: a wavefront reads 1 KiB of one A row per load),
-//           each wave owns a few A rows at a time, bf16 pairs are multiplied
-//           with v_dot2, and the 64 lane partials are folded with a
-//           reduce-scatter butterfly so one pass yields RG*JW sums;
-//   v       stays in LDS (fp32), never in global memory;
-//   expand  d[i][n] = sum_j v[i][j] B[n][j]        -- one thread per output
-//           column n of this split; Y is read (add_inputs) and written with
-//           consecutive columns on consecutive lanes.
+//   shrink  v[i][j] = sum_t X[row_i][t] A[j][t].  The wavefronts form RGW row
+//           groups x KP partitions of K.  A wavefront owns JW rows of A and
+//           walks its part of K in 16-byte chunks, lanes side by side (one
+//           wavefront load reads 1 KiB of one A row).  All row loads of a step
+//           are issued before any is used, so every lane keeps up to 16 loads
+//           in flight.  bf16 pairs are multiplied with v_dot2; the 64 lane
+//           partials are folded with a reduce-scatter butterfly and the KP
+//           partial sums are added in LDS.
+//   v       stays on chip (LDS, fp32); it never goes to global memory.
+//   expand  d[i][n] = sum_j v[i][j] B[n][j].  For r in {8,...,128} the B tile
+//           of the split (consecutive rows n, r contiguous) is read as one
+//           coalesced stream of 16-byte chunks; a lane always sees the same
+//           8 ranks, keeps those v values in registers, and the partial sums
+//           of one row are folded over the r/8 lanes that share it.  Other
+//           ranks take one thread per column.
 //
 // The prhub summary of vLLM PR #42290 (implementation steps) describes the
 // one-shot kernel: x loaded once, multiplied by lora_a, the rank-sized result
 // kept in registers and multiplied by lora_b, written over or added onto the
-// output.  This kernel keeps that shape; the column split (several
-// workgroups per block, each redoing the small shrink) gives a decode batch
-// enough workgroups to pull HBM bandwidth, and workgroup ids are mapped so the
-// splits of one block land on the same XCD and re-read A from its L2.
+// output.  Here several workgroups share a block by splitting its output
+// columns (each redoes the small shrink), so that a decode batch with few
+// active groups still spreads over the chip.  The split count is chosen on
+// the device from the number of blocks actually present, and the splits of a
+// block get workgroup ids of equal residue mod 8, which places them on one XCD
+// where they re-read A from its L2.
 #include <algorithm>
 
 #include "common.h"
@@ -25,20 +33,44 @@
 
 namespace mlr {
 
-constexpr int kValuThreads = 256;
-constexpr int kValuWaves = kValuThreads / kWave;
-constexpr int kRG = 4;   // X rows per group
-constexpr int kJW = 4;   // A rows per wave per pass
+// Launch shape.  The defaults were picked by timing the decode shapes on
+// MI355X; they can be overridden when building to re-tune.
+#ifndef MLR_VALU_THREADS
+#define MLR_VALU_THREADS 1024
+#endif
+#ifndef MLR_VALU_WG_TARGET   // working workgroups to aim for
+#define MLR_VALU_WG_TARGET 192
+#endif
+#ifndef MLR_VALU_LOADS       // A rows loaded per wavefront per step (x RG <= 32)
+#define MLR_VALU_LOADS 16
+#endif
+#ifndef MLR_VALU_MIN_COLS    // fewest output columns per split
+#define MLR_VALU_MIN_COLS 256
+#endif
+constexpr int kThreads = MLR_VALU_THREADS;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxB = 128;
 constexpr int kMaxR = 128;
+constexpr int kMaxRG = 4;    // X rows per group
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Block g (over all active slots, in slot order) -> slot l, block b in slot.
-// Every lane of the calling wavefront gets the same answer.
-__device__ __forceinline__ bool find_block(const FusedParams& p, int g, int& l, int& b) {
+// Number of blocks over all slots (every lane gets it).
+__device__ __forceinline__ int count_blocks(const FusedParams& p) {
+  int run = 0;
+  for (int c0 = 0; c0 < p.L; c0 += kWave) {
+    const int sl = c0 + lane_id();
+    const int nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
+    run += __shfl(wave_incl_scan(nbk), kWave - 1);
+  }
+  return run;
+}
+
+// Block g (over all active slots, in slot order; g < total) -> slot l and
+// block b inside the slot.  Every lane of the wavefront gets the same answer.
+__device__ __forceinline__ void find_block(const FusedParams& p, int g, int& l, int& b) {
   int run = 0;
   for (int c0 = 0; c0 < p.L; c0 += kWave) {
     const int sl = c0 + lane_id();
@@ -49,27 +81,32 @@ __device__ __forceinline__ bool find_block(const FusedParams& p, int g, int& l, 
       const int first = __builtin_ctzll(hit);
       l = c0 + first;
       b = g - (__shfl(incl, first) - __shfl(nbk, first));
-      return true;
+      return;
     }
     run = __shfl(incl, kWave - 1);
   }
-  return false;
+  l = b = 0;
 }
 
 // Sum NV per-lane values over the wavefront.  On return the lane holds the
 // total of value index `which`; lanes whose index bits agree hold the same.
 template <int NV>
 __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int& which) {
+  static_assert(NV >= 1 && NV <= kWave && (NV & (NV - 1)) == 0, "NV: power of two <= 64");
   const int lane = lane_id();
   which = 0;
   int o = kWave / 2;
 #pragma unroll
   for (int half = NV / 2; half >= 1; half >>= 1, o >>= 1) {
     const bool up = lane & o;
+    // select on the values (bit masks), not on array indices: an index
+    // select would turn v into a dynamically indexed (scratch) array
+    const uint32_t m = up ? 0xffffffffu : 0u;
 #pragma unroll
     for (int q = 0; q < half; ++q) {
-      const float send = up ? v[q] : v[q + half];
-      const float keep = up ? v[q + half] : v[q];
+      const uint32_t lo = __float_as_uint(v[q]), hi = __float_as_uint(v[q + half]);
+      const float send = __uint_as_float((lo & m) | (hi & ~m));
+      const float keep = __uint_as_float((hi & m) | (lo & ~m));
       v[q] = keep + __shfl_xor(send, o);
     }
     if (up) which += half;
@@ -79,101 +116,253 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int& which) {
   return t;
 }
 
-__device__ void shrink_group(const FusedParams& p, const uint16_t* __restrict__ A,
-                             const int* s_row, int nr, float* s_v) {
+struct ShrinkShape {
+  int rgw;    // row groups of wavefronts
+  int kp;     // K partitions
+};
+
+// One wavefront: JW rows of A starting at j0 (rows >= r are loaded clamped and
+// dropped), K chunks [c0, c1), RG X rows.  Writes RG x JW partial sums to
+// part[(i) * r + j] of its K partition.
+template <int RG, int JW>
+__device__ __forceinline__ void shrink_wave(const FusedParams& p, const uint16_t* __restrict__ A,
+                                            const uint16_t* const (&xr)[kMaxRG], int j0, int c0,
+                                            int c1, float* part) {
+  const int lane = lane_id();
+  float acc[RG * JW];
+#pragma unroll
+  for (int q = 0; q < RG * JW; ++q) acc[q] = 0.f;
+  const uint16_t* arow[JW];
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj) arow[jj] = A + int64_t(min(j0 + jj, p.r - 1)) * p.K;
+#pragma unroll 1
+  for (int c = c0 + lane; c < c1; c += kWave) {
+    uint4 av[JW];
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) av[jj] = ld16(arow[jj] + c * 8);
+    uint4 xv[RG];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) xv[i] = ld16(xr[i] + c * 8);
+    // every load of the step is issued before the first product waits
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+      for (int i = 0; i < RG; ++i) acc[i * JW + jj] = dot8_bf16(av[jj], xv[i], acc[i * JW + jj]);
+  }
+  int which;
+  const float t = reduce_scatter<RG * JW>(acc, which);
+  if ((lane & (kWave / (RG * JW) - 1)) == 0) {
+    const int i = which / JW, j = j0 + which % JW;
+    if (j < p.r) part[i * p.r + j] = t;
+  }
+}
+
+// v[i][j] for the RG rows of a group into s_v (fp32, row stride kMaxR).
+template <int RG, int JW>
+__device__ __forceinline__ void shrink_group(const FusedParams& p, const uint16_t* __restrict__ A,
+                                             const int* s_row, int nr, ShrinkShape sh,
+                                             float* s_part, float* s_v) {
+  constexpr int JL = JW < MLR_VALU_LOADS ? JW : MLR_VALU_LOADS;
+  constexpr int JB = (RG * JL > 32) ? 32 / RG : JL;
+  const int w = wave_id();
+  const int rg = w % sh.rgw, kpi = w / sh.rgw;
+  const uint16_t* xr[kMaxRG];
+#pragma unroll
+  for (int i = 0; i < kMaxRG; ++i)
+    xr[i] = p.x + int64_t(__builtin_amdgcn_readfirstlane(s_row[i < nr ? i : 0])) * p.K;
   const int K8 = p.K >> 3;
-  const int w = wave_id(), lane = lane_id();
-  const uint16_t* xr[kRG];
+  if (kpi < sh.kp) {
+    const int per = (K8 + sh.kp - 1) / sh.kp;
+    const int c0 = kpi * per, c1 = min(K8, c0 + per);
+    for (int j0 = rg * JW; j0 < p.r; j0 += sh.rgw * JW)
+      for (int jb = j0; jb < min(j0 + JW, p.r); jb += JB)
+        shrink_wave<RG, JB>(p, A, xr, jb, c0, c1, s_part + kpi * RG * p.r);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nr * p.r; t += kThreads) {
+    const int i = t / p.r, j = t - i * p.r;
+    float sum = 0.f;
+    for (int q = 0; q < sh.kp; ++q) sum += s_part[(q * RG + i) * p.r + j];
+    s_v[i * kMaxR + j] = sum;
+  }
+  __syncthreads();
+}
+
+// Per-row output scale: the routed weight, or 1.
+template <int RG>
+__device__ __forceinline__ void row_scales(const FusedParams& p, const int* s_pair, int nr,
+                                           float (&wt)[RG]) {
 #pragma unroll
-  for (int i = 0; i < kRG; ++i) xr[i] = p.x + int64_t(s_row[i < nr ? i : 0]) * p.K;
-  for (int jb = w * kJW; jb < p.r; jb += kValuWaves * kJW) {
-    float acc[kRG * kJW];
+  for (int i = 0; i < RG; ++i) wt[i] = (p.mul && i < nr) ? p.w[s_pair[i]] : 1.f;
+}
+
+// Y[pair, col] = bf16(w * d + (add ? y : 0)) for the valid rows of a group;
+// y holds the bf16 input values, loaded earlier.
+template <int RG>
+__device__ __forceinline__ void store_out(const FusedParams& p, const int* s_pair, int nr,
+                                          int col, const float (&d)[RG], const float (&wt)[RG],
+                                          const uint16_t (&y)[RG]) {
 #pragma unroll
-    for (int q = 0; q < kRG * kJW; ++q) acc[q] = 0.f;
-    const int jn = min(kJW, p.r - jb);
-    for (int c = lane; c < K8; c += kWave) {
-      uint4 xv[kRG];
-#pragma unroll
-      for (int i = 0; i < kRG; ++i) xv[i] = ld16(xr[i] + c * 8);
-#pragma unroll
-      for (int jj = 0; jj < kJW; ++jj) {
-        if (jj < jn) {
-          const uint4 av = ld16(A + int64_t(jb + jj) * p.K + c * 8);
-#pragma unroll
-          for (int i = 0; i < kRG; ++i) acc[i * kJW + jj] = dot8_bf16(av, xv[i], acc[i * kJW + jj]);
-        }
-      }
-    }
-    int which;
-    const float t = reduce_scatter<kRG * kJW>(acc, which);
-    if ((lane & (kWave / (kRG * kJW) - 1)) == 0) {
-      const int i = which / kJW, jj = which % kJW;
-      if (i < nr && jj < jn) s_v[i * kMaxR + jb + jj] = t;
+  for (int i = 0; i < RG; ++i) {
+    if (i < nr) {
+      float val = d[i] * wt[i];
+      if (p.add) val += bf16_to_f32(y[i]);
+      p.y[int64_t(s_pair[i]) * p.N + col] = f32_to_bf16(val);
     }
   }
 }
 
-__device__ void expand_group(const FusedParams& p, const uint16_t* __restrict__ Bm,
-                             const int* s_pair, int nr, const float* s_v, int s, int n0,
-                             int n1) {
-  for (int n = n0 + int(threadIdx.x); n < n1; n += kValuThreads) {
+template <int RG>
+__device__ __forceinline__ void load_y(const FusedParams& p, const int* s_pair, int nr, int col,
+                                       uint16_t (&y)[RG]) {
+#pragma unroll
+  for (int i = 0; i < RG; ++i)
+    y[i] = (p.add && i < nr) ? p.y[int64_t(s_pair[i]) * p.N + col] : uint16_t(0);
+}
+
+// Expand for r == 8 * CPR: the B tile rows [n0, n1) read as one coalesced
+// stream of 16-byte chunks.  Chunk q of the tile is row q / CPR, ranks
+// 8 * (q % CPR) .. +8; since the thread count is a multiple of CPR a thread
+// always sees the same eight ranks.  The row sums land in LDS (s_d), and the
+// epilogue then reads Y and writes it back in 16-byte pieces (8 columns per
+// thread), the Y reads issued before the B chunks are consumed.
+constexpr int kRowsPerBatch = 2048;
+
+template <int RG, int CPR>
+__device__ __forceinline__ void expand_stream(const FusedParams& p, const uint16_t* __restrict__ Bm,
+                                              const int* s_pair, int nr, const float* s_v, int s,
+                                              int n0, int n1, float* s_d) {
+  // chunk loads in flight per thread; one batch covers at most kRowsPerBatch rows
+  constexpr int NB0 = RG <= 2 ? 16 : 8;
+  constexpr int NBR = kRowsPerBatch * CPR / kThreads;
+  constexpr int NB = NB0 < NBR ? NB0 : (NBR > 0 ? NBR : 1);
+  const int tid = threadIdx.x;
+  const int jc = tid % CPR;
+  float vr[RG][8];
+#pragma unroll
+  for (int i = 0; i < RG; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) vr[i][q] = s_v[i * kMaxR + jc * 8 + q];
+  float wt[RG];
+  row_scales<RG>(p, s_pair, nr, wt);
+  const uint16_t* tile = Bm + int64_t(n0) * p.r;
+  const int nchunks = (n1 - n0) * CPR;
+  const int col0 = s * p.Ns + n0;
+#pragma unroll 1
+  for (int base = 0; base < nchunks; base += NB * kThreads) {
+    const int rows = min(NB * kThreads, nchunks - base) / CPR;  // columns in this batch
+    const int row0 = base / CPR;
+    // epilogue task of this thread: row i, 8 columns starting at 8 * c8
+    const int c8n = rows / 8;
+    const int task_i = tid / max(c8n, 1), task_c = tid - task_i * max(c8n, 1);
+    const bool has_task = c8n > 0 && task_i < nr;
+    uint4 yv = make_uint4(0, 0, 0, 0);
+    uint16_t* yp = nullptr;
+    if (has_task) {
+      yp = p.y + int64_t(s_pair[task_i]) * p.N + col0 + row0 + task_c * 8;
+      if (p.add) yv = *reinterpret_cast<const uint4*>(yp);
+    }
+    uint4 bv[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int q = min(base + k * kThreads + tid, nchunks - 1);
+      bv[k] = ld16(tile + int64_t(q) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int q = base + k * kThreads + tid;
+      const uint4 b4 = bv[k];
+      const float b[8] = {bf16_lo(b4.x), bf16_hi(b4.x), bf16_lo(b4.y), bf16_hi(b4.y),
+                          bf16_lo(b4.z), bf16_hi(b4.z), bf16_lo(b4.w), bf16_hi(b4.w)};
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) d += vr[i][t] * b[t];
+#pragma unroll
+        for (int o = CPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
+        if (jc == 0 && q < nchunks) s_d[i * kRowsPerBatch + q / CPR - row0] = d;
+      }
+    }
+    __syncthreads();
+    if (has_task) {
+      const float* dd = s_d + task_i * kRowsPerBatch + task_c * 8;
+      const float w = wt[task_i];
+      const uint32_t in[4] = {yv.x, yv.y, yv.z, yv.w};
+      uint32_t outw[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float lo = dd[2 * h] * w, hi = dd[2 * h + 1] * w;
+        if (p.add) {
+          lo += bf16_lo(in[h]);
+          hi += bf16_hi(in[h]);
+        }
+        outw[h] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(yp) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    }
+    __syncthreads();
+  }
+}
+
+// Expand for any other rank: one thread per output column.
+template <int RG>
+__device__ __forceinline__ void expand_columns(const FusedParams& p, const uint16_t* __restrict__ Bm,
+                                               const int* s_pair, int nr, const float* s_v, int s,
+                                               int n0, int n1) {
+  float wt[RG];
+  row_scales<RG>(p, s_pair, nr, wt);
+#pragma unroll 1
+  for (int n = n0 + int(threadIdx.x); n < n1; n += kThreads) {
+    uint16_t yv[RG];
+    load_y<RG>(p, s_pair, nr, s * p.Ns + n, yv);
     const uint16_t* brow = Bm + int64_t(n) * p.r;
-    float acc[kRG];
+    float d[RG];
 #pragma unroll
-    for (int i = 0; i < kRG; ++i) acc[i] = 0.f;
-    if ((p.r & 7) == 0) {
-      for (int j0 = 0; j0 < p.r; j0 += 8) {
-        const uint4 bv = ld16(brow + j0);
-        const float bf[8] = {bf16_lo(bv.x), bf16_hi(bv.x), bf16_lo(bv.y), bf16_hi(bv.y),
-                             bf16_lo(bv.z), bf16_hi(bv.z), bf16_lo(bv.w), bf16_hi(bv.w)};
+    for (int i = 0; i < RG; ++i) d[i] = 0.f;
+    for (int j = 0; j < p.r; ++j) {
+      const float bj = bf16_to_f32(brow[j]);
 #pragma unroll
-        for (int i = 0; i < kRG; ++i) {
-          if (i < nr) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[i] += s_v[i * kMaxR + j0 + q] * bf[q];
-          }
-        }
-      }
-    } else {
-      for (int j = 0; j < p.r; ++j) {
-        const float bj = bf16_to_f32(brow[j]);
-#pragma unroll
-        for (int i = 0; i < kRG; ++i)
-          if (i < nr) acc[i] += s_v[i * kMaxR + j] * bj;
-      }
+      for (int i = 0; i < RG; ++i) d[i] += s_v[i * kMaxR + j] * bj;
     }
-#pragma unroll
-    for (int i = 0; i < kRG; ++i) {
-      if (i < nr) {
-        const int pair = s_pair[i];
-        float val = acc[i];
-        if (p.mul) val *= p.w[pair];
-        uint16_t* yp = p.y + int64_t(pair) * p.N + s * p.Ns + n;
-        if (p.add) val += bf16_to_f32(*yp);
-        *yp = f32_to_bf16(val);
-      }
-    }
+    store_out<RG>(p, s_pair, nr, s * p.Ns + n, d, wt, yv);
   }
 }
 
-__global__ void __launch_bounds__(kValuThreads) fused_valu_kernel(FusedParams p) {
+template <int RG, int JW, int CPR>
+__global__ void __launch_bounds__(kThreads) fused_valu_kernel(FusedParams p, ShrinkShape sh) {
   __shared__ int s_pair[kMaxB];
   __shared__ int s_row[kMaxB];
-  __shared__ float s_v[kRG * kMaxR];
+  __shared__ float s_v[kMaxRG * kMaxR];
+  __shared__ float s_part[kMaxRG * 256];
+  __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
 
-  // workgroup id -> (unit, split); the splits of one unit share an XCD
+  // The blocks present decide the split count: enough working workgroups to
+  // fill the chip, at least MLR_VALU_MIN_COLS columns each.
+  const int total = __builtin_amdgcn_readfirstlane(count_blocks(p));
+  const int units = total * p.S;
+  const int u8 = (units + kXcds - 1) / kXcds * kXcds;
+  const int max_split = max(1, p.Ns / MLR_VALU_MIN_COLS);
+  const int n_split = min(max_split, max(1, (MLR_VALU_WG_TARGET + u8 - 1) / max(u8, 1)));
+  // workgroup -> (split, unit), split-major; equal unit residue mod 8 = same XCD
   const int id = blockIdx.x;
-  const int xcd = id % kXcds, q = id / kXcds;
-  const int unit = (q / p.n_split) * kXcds + xcd;
-  const int split = q % p.n_split;
-  if (unit >= p.units) return;
-  const int g = unit / p.S, s = unit - g * p.S;
-  const int n0 = split * p.nsz;
+  const int split = id / max(u8, 1), unit = id - split * u8;
+  if (unit >= units || split >= n_split) return;
+  const int nsz = ((p.Ns + n_split - 1) / n_split + 7) / 8 * 8;
+  const int n0 = split * nsz;
   if (n0 >= p.Ns) return;
-  const int n1 = min(p.Ns, n0 + p.nsz);
+  const int n1 = min(p.Ns, n0 + nsz);
+  const int g = unit / p.S, s = unit - g * p.S;
   int l, b;
-  if (!find_block(p, g, l, b)) return;
-  const int e = p.eids[l * p.nb + b];
+  find_block(p, g, l, b);
+  l = __builtin_amdgcn_readfirstlane(l);
+  b = __builtin_amdgcn_readfirstlane(b);
+  const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
+  const uint16_t* A = p.a + wsel * p.r * p.K;
+  const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
 
   const int tid = threadIdx.x;
   int valid = 0;
@@ -184,31 +373,58 @@ __global__ void __launch_bounds__(kValuThreads) fused_valu_kernel(FusedParams p)
     s_row[tid] = valid ? (p.x_per_pair ? pid : pid / p.topk) : 0;
   }
   // valid rows form a prefix of the block (sentinels only pad a group's end)
-  const int nv = __syncthreads_count(valid);
+  const int nv = __builtin_amdgcn_readfirstlane(__syncthreads_count(valid));
 
-  const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
-  const uint16_t* A = p.a + wsel * p.r * p.K;
-  const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
-  for (int g0 = 0; g0 < nv; g0 += kRG) {
-    const int nr = min(kRG, nv - g0);
-    shrink_group(p, A, s_row + g0, nr, s_v);
-    __syncthreads();
-    expand_group(p, Bm, s_pair + g0, nr, s_v, s, n0, n1);
+  // rows in groups of RG (a group with fewer valid rows repeats row 0 and
+  // drops its sums)
+  for (int g0 = 0; g0 < nv; g0 += RG) {
+    const int nr = min(RG, nv - g0);
+    shrink_group<RG, JW>(p, A, s_row + g0, nr, sh, s_part, s_v);
+      if constexpr (CPR > 0)
+      expand_stream<RG, CPR>(p, Bm, s_pair + g0, nr, s_v, s, n0, n1, s_d);
+    else
+      expand_columns<RG>(p, Bm, s_pair + g0, nr, s_v, s, n0, n1);
     __syncthreads();
   }
 }
 
+template <int JW, int CPR>
+static void launch(const FusedParams& p, ShrinkShape sh, int rg, dim3 grid, hipStream_t st) {
+  if (rg == 2)
+    hipLaunchKernelGGL((fused_valu_kernel<2, JW, CPR>), grid, dim3(kThreads), 0, st, p, sh);
+  else
+    hipLaunchKernelGGL((fused_valu_kernel<4, JW, CPR>), grid, dim3(kThreads), 0, st, p, sh);
+}
+
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
-  // enough workgroups to keep every CU streaming: aim for ~512 in total
-  int n_split = (512 + p.units - 1) / p.units;
-  const int max_split = std::max(1, p.Ns / 256);
-  n_split = std::max(1, std::min(n_split, max_split));
-  p.n_split = n_split;
-  p.nsz = ((p.Ns + n_split - 1) / n_split + 7) / 8 * 8;
+  // rows of A per wavefront and the wave arrangement
+  int jw = 1;
+  while (jw < p.r && jw < 16) jw <<= 1;
+  ShrinkShape sh;
+  sh.rgw = std::min(kWaves, (p.r + jw - 1) / jw);
+  sh.kp = std::max(1, kWaves / sh.rgw);
+  // grid: the most working workgroups any block count can ask for, plus the
+  // padding of the unit count to a multiple of 8 per split
   const int64_t units_pad = (int64_t(p.units) + kXcds - 1) / kXcds * kXcds;
-  const int64_t grid = units_pad * n_split;
-  hipLaunchKernelGGL(fused_valu_kernel, dim3(unsigned(grid)), dim3(kValuThreads), 0, st, p);
-  return hipGetLastError();
+  const int64_t grid = MLR_VALU_WG_TARGET + units_pad;
+  const int cpr = (p.r % 8 == 0 && ((p.r / 8) & (p.r / 8 - 1)) == 0) ? p.r / 8 : 0;
+  // X rows per group: 2 when blocks are expected to hold few valid rows
+  const int64_t groups = std::min<int64_t>(p.numel, int64_t(p.L) * p.E);
+  const int rg = (p.numel <= 2 * groups + groups / 2) ? 2 : 4;
+#define MLR_CASE(JW_, CPR_) \
+  if (jw == JW_ && cpr == CPR_) { launch<JW_, CPR_>(p, sh, rg, dim3(unsigned(grid)), st); return hipGetLastError(); }
+  MLR_CASE(16, 16)
+  MLR_CASE(16, 8)
+  MLR_CASE(16, 4)
+  MLR_CASE(16, 2)
+  MLR_CASE(8, 1)
+  MLR_CASE(16, 0)
+  MLR_CASE(8, 0)
+  MLR_CASE(4, 0)
+  MLR_CASE(2, 0)
+  MLR_CASE(1, 0)
+#undef MLR_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mlr

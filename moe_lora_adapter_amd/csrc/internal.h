@@ -51,8 +51,6 @@ struct FusedParams {
   int32_t numel, topk, K, Ns, S, E, L, r, B, N;
   int32_t cap, nb;
   int32_t units;       // upper bound on blocks, times S
-  int32_t n_split;     // workgroups sharing one (block, slice)
-  int32_t nsz;         // output columns per split (multiple of 8)
 };
 
 // Upper bound on the number of blocks over all slots: every non-empty
