@@ -181,10 +181,12 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
   if (variant == MOE_LORA_VARIANT_MFMA) {
     use_mfma = true;
   } else if (variant == MOE_LORA_VARIANT_AUTO) {
-    // expected valid rows per block: pairs over the groups they can fill
+    // expected valid rows per block: pairs over the groups they can fill.
+    // MFMA pays off once blocks are dense and the rank is large enough that
+    // the contraction, not the X / Y streams, carries the work (measured).
     const int64_t groups = std::min<int64_t>(numel, int64_t(L) * E);
     const int64_t rows_per_group = numel / std::max<int64_t>(groups, 1);
-    use_mfma = mfma_supported(r, block_m) && rows_per_group >= 8;
+    use_mfma = mfma_supported(r, block_m) && rows_per_group >= 8 && r >= 64;
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);

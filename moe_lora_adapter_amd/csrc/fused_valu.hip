@@ -28,6 +28,7 @@
 // where they re-read A from its L2.
 #include <algorithm>
 
+#include "blocks.h"
 #include "common.h"
 #include "internal.h"
 
@@ -55,37 +56,6 @@ constexpr int kMaxRG = 4;    // X rows per group
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
-}
-
-// Number of blocks over all slots (every lane gets it).
-__device__ __forceinline__ int count_blocks(const FusedParams& p) {
-  int run = 0;
-  for (int c0 = 0; c0 < p.L; c0 += kWave) {
-    const int sl = c0 + lane_id();
-    const int nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
-    run += __shfl(wave_incl_scan(nbk), kWave - 1);
-  }
-  return run;
-}
-
-// Block g (over all active slots, in slot order; g < total) -> slot l and
-// block b inside the slot.  Every lane of the wavefront gets the same answer.
-__device__ __forceinline__ void find_block(const FusedParams& p, int g, int& l, int& b) {
-  int run = 0;
-  for (int c0 = 0; c0 < p.L; c0 += kWave) {
-    const int sl = c0 + lane_id();
-    const int nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
-    const int incl = wave_incl_scan(nbk) + run;
-    const uint64_t hit = __ballot(incl > g);
-    if (hit) {
-      const int first = __builtin_ctzll(hit);
-      l = c0 + first;
-      b = g - (__shfl(incl, first) - __shfl(nbk, first));
-      return;
-    }
-    run = __shfl(incl, kWave - 1);
-  }
-  l = b = 0;
 }
 
 // Sum NV per-lane values over the wavefront.  On return the lane holds the
