@@ -48,6 +48,14 @@ __device__ __forceinline__ uint64_t match_key(int key, uint64_t active, int nbit
   return peers;
 }
 
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a __syncthreads() fence
+// would drain those too and stall a load pipeline at every barrier).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
 // Exclusive prefix sum, in place, of a[0..n) held in LDS, by the whole
 // workgroup (blockDim.x a multiple of 64, at most 1024).  `wtot` is LDS
 // scratch of at least 17 ints.  Returns the total to every thread.  Contains
@@ -88,6 +96,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// Raw buffer access: a wave-uniform descriptor (base, byte range) in scalar
+// registers, a 32-bit per-lane byte offset and a wave-uniform byte offset.
+// Reads past the range return zero.  Word 3 is the gfx9-family format word.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
+  return make_uint4(uint32_t(v.x), uint32_t(v.y), uint32_t(v.z), uint32_t(v.w));
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -224,6 +224,10 @@ EDGE = [
     dict(K=256, Ns=128, r=16, block_m=64, M=300, E=4, topk=3, x_per_pair=True, mul=True),
     dict(K=256, Ns=128, r=32, block_m=16, M=200, E=1024, topk=8, L=2, active=2),
     dict(K=64, Ns=64, r=16, block_m=16, M=70, E=3, L=100, active=70, p_neg=0.1),
+    # full decode blocks: many valid rows per block (4-row and looped passes)
+    dict(K=256, Ns=2184, r=64, block_m=16, M=64, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    dict(K=512, Ns=256, r=128, block_m=16, M=40, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    dict(K=2880, Ns=4096, r=32, block_m=32, M=48, E=3, topk=2, L=2, active=2, p_neg=0.0),
 ]
 
 
