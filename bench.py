@@ -326,21 +326,8 @@ def main(argv=None):
 
 
 def _uses_mfma(s, variant):
-    if variant == "mfma":
-        return True
-    if variant == "valu":
-        return False
-    groups = min(s.numel, s.L * s.E)
-    return (s.numel // max(groups, 1)) >= 8 and _mfma_available(s)
-
-
-def _mfma_available(s):
-    import ctypes
     import moe_lora_adapter_amd as mla
-    P = ctypes.c_void_p(16)
-    rc = mla.lib().fused_moe_lora(P, 0, P, P, P, P, P, None, 0, 1, 0, s.topk, s.K, s.Ns, s.S,
-                                  s.E, s.L, s.r, s.block_m, P, 2, None)
-    return rc == 0
+    return mla.fused_variant(s.M, s.topk, s.E, s.L, s.r, s.block_m, variant) == "mfma"
 
 
 if __name__ == "__main__":

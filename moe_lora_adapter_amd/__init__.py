@@ -35,6 +35,7 @@ SIGNATURES = {
     "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
+    "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32]),
 }
 
 
@@ -80,6 +81,16 @@ def align_workspace_bytes(M: int, topk: int, E: int, L: int, block_m: int) -> in
     if v < 0:
         raise MoeLoraError(v, "moe_lora_align_workspace_bytes")
     return int(v)
+
+
+def fused_variant(M: int, topk: int, E: int, L: int, r: int, block_m: int,
+                  variant: str | int = "auto") -> str:
+    """Name of the kernel ("valu" or "mfma") fused_moe_lora runs for these sizes."""
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    rc = lib().fused_moe_lora_variant(M, topk, E, L, r, block_m, v)
+    if rc < 0:
+        raise MoeLoraError(rc, "fused_moe_lora_variant")
+    return {VARIANT_VALU: "valu", VARIANT_MFMA: "mfma"}[rc]
 
 
 @dataclass

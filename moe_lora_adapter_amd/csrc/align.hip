@@ -30,12 +30,15 @@ __device__ __forceinline__ int pair_key(const AlignParams& a, int p) {
   return (unsigned(l) < unsigned(a.L) && unsigned(e) < unsigned(a.E)) ? l * a.E + e : -1;
 }
 
-// One wavefront counts pairs [s0, s1) into row[key] (LDS).
-__device__ void count_segment(const AlignParams& a, int s0, int s1, int* row) {
+// One wavefront counts pairs [s0, s1) into row[key] (LDS).  If keys is not
+// null the pair keys are also kept there (LDS, indexed by pair) for the
+// placement pass.
+__device__ void count_segment(const AlignParams& a, int s0, int s1, int* row, int* keys) {
   for (int base = s0; base < s1; base += kWave) {
     const int p = base + lane_id();
     if (p < s1) {
       const int key = pair_key(a, p);
+      if (keys) keys[p] = key;
       if (key >= 0) atomicAdd(&row[key], 1);
     }
   }
@@ -43,11 +46,12 @@ __device__ void count_segment(const AlignParams& a, int s0, int s1, int* row) {
 
 // One wavefront places pairs [s0, s1).  row[key] holds the position of the
 // next pair of that key; the lowest lane of each equal-key set advances it.
-__device__ void scatter_segment(const AlignParams& a, int s0, int s1, int* row) {
+// Keys come from LDS when keys is not null, else are recomputed.
+__device__ void scatter_segment(const AlignParams& a, int s0, int s1, int* row, const int* keys) {
   const int lane = lane_id();
   for (int base = s0; base < s1; base += kWave) {
     const int p = base + lane;
-    const int key = p < s1 ? pair_key(a, p) : -1;
+    const int key = p < s1 ? (keys ? keys[p] : pair_key(a, p)) : -1;
     const uint64_t valid = __ballot(key >= 0);
     if (valid == 0) continue;
     const uint64_t peers = match_key(key, valid, a.nbits);
@@ -114,11 +118,12 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
   int* off = tot + a.LE;          // [LE]
   int* sb = off + a.LE;           // [L + 1]
   int* wtot = sb + a.L + 1;       // [17]
+  int* keys = wtot + 17;          // [numel]: each pair's key, read once
   const int tid = threadIdx.x, w = wave_id();
   for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   const int s0 = w * a.seg, s1 = min(a.numel, s0 + a.seg);
-  if (w < a.W) count_segment(a, s0, s1, cnt + w * a.LE);
+  if (w < a.W) count_segment(a, s0, s1, cnt + w * a.LE, keys);
   __syncthreads();
   for (int key = tid; key < a.LE; key += blockDim.x) {
     int run = 0;
@@ -133,7 +138,7 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
   layout_groups(a, tot, off, sb, wtot);
   for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] += off[i % a.LE];
   __syncthreads();
-  if (w < a.W) scatter_segment(a, s0, s1, cnt + w * a.LE);
+  if (w < a.W) scatter_segment(a, s0, s1, cnt + w * a.LE, keys);
 }
 
 // ---------------------------------------------------------------- tiles
@@ -144,7 +149,7 @@ __global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
   for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
-  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE);
+  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE, nullptr);
   __syncthreads();
   for (int key = tid; key < a.LE; key += blockDim.x) {
     int sum = 0;
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(1024) align_tile_scatter_kernel(AlignParams a)
   for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
-  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE);
+  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE, nullptr);
   __syncthreads();
   for (int key = tid; key < a.LE; key += blockDim.x) {
     int run = a.key_off[key] + a.tile_cnt[t * a.LE + key];
@@ -195,7 +200,7 @@ __global__ void __launch_bounds__(1024) align_tile_scatter_kernel(AlignParams a)
     }
   }
   __syncthreads();
-  if (s0 < s1) scatter_segment(a, s0, s1, cnt + w * a.LE);
+  if (s0 < s1) scatter_segment(a, s0, s1, cnt + w * a.LE, nullptr);
 }
 
 // ---------------------------------------------------------------- host
@@ -205,7 +210,7 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   (void)B;
   AlignPlan pl{};
   const int64_t LE = int64_t(L) * E;
-  const int64_t fixed = 2 * LE + L + 1 + 17;
+  const int64_t fixed = 2 * LE + L + 1 + 17 + numel;   // tot, off, sb, wtot, keys
   const int64_t wmax_single = (kLdsInts - fixed) / LE;
   if (numel <= 4096 && wmax_single >= 1) {
     pl.single = true;

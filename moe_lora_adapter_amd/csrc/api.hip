@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "../../include/moe_lora.h"
+#include "common.h"
 #include "internal.h"
 
 using namespace mlr;
@@ -39,6 +40,18 @@ int check_sizes(int64_t M, int64_t topk, int64_t E, int64_t L, int64_t block_m,
   return MOE_LORA_OK;
 }
 
+// The kernel that runs; the sizes have been checked and, for MFMA, supported.
+int pick_variant(int64_t numel, int64_t E, int64_t L, int r, int block_m, int variant) {
+  if (variant != MOE_LORA_VARIANT_AUTO) return variant;
+  // expected valid rows per block: pairs over the groups they can fill.
+  // MFMA pays off once blocks are dense and the rank is large enough that
+  // the contraction, not the X / Y streams, carries the work (measured).
+  const int64_t groups = std::min<int64_t>(numel, L * E);
+  const int64_t rows_per_group = numel / std::max<int64_t>(groups, 1);
+  const bool mfma = mfma_supported(r, block_m) && rows_per_group >= 8 && r >= 64;
+  return mfma ? MOE_LORA_VARIANT_MFMA : MOE_LORA_VARIANT_VALU;
+}
+
 int nbits_for(int64_t keys) {
   int n = 0;
   while ((int64_t(1) << n) < keys) ++n;
@@ -46,6 +59,25 @@ int nbits_for(int64_t keys) {
 }
 
 }  // namespace
+
+namespace mlr {
+
+// The device's compute units over its XCDs; each device is queried once.  Two
+// threads that race on the first call store the same value.
+int xcd_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int per = cus / kXcds;
+  if (dev < kMaxDevices) cache[dev] = per;
+  return per;
+}
+
+}  // namespace mlr
 
 extern "C" {
 
@@ -176,21 +208,24 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
   p.cap = int32_t(cap);
   p.nb = int32_t(cap / block_m);
   p.units = int32_t(units);
+  p.xcd_cus = xcd_compute_units();
 
-  bool use_mfma = false;
-  if (variant == MOE_LORA_VARIANT_MFMA) {
-    use_mfma = true;
-  } else if (variant == MOE_LORA_VARIANT_AUTO) {
-    // expected valid rows per block: pairs over the groups they can fill.
-    // MFMA pays off once blocks are dense and the rank is large enough that
-    // the contraction, not the X / Y streams, carries the work (measured).
-    const int64_t groups = std::min<int64_t>(numel, int64_t(L) * E);
-    const int64_t rows_per_group = numel / std::max<int64_t>(groups, 1);
-    use_mfma = mfma_supported(r, block_m) && rows_per_group >= 8 && r >= 64;
-  }
+  const bool use_mfma = pick_variant(numel, E, L, r, block_m, variant) == MOE_LORA_VARIANT_MFMA;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t E, int32_t L, int32_t r,
+                           int32_t block_m, int32_t variant) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  if (r < 1 || variant < 0 || variant > 2) return MOE_LORA_ERR_INVALID;
+  if (r > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_supported(r, block_m))
+    return MOE_LORA_ERR_UNSUPPORTED;
+  return pick_variant(numel, E, L, r, block_m, variant);
 }
 
 }  // extern "C"

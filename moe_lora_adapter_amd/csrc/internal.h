@@ -51,6 +51,7 @@ struct FusedParams {
   int32_t numel, topk, K, Ns, S, E, L, r, B, N;
   int32_t cap, nb;
   int32_t units;       // upper bound on blocks, times S
+  int32_t xcd_cus;     // compute units per XCD of the current device
 };
 
 // Upper bound on the number of blocks over all slots: every non-empty
@@ -59,6 +60,9 @@ inline int64_t max_total_blocks(int64_t numel, int64_t LE, int64_t B) {
   const int64_t groups = numel < LE ? numel : LE;
   return (numel + groups * (B - 1)) / B;
 }
+
+// Compute units per XCD of the current device (cached per device).
+int xcd_compute_units();
 
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st);
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st);

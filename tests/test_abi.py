@@ -124,6 +124,33 @@ def test_fused_rejects(kw, status):
     assert fused_call(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=0), mla.ERR_INVALID),
+    (dict(r=129), mla.ERR_UNSUPPORTED),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(B=24), mla.ERR_UNSUPPORTED),
+    (dict(variant=3), mla.ERR_INVALID),
+    (dict(variant=mla.VARIANT_MFMA, r=12), mla.ERR_UNSUPPORTED),
+])
+def test_variant_query_rejects_like_fused(kw, status):
+    a = dict(M=16, topk=4, E=32, L=6, r=64, B=16, variant=0)
+    a.update(kw)
+    assert mla.lib().fused_moe_lora_variant(a["M"], a["topk"], a["E"], a["L"], a["r"], a["B"],
+                                            a["variant"]) == status
+    assert fused_call(**a) == status
+
+
+def test_variant_query_resolves_auto():
+    # decode: about two rows per (slot, expert) group -> vector kernel
+    assert mla.fused_variant(16, 4, 32, 6, 64, 16) == "valu"
+    # dense prefill blocks with a large rank -> MFMA kernel
+    assert mla.fused_variant(8192, 8, 128, 8, 128, 64) == "mfma"
+    # MFMA needs r % 8 == 0, so AUTO never picks it otherwise
+    assert mla.fused_variant(8192, 8, 128, 8, 100, 64) == "valu"
+    assert mla.fused_variant(16, 4, 32, 6, 64, 16, "mfma") == "mfma"
+    assert mla.fused_variant(8192, 8, 128, 8, 128, 64, "valu") == "valu"
+
+
 def test_binding_checks_dtypes_before_calling():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
