@@ -35,7 +35,8 @@ SIGNATURES = {
     "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
-    "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _I32]),
 }
 
 
@@ -83,11 +84,11 @@ def align_workspace_bytes(M: int, topk: int, E: int, L: int, block_m: int) -> in
     return int(v)
 
 
-def fused_variant(M: int, topk: int, E: int, L: int, r: int, block_m: int,
-                  variant: str | int = "auto") -> str:
+def fused_variant(M: int, topk: int, K: int, Ns: int, E: int, L: int, r: int, block_m: int,
+                  x_per_pair: bool = False, variant: str | int = "auto") -> str:
     """Name of the kernel ("valu" or "mfma") fused_moe_lora runs for these sizes."""
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    rc = lib().fused_moe_lora_variant(M, topk, E, L, r, block_m, v)
+    rc = lib().fused_moe_lora_variant(M, topk, K, Ns, E, L, r, block_m, int(bool(x_per_pair)), v)
     if rc < 0:
         raise MoeLoraError(rc, "fused_moe_lora_variant")
     return {VARIANT_VALU: "valu", VARIANT_MFMA: "mfma"}[rc]

@@ -39,4 +39,18 @@ __device__ __forceinline__ void find_block(const FusedParams& p, int g, int& l, 
   l = b = 0;
 }
 
+// Workgroup id -> (unit, split).  The units are cut into 8 contiguous ranges
+// of nearly equal size, range x for XCD x (workgroup i runs on XCD i % 8);
+// the splits of a unit take adjacent ids of one XCD.  Consecutive units --
+// the blocks of one (slot, expert) group, and the slices of a block -- thus
+// share an L2.  Returns false for a workgroup with no unit.
+__device__ __forceinline__ bool map_unit_xcd(int id, int units, int n_split, int& unit, int& split) {
+  const int x = id % kXcds, slot = id / kXcds;
+  const int lo = int(int64_t(x) * units / kXcds), hi = int(int64_t(x + 1) * units / kXcds);
+  const int local = slot / n_split;
+  split = slot - local * n_split;
+  unit = lo + local;
+  return unit < hi;
+}
+
 }  // namespace mlr

@@ -1,21 +1,26 @@
 // Fused shrink + expand on bf16 MFMA tiles (the prefill-sized path).
 //
-// One workgroup (4 wavefronts) handles one (block, slice, column split).
-// Rows of a block are taken 64 at a time:
+// One workgroup (4 wavefronts) handles one (block, slice, column split); the
+// rows of a block are taken up to 64 at a time (a "pass"), in 1, 2 or 4 row
+// tiles of 16 depending on how many of them hold valid pairs.
 //
-//   shrink  V[64 x RP] = X_rows[64 x K] . A[s,l,e][RP x K]^T with
-//           v_mfma_f32_16x16x32_bf16.  K advances in tiles of 64: the X rows
-//           (gathered through sorted_token_ids) and the A rows are staged in
-//           LDS, the next tile is fetched into registers while the current
-//           one is multiplied.  Wavefront w owns output rows 16w..16w+15 and
-//           all RP = r rounded up to 16 columns.
-//   v       rounded to bf16 into LDS (the expand's A operand), zero padded to
-//           RK = r rounded up to 32; it never leaves the chip.
-//   expand  D[64 x 16] per wavefront and column tile = V . B[cols][RK]^T,
-//           wavefront w taking columns 16w..16w+15 of every 64-column tile,
-//           with V held in registers and B read straight from global memory
-//           (each B element is read once).  The epilogue scales by the routed
-//           weight and adds onto Y (add_inputs) before the bf16 store.
+//   shrink  V[rows x r] = X[rows x K] . A[s,l,e][r x K]^T on
+//           v_mfma_f32_16x16x32_bf16.  K is streamed in stages of 64 (128 when
+//           the four wavefronts split K) through a ring of three LDS slots
+//           filled by buffer loads that write LDS directly: two stages are in
+//           flight while the third is multiplied, and no VGPR holds the
+//           staged data.  Rows of a stage are stored with their 16-byte chunks
+//           XOR-permuted by the row index, so the MFMA operand reads of 16
+//           rows spread over the LDS banks.  Loads past the end of a buffer
+//           return zero, which pads invalid rows, ranks >= r and the K tail.
+//   v       rounded to bf16 into LDS; it never leaves the chip.
+//   expand  every wavefront holds V of all rows of the pass as MFMA operands
+//           and takes a share of the output columns.  The product is formed
+//           transposed, D^T = B[cols] . V^T, so that a lane ends with four
+//           consecutive output columns of one row: the routed weight, the
+//           add onto Y and the bf16 rounding happen in registers and Y is
+//           read and written 8 bytes per lane.  B and Y of the next column
+//           group are loaded while the current one is multiplied.
 //
 // Operand layouts of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row
 // l % 16 of A and column l % 16 of B, each with eight consecutive k values
@@ -37,97 +42,389 @@ namespace mlr {
 namespace {
 
 constexpr int kThreadsM = 256;
-constexpr int kTileM = 64;    // rows per row tile
-constexpr int kTileK = 64;    // K per staged tile
-constexpr int kPitch = kTileK + 8;  // LDS row pitch (bf16) of X / A tiles
-constexpr int kMaxRP = 128;
-constexpr int kVPitch = kMaxRP + 8;  // LDS row pitch (bf16) of V
+constexpr int kWavesM = kThreadsM / kWave;
+constexpr int kPassRows = 64;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads 0
+constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 
-#ifndef MLR_MFMA_WG_TARGET
-#define MLR_MFMA_WG_TARGET 512
-#endif
 #ifndef MLR_MFMA_MIN_COLS
 #define MLR_MFMA_MIN_COLS 256
+#endif
+#ifndef MLR_MFMA_OCCUPANCY  // workgroups per compute unit the split count assumes
+#define MLR_MFMA_OCCUPANCY 2
 #endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Register staging of one K tile: X rows (64 x 64) and A rows (RP x 64), as
-// 16-byte chunks; each thread holds XC + AC chunks.
-template <int RT>
-struct TileRegs {
-  static constexpr int XC = kTileM * (kTileK / 8) / kThreadsM;                   // 2
-  static constexpr int ACN = ((RT * 16) * (kTileK / 8) + kThreadsM - 1) / kThreadsM;  // ceil
-  uint4 x[XC];
-  uint4 a[ACN];
+// Buffer resource (raw, 32-bit elements, no stride) as four scalar words, for
+// the inline DMA below.
+__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane buffer load written straight to LDS: lane i's chunk
+// lands at byte lds + 16 i.  Written as inline assembly so that the compiler
+// does not see an LDS store in flight; it would otherwise wait for every
+// outstanding stage before each LDS read.  The waits for these loads are the
+// explicit ones in stage_barrier.  M0 (the LDS base) is saved and restored.
+__device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// Wait until at most VM vector memory operations of this wavefront are
+// outstanding and its LDS operations are done, then meet the workgroup.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier; no release fence is used, since one would also wait for
+// the stages still in flight.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt is a 6-bit field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Shrink layout of a pass with MT row tiles and RT rank tiles (16 each).
+// The 4 wavefronts are arranged as MT row tiles x WR rank groups x WK parts
+// of K; a wavefront owns one row tile and TR rank tiles.
+template <int MT, int RT>
+struct Shrink {
+  static constexpr int RB = 16 * MT;                                // rows
+  static constexpr int RP = 16 * RT;                                // A rows staged
+  static constexpr int WR = RT < kWavesM / MT ? RT : kWavesM / MT;  // rank groups
+  static constexpr int WK = kWavesM / (MT * WR);                    // K parts
+  static constexpr int TR = (RT + WR - 1) / WR;                     // rank tiles per wave
+  static constexpr int KT = WK == 4 ? 128 : 64;                     // K per stage
+  static constexpr int CPR = KT / 8;                                // chunks per staged row
+  static constexpr int KSW = KT / WK / 32;                          // k-steps per wave, stage
+  static constexpr int XI = RB * CPR / kWave;                       // DMA instrs for X
+  static constexpr int AI = RP * CPR / kWave;                       // DMA instrs for A
+  static constexpr int IPW = (XI + AI + kWavesM - 1) / kWavesM;     // per wavefront
+  static constexpr int BYTES = kWavesM * IPW * kWave * 16;          // slot size
+  static_assert(KSW >= 1 && (RB * CPR) % kWave == 0 && (RP * CPR) % kWave == 0, "layout");
 };
 
-// Chunk c of a [rows x 8] chunk grid: row c / 8, chunk c % 8.
 template <int RT>
-__device__ __forceinline__ void fetch_tile(const FusedParams& p, const uint16_t* __restrict__ A,
-                                           const int* s_row, int k0, TileRegs<RT>& t) {
-  const int tid = threadIdx.x;
+struct Slots {
+  static constexpr int KS = (RT + 1) / 2;   // expand k-steps of 32 ranks
+  static constexpr int RK = 32 * KS;
+  static constexpr int VP = RK + 8;         // bf16 pitch of V rows in LDS
+  static constexpr int a = Shrink<1, RT>::BYTES, b = Shrink<2, RT>::BYTES, c = Shrink<4, RT>::BYTES;
+  static constexpr int ab = a > b ? a : b;
+  static constexpr int BYTES = ab > c ? ab : c;
+  static_assert(kPassRows * VP * 2 <= BYTES, "V must fit in one slot");
+  static_assert(kThreadsM * 4 * ((RT + 3) / 4) * 4 <= BYTES, "partials must fit in one slot");
+};
+
+struct PassCtx {
+  i32x4_t xr, ar;               // DMA sources: x, A[s,l,e]
+  __amdgpu_buffer_rsrc_t br;    // B[s,l,e]
+  uint8_t* ring;                // three slots of Slots<RT>::BYTES
+  uint32_t ring_lds;            // LDS byte address of ring
+  const int* s_row;    // X row per pass row, -1 = none
+  const int* s_pair;   // pair per pass row, numel = none
+  const float* s_wt;   // routed weight per pass row (1 when not applied)
+  int s, n0, n1;
+};
+
+// Per-lane DMA source of this wavefront's instructions (fixed over K).
+template <int IPW>
+struct DmaSrc {
+  int base[IPW];  // element offset of the chunk's row, -1 = zero fill
+  int c8[IPW];    // k offset of the chunk inside a stage
+};
+
+template <int MT, int RT>
+__device__ __forceinline__ void dma_plan(const FusedParams& p, const PassCtx& c, DmaSrc<Shrink<MT, RT>::IPW>& d) {
+  using S = Shrink<MT, RT>;
+  const int w = wave_id(), lane = lane_id();
 #pragma unroll
-  for (int q = 0; q < TileRegs<RT>::XC; ++q) {
-    const int c = q * kThreadsM + tid;
-    const int row = c >> 3, k = k0 + (c & 7) * 8;
-    const int xr = s_row[row];
-    t.x[q] = (xr >= 0 && k < p.K) ? ldg16(p.x + int64_t(xr) * p.K + k) : make_uint4(0, 0, 0, 0);
-  }
-  constexpr int RP = RT * 16;
-#pragma unroll
-  for (int q = 0; q < TileRegs<RT>::ACN; ++q) {
-    const int c = q * kThreadsM + tid;
-    const int j = c >> 3, k = k0 + (c & 7) * 8;
-    const bool ok = c < RP * 8 && j < p.r && k < p.K;
-    t.a[q] = ok ? ldg16(A + int64_t(j) * p.K + k) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < S::IPW; ++i) {
+    const int ins = w + kWavesM * i;
+    const int chunk = ins * kWave + lane;
+    const int q = chunk / S::CPR, j = chunk % S::CPR;
+    d.c8[i] = 8 * (j ^ (q & 7));
+    int base = -1;
+    if (ins < S::XI) {
+      const int xr = c.s_row[q];
+      if (xr >= 0) base = xr * p.K;
+    } else if (ins < S::XI + S::AI) {
+      const int jr = q - S::RB;
+      if (jr < p.r) base = jr * p.K;
+    }
+    d.base[i] = base;
   }
 }
 
-template <int RT>
-__device__ __forceinline__ void store_tile(const TileRegs<RT>& t, uint16_t* s_x, uint16_t* s_a) {
-  const int tid = threadIdx.x;
+template <int MT, int RT>
+__device__ __forceinline__ void dma_issue(const FusedParams& p, const PassCtx& c, const DmaSrc<Shrink<MT, RT>::IPW>& d,
+                                          int stage, uint32_t slot_lds) {
+  using S = Shrink<MT, RT>;
+  const int w = wave_id();
+  const int k0 = stage * S::KT;
 #pragma unroll
-  for (int q = 0; q < TileRegs<RT>::XC; ++q) {
-    const int c = q * kThreadsM + tid;
-    *reinterpret_cast<uint4*>(s_x + (c >> 3) * kPitch + (c & 7) * 8) = t.x[q];
-  }
-  constexpr int RP = RT * 16;
-#pragma unroll
-  for (int q = 0; q < TileRegs<RT>::ACN; ++q) {
-    const int c = q * kThreadsM + tid;
-    if (c < RP * 8) *reinterpret_cast<uint4*>(s_a + (c >> 3) * kPitch + (c & 7) * 8) = t.a[q];
+  for (int i = 0; i < S::IPW; ++i) {
+    const int ins = w + kWavesM * i;
+    const int k = k0 + d.c8[i];
+    const uint32_t off = (d.base[i] >= 0 && k < p.K) ? uint32_t(d.base[i] + k) * 2u : kOob;
+    dma16(ins < S::XI ? c.xr : c.ar, slot_lds + ins * (kWave * 16), off);
   }
 }
 
-template <int RT, int KS>
+// MFMAs of one staged K slice for this wavefront's tiles.
+template <int MT, int RT>
+__device__ __forceinline__ void shrink_compute(const uint8_t* slot, f32x4_t (&acc)[Shrink<MT, RT>::TR]) {
+  using S = Shrink<MT, RT>;
+  // all four wavefronts have a tile unless WR does not divide the rank tiles
+  constexpr bool kAllBusy = MT * S::WR * S::WK == kWavesM;
+  constexpr bool kAllRanks = RT % S::WR == 0;
+  const int w = wave_id(), lane = lane_id();
+  if (!kAllBusy && w >= MT * S::WR * S::WK) return;
+  const int mt = w % MT, wr = (w / MT) % S::WR, kp = w / (MT * S::WR);
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint4* st = reinterpret_cast<const uint4*>(slot);
+#pragma unroll
+  for (int ks = 0; ks < S::KSW; ++ks) {
+    const int ch = 4 * (kp * S::KSW + ks) + lq;
+    const int qx = 16 * mt + lr;
+    const uint4 xa = st[qx * S::CPR + (ch ^ (qx & 7))];
+#pragma unroll
+    for (int tr = 0; tr < S::TR; ++tr) {
+      const int rt = wr + tr * S::WR;
+      if (kAllRanks || rt < RT) {
+        const int qa = S::RB + 16 * rt + lr;
+        const uint4 ab = st[qa * S::CPR + (ch ^ (qa & 7))];
+        acc[tr] = mfma16(xa, ab, acc[tr]);
+      }
+    }
+  }
+}
+
+// One ring step: stage t is complete once at most one later stage of this
+// wavefront is still loading; then stage t + 2 goes into the slot of t - 1,
+// which every wavefront has finished with (it passed the barrier).
+template <int MT, int RT>
+__device__ __forceinline__ void shrink_step(const FusedParams& p, const PassCtx& c, const DmaSrc<Shrink<MT, RT>::IPW>& d,
+                                            int t, int nst, f32x4_t (&acc)[Shrink<MT, RT>::TR]) {
+  using S = Shrink<MT, RT>;
+  constexpr int SB = Slots<RT>::BYTES;
+  if (t + 1 < nst) stage_barrier<S::IPW>();
+  else stage_barrier<0>();
+  const int cur = t % 3, nxt = (t + 2) % 3;
+  if (t + 2 < nst) dma_issue<MT, RT>(p, c, d, t + 2, c.ring_lds + nxt * SB);
+  shrink_compute<MT, RT>(c.ring + cur * SB, acc);
+}
+
+// B chunks and Y values of one column group of the expand.
+template <int MT, int KS, int CTW>
+struct ExpandRegs {
+  uint4 b[CTW][KS];
+  uint2 y[CTW][MT];
+};
+
+// Loads of column group nb: every load is issued (out-of-range B chunks read
+// as zero through the buffer resource, Y of an invalid row or column reads
+// row 0 and is not used), so no load sits behind a per-lane branch.
+template <int MT, int KS, int CTW>
+__device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx& c, int nb,
+                                            const int64_t (&yrow)[MT], ExpandRegs<MT, KS, CTW>& r) {
+  const int w = wave_id(), lane = lane_id();
+  const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CTW; ++i) {
+    const int n = nb + 16 * (w + 4 * i) + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int j = 32 * ks + 8 * lq;
+      const uint32_t off = (n < c.n1 && j < p.r) ? uint32_t(n * p.r + j) * 2u : kOob;
+      r.b[i][ks] = buf_ld16(c.br, off, 0);
+    }
+  }
+  if (p.add) {
+#pragma unroll
+    for (int i = 0; i < CTW; ++i) {
+      const int n = nb + 16 * (w + 4 * i) + 4 * lq;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int64_t at = n < c.n1 ? yrow[m] + n : 0;
+        r.y[i][m] = *reinterpret_cast<const uint2*>(p.y + at);
+      }
+    }
+  }
+}
+
+// MFMAs and the epilogue of column group nb.
+template <int MT, int KS, int CTW>
+__device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx& c, int nb,
+                                             const int64_t (&yrow)[MT], const bool (&rv)[MT],
+                                             const float (&wt)[MT], const uint4 (&va)[MT][KS],
+                                             const ExpandRegs<MT, KS, CTW>& r) {
+  const int w = wave_id(), lane = lane_id();
+  const int lq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CTW; ++i) {
+    const int n = nb + 16 * (w + 4 * i) + 4 * lq;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dt = mfma16(r.b[i][ks], va[m][ks], dt);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = dt[e] * wt[m];
+      if (p.add) {
+        o[0] += bf16_lo(r.y[i][m].x);
+        o[1] += bf16_hi(r.y[i][m].x);
+        o[2] += bf16_lo(r.y[i][m].y);
+        o[3] += bf16_hi(r.y[i][m].y);
+      }
+      if (rv[m] && n < c.n1) {
+        const uint2 out = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
+                                     uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+        *reinterpret_cast<uint2*>(p.y + yrow[m] + n) = out;
+      }
+    }
+  }
+}
+
+template <int MT, int RT>
+__device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c) {
+  using S = Shrink<MT, RT>;
+  using SS = Slots<RT>;
+  constexpr int KS = SS::KS, VP = SS::VP;
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const int lr = lane & 15, lq = lane >> 4;
+
+  // ---------------- shrink
+  DmaSrc<S::IPW> d;
+  dma_plan<MT, RT>(p, c, d);
+  const int nst = (p.K + S::KT - 1) / S::KT;
+  dma_issue<MT, RT>(p, c, d, 0, c.ring_lds);
+  if (nst > 1) dma_issue<MT, RT>(p, c, d, 1, c.ring_lds + SS::BYTES);
+  f32x4_t acc[S::TR];
+#pragma unroll
+  for (int i = 0; i < S::TR; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < nst; ++t) shrink_step<MT, RT>(p, c, d, t, nst, acc);
+  stage_barrier<0>();  // every wavefront is done with the ring
+
+  // K parts -> one sum (slot 1 holds the partials of parts 1..WK-1)
+  const bool owner = w < MT * S::WR;
+  if constexpr (S::WK > 1) {
+    float* part = reinterpret_cast<float*>(c.ring + SS::BYTES);
+    if (!owner && w < MT * S::WR * S::WK) {
+#pragma unroll
+      for (int i = 0; i < S::TR; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[((w * S::TR + i) * 4 + e) * kWave + lane] = acc[i][e];
+    }
+    stage_barrier<0>();
+    if (owner) {
+#pragma unroll
+      for (int kp = 1; kp < S::WK; ++kp) {
+        const int src = w + kp * MT * S::WR;
+#pragma unroll
+        for (int i = 0; i < S::TR; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] += part[((src * S::TR + i) * 4 + e) * kWave + lane];
+      }
+    }
+  }
+  // V -> bf16 rows of slot 0, zero from RP up to RK
+  uint16_t* s_v = reinterpret_cast<uint16_t*>(c.ring);
+  if (owner) {
+    const int mt = w % MT, wr = (w / MT) % S::WR;
+#pragma unroll
+    for (int i = 0; i < S::TR; ++i) {
+      const int rt = wr + i * S::WR;
+      if (rt < RT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_v[(16 * mt + 4 * lq + e) * VP + 16 * rt + lr] = f32_to_bf16(acc[i][e]);
+      }
+    }
+  }
+  if constexpr (SS::RK > S::RP) {
+    for (int i = tid; i < S::RB * (SS::RK - S::RP); i += kThreadsM)
+      s_v[(i / (SS::RK - S::RP)) * VP + S::RP + i % (SS::RK - S::RP)] = 0;
+  }
+  stage_barrier<0>();
+
+  // ---------------- expand
+  // wavefront w: all MT row tiles, column tiles w + 4 i (i < CTW) of each
+  // group of 64 * CTW columns
+  constexpr int CTW0 = 8 / (MT * KS);
+  constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);
+  constexpr int NCG = 64 * CTW;
+  ExpandRegs<MT, KS, CTW> cur, nxt;
+  uint4 va[MT][KS];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      va[m][ks] = *reinterpret_cast<const uint4*>(s_v + (16 * m + lr) * VP + 32 * ks + 8 * lq);
+  // per row tile: this lane's output row as an element offset into y (row 0
+  // for an invalid row, which is then neither stored nor used) and its weight
+  int64_t yrow[MT];
+  bool rv[MT];
+  float wt[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int pid = c.s_pair[16 * m + lr];
+    rv[m] = pid < p.numel;
+    yrow[m] = rv[m] ? int64_t(pid) * p.N + int64_t(c.s) * p.Ns : 0;
+    wt[m] = c.s_wt[16 * m + lr];
+  }
+  expand_load<MT, KS, CTW>(p, c, c.n0, yrow, cur);
+  for (int nb = c.n0; nb < c.n1; nb += 2 * NCG) {
+    if (nb + NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + NCG, yrow, nxt);
+    expand_store<MT, KS, CTW>(p, c, nb, yrow, rv, wt, va, cur);
+    if (nb + NCG >= c.n1) break;
+    if (nb + 2 * NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + 2 * NCG, yrow, cur);
+    expand_store<MT, KS, CTW>(p, c, nb + NCG, yrow, rv, wt, va, nxt);
+  }
+  stage_barrier<0>();  // V (slot 0) and the row tables are reused by the next pass
+}
+
+template <int RT>
 __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
-  constexpr int RP = RT * 16;
-  constexpr int RK = KS * 32;
-  __shared__ int s_pair[kTileM];
-  __shared__ int s_row[kTileM];
-  __shared__ __align__(16) uint16_t s_x[kTileM * kPitch];
-  __shared__ __align__(16) uint16_t s_a[RP * kPitch];
-  __shared__ __align__(16) uint16_t s_v[kTileM * kVPitch];
+  __shared__ __align__(16) uint8_t ring[3 * Slots<RT>::BYTES];
+  __shared__ int s_row[kPassRows];
+  __shared__ int s_pair[kPassRows];
+  __shared__ float s_wt[kPassRows];
 
+  // units = (block, slice); the split count gives every working workgroup a
+  // slot (MLR_MFMA_OCCUPANCY per compute unit), at least MLR_MFMA_MIN_COLS
+  // columns each
   const int total = __builtin_amdgcn_readfirstlane(count_blocks(p));
   const int units = total * p.S;
-  const int u8 = (units + kXcds - 1) / kXcds * kXcds;
+  const int per_xcd = (units + kXcds - 1) / kXcds;
   const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
-  const int n_split = min(max_split, max(1, (MLR_MFMA_WG_TARGET + u8 - 1) / max(u8, 1)));
-  const int id = blockIdx.x;
-  const int split = id / max(u8, 1), unit = id - split * u8;
-  if (unit >= units || split >= n_split) return;
+  const int n_split = min(max_split, max(1, p.xcd_cus * MLR_MFMA_OCCUPANCY / max(per_xcd, 1)));
+  int unit, split;
+  if (!map_unit_xcd(blockIdx.x, units, n_split, unit, split)) return;
   const int nsz = ((p.Ns + n_split - 1) / n_split + 15) / 16 * 16;
   const int n0 = split * nsz;
   if (n0 >= p.Ns) return;
@@ -139,146 +436,77 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   b = __builtin_amdgcn_readfirstlane(b);
   const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
-  const uint16_t* A = p.a + wsel * p.r * p.K;
-  const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
 
-  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
-  const int lr = lane & 15, lq = lane >> 4;
+  PassCtx c;
+  const int64_t x_rows = p.x_per_pair ? int64_t(p.numel) : int64_t(p.numel / p.topk);
+  c.xr = dma_rsrc(p.x, uint32_t(x_rows * p.K * 2));
+  c.ar = dma_rsrc(p.a + wsel * p.r * p.K, uint32_t(p.r * p.K * 2));
+  c.br = make_rsrc(p.b + wsel * p.Ns * p.r, uint32_t(p.Ns * p.r * 2));
+  c.ring = ring;
+  c.ring_lds = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_u8_t*)ring)));
+  c.s_row = s_row;
+  c.s_pair = s_pair;
+  c.s_wt = s_wt;
+  c.s = s;
+  c.n0 = n0;
+  c.n1 = n1;
 
-  for (int rt0 = 0; rt0 < p.B; rt0 += kTileM) {
-    // rows of this tile: X row index (-1 = no row) and pair index
-    if (tid < kTileM) {
+  const int tid = threadIdx.x;
+  for (int r0 = 0; r0 < p.B; r0 += kPassRows) {
+    if (tid < kPassRows) {
       int pid = p.numel, xr = -1;
-      if (rt0 + tid < p.B) {
-        pid = p.sorted[l * p.cap + b * p.B + rt0 + tid];
-        if (pid < p.numel) xr = p.x_per_pair ? pid : pid / p.topk;
+      float wv = 1.f;
+      if (r0 + tid < p.B) {
+        pid = p.sorted[l * p.cap + b * p.B + r0 + tid];
+        if (pid < p.numel) {
+          xr = p.x_per_pair ? pid : pid / p.topk;
+          if (p.mul) wv = p.w[pid];
+        } else {
+          pid = p.numel;
+        }
       }
       s_pair[tid] = pid;
       s_row[tid] = xr;
+      s_wt[tid] = wv;
     }
-    const int nv = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kTileM && s_row[tid] >= 0 ? 1 : 0));
-    if (nv == 0) break;  // only sentinels from here on
-
-    // ---------------- shrink
-    f32x4_t acc[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    TileRegs<RT> regs;
-    fetch_tile<RT>(p, A, s_row, 0, regs);
-    for (int k0 = 0; k0 < p.K; k0 += kTileK) {
-      __syncthreads();  // previous tile fully consumed
-      store_tile<RT>(regs, s_x, s_a);
-      __syncthreads();
-      if (k0 + kTileK < p.K) fetch_tile<RT>(p, A, s_row, k0 + kTileK, regs);
-#pragma unroll
-      for (int ks = 0; ks < kTileK / 32; ++ks) {
-        const uint4 xa = *reinterpret_cast<const uint4*>(s_x + (16 * w + lr) * kPitch + ks * 32 + lq * 8);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          const uint4 ab = *reinterpret_cast<const uint4*>(s_a + (16 * t + lr) * kPitch + ks * 32 + lq * 8);
-          acc[t] = mfma16(xa, ab, acc[t]);
-        }
-      }
-    }
-    // V (fp32, MFMA layout) -> bf16 rows of s_v, zero past RP up to RK
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_v[(16 * w + 4 * lq + i) * kVPitch + 16 * t + lr] = f32_to_bf16(acc[t][i]);
-    if constexpr (RK > RP) {
-      for (int c = tid; c < kTileM * (RK - RP); c += kThreadsM)
-        s_v[(c / (RK - RP)) * kVPitch + RP + c % (RK - RP)] = 0;
-    }
-    __syncthreads();
-
-    // ---------------- expand: V (all 64 rows) in registers as MFMA A operands
-    uint4 va[4][KS];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        va[rt][ks] = *reinterpret_cast<const uint4*>(s_v + (16 * rt + lr) * kVPitch + ks * 32 + lq * 8);
-    float wrow[4][4];
-    int prow[4][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rt + 4 * lq + i;
-        const int pid = s_pair[row];
-        prow[rt][i] = pid;
-        wrow[rt][i] = (p.mul && pid < p.numel) ? p.w[pid] : 1.f;
-      }
-    const int col_base = s * p.Ns;
-    for (int nt = n0 + 16 * w; nt < n1; nt += 64) {
-      const int n = nt + lr;
-      uint4 bb[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int j = ks * 32 + lq * 8;
-        bb[ks] = (n < n1 && j < p.r) ? ldg16(Bm + int64_t(n) * p.r + j) : make_uint4(0, 0, 0, 0);
-      }
-      uint16_t yin[4][4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pid = prow[rt][i];
-          yin[rt][i] = (p.add && pid < p.numel && n < n1) ? p.y[int64_t(pid) * p.N + col_base + n] : uint16_t(0);
-        }
-      f32x4_t d[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        d[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) d[rt] = mfma16(va[rt][ks], bb[ks], d[rt]);
-      }
-      if (n < n1) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int pid = prow[rt][i];
-            if (pid < p.numel) {
-              float val = d[rt][i] * wrow[rt][i];
-              if (p.add) val += bf16_to_f32(yin[rt][i]);
-              p.y[int64_t(pid) * p.N + col_base + n] = f32_to_bf16(val);
-            }
-          }
-      }
-    }
-    __syncthreads();  // s_row / s_pair / s_v reused by the next row tile
+    // valid rows are a prefix of the block (sentinels only pad a group's end)
+    const int nv = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kPassRows && s_row[tid] >= 0));
+    if (nv == 0) break;
+    if (nv <= 16) run_pass<1, RT>(p, c);
+    else if (nv <= 32) run_pass<2, RT>(p, c);
+    else run_pass<4, RT>(p, c);
   }
-}
-
-// RT = ceil(r / 16) row tiles of the shrink, KS = ceil(r / 32) K steps of the
-// expand; KS is fixed by RT.
-template <int RT>
-void launch_rt(const FusedParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((fused_mfma_kernel<RT, (RT + 1) / 2>), grid, dim3(kThreadsM), 0, st, p);
 }
 
 }  // namespace
 
 // B rows are read as 16-byte chunks of 8 ranks, so r must be a multiple of 8.
 bool mfma_supported(int r, int B) {
-  return r >= 8 && r <= kMaxRP && r % 8 == 0 && B >= 16 && B <= 128;
+  return r >= 8 && r <= 16 * 8 && r % 8 == 0 && B >= 16 && B <= 128;
+}
+
+// Every buffer the kernel reads through a buffer resource stays below 2 GiB,
+// so that one offset past the end (kOob) is out of range for all of them.
+bool mfma_fits(int64_t x_bytes, int64_t r, int64_t K, int64_t Ns) {
+  return x_bytes <= kMaxXBytes && r * K * 2 <= kMaxXBytes && r * Ns * 2 <= kMaxXBytes;
 }
 
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st) {
   const int rt = (p.r + 15) / 16;
-  const int64_t units_pad = (int64_t(p.units) + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid(unsigned(MLR_MFMA_WG_TARGET + units_pad));
+  // grid: 8 XCD ranges of ceil(units / 8) units times the split count, which
+  // the kernel keeps within xcd_cus * MLR_MFMA_OCCUPANCY slots per XCD
+  const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
+  const int64_t slots = std::max<int64_t>(per_xcd, int64_t(p.xcd_cus) * MLR_MFMA_OCCUPANCY);
+  const dim3 grid(unsigned(kXcds * slots));
   switch (rt) {
-    case 1: launch_rt<1>(p, grid, st); break;
-    case 2: launch_rt<2>(p, grid, st); break;
-    case 3: launch_rt<3>(p, grid, st); break;
-    case 4: launch_rt<4>(p, grid, st); break;
-    case 5: launch_rt<5>(p, grid, st); break;
-    case 6: launch_rt<6>(p, grid, st); break;
-    case 7: launch_rt<7>(p, grid, st); break;
-    default: launch_rt<8>(p, grid, st); break;
+    case 1: hipLaunchKernelGGL(fused_mfma_kernel<1>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 2: hipLaunchKernelGGL(fused_mfma_kernel<2>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 3: hipLaunchKernelGGL(fused_mfma_kernel<3>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 4: hipLaunchKernelGGL(fused_mfma_kernel<4>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 5: hipLaunchKernelGGL(fused_mfma_kernel<5>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 6: hipLaunchKernelGGL(fused_mfma_kernel<6>, grid, dim3(kThreadsM), 0, st, p); break;
+    case 7: hipLaunchKernelGGL(fused_mfma_kernel<7>, grid, dim3(kThreadsM), 0, st, p); break;
+    default: hipLaunchKernelGGL(fused_mfma_kernel<8>, grid, dim3(kThreadsM), 0, st, p); break;
   }
   return hipGetLastError();
 }

@@ -228,6 +228,19 @@ EDGE = [
     dict(K=256, Ns=2184, r=64, block_m=16, M=64, E=2, topk=1, L=1, active=1, p_neg=0.0),
     dict(K=512, Ns=256, r=128, block_m=16, M=40, E=2, topk=1, L=1, active=1, p_neg=0.0),
     dict(K=2880, Ns=4096, r=32, block_m=32, M=48, E=3, topk=2, L=2, active=2, p_neg=0.0),
+    # MFMA passes of 1, 2 and 4 row tiles; K and column tails; odd rank tiles
+    # (r = 40: three tiles, one idle wavefront when they are split by rank)
+    dict(K=200, Ns=200, r=40, block_m=64, M=256, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    # block_m = 128: two passes of 64 rows, rank 24 and 128
+    dict(K=136, Ns=72, r=24, block_m=128, M=400, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    dict(K=256, Ns=136, r=128, block_m=128, M=300, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    # small ranks with few rows per block: K split over the wavefronts
+    dict(K=392, Ns=104, r=8, block_m=32, M=40, E=4, topk=2, L=2, active=2),
+    dict(K=328, Ns=88, r=32, block_m=64, M=24, E=2, topk=2, L=2, active=2),
+    # ranks that are not a multiple of 16 / 32
+    dict(K=320, Ns=96, r=96, block_m=32, M=64, E=2, topk=2, L=1, active=1, p_neg=0.0),
+    dict(K=128, Ns=48, r=120, block_m=64, M=100, E=2, topk=1, L=1, active=1, mul=True),
+    dict(K=136, Ns=64, r=56, block_m=16, M=50, E=3, topk=2, L=2, active=2, x_per_pair=True),
 ]
 
 
