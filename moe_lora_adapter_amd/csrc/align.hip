@@ -68,7 +68,8 @@ __device__ void scatter_segment(const AlignParams& a, int s0, int s1, int* row, 
 // From per-key pair counts: padded group starts (within the slot) in off[],
 // slot starts in sb[0..L], and the outputs num_tokens_post_padded,
 // expert_ids, padding sentinels, lora_ids and num_active.  All threads of the
-// workgroup call it (barriers inside).  tot may live in LDS or global memory.
+// workgroup call it (barriers inside).  tot may live in LDS or in global
+// memory written by this workgroup before the call (the barriers order it).
 __device__ void layout_groups(const AlignParams& a, const int* tot, int* off, int* sb,
                               int* wtot) {
   const int tid = threadIdx.x;
@@ -80,15 +81,37 @@ __device__ void layout_groups(const AlignParams& a, const int* tot, int* off, in
   const int total = block_excl_scan(off, a.LE, wtot);
   for (int l = tid; l <= a.L; l += blockDim.x) sb[l] = l < a.L ? off[l * a.E] : total;
   __syncthreads();
-  for (int key = tid; key < a.LE; key += blockDim.x) {
-    const int l = key / a.E, e = key - l * a.E;
-    const int o = off[key] - sb[l];
-    const int c = tot[key];
-    const int P = (c + a.B - 1) / a.B * a.B;
-    int32_t* srow = a.sorted + l * a.cap;
-    int32_t* erow = a.eids + l * a.nb;
-    for (int blk = o / a.B; blk < (o + P) / a.B; ++blk) erow[blk] = e;
-    for (int i = o + c; i < o + P; ++i) srow[i] = a.numel;
+  // a group's expert ids and padding sentinels are consecutive: block_m / 4
+  // lanes share a group (at most three stores each), so a store instruction
+  // touches a few cache lines instead of one per lane.  The counts of
+  // kFillBatch rounds are loaded before any is used (tot may be global).
+  constexpr int kFillBatch = 8;
+  const int lpk = a.B / 4;
+  const int kpw = kWave / lpk;
+  const int lane = lane_id(), nw = blockDim.x / kWave;
+  const int sub = lane / lpk, sl = lane % lpk;
+  const int stride = nw * kpw;
+  for (int key0 = wave_id() * kpw + sub; key0 < a.LE; key0 += kFillBatch * stride) {
+    int cs[kFillBatch];
+#pragma unroll
+    for (int j = 0; j < kFillBatch; ++j) {
+      const int key = key0 + j * stride;
+      cs[j] = key < a.LE ? tot[key] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kFillBatch; ++j) {
+      const int key = key0 + j * stride;
+      if (key < a.LE) {
+        const int l = key / a.E, e = key - l * a.E;
+        const int o = off[key] - sb[l];
+        const int c = cs[j];
+        const int P = (c + a.B - 1) / a.B * a.B;
+        int32_t* srow = a.sorted + l * a.cap + o;
+        int32_t* erow = a.eids + l * a.nb + o / a.B;
+        for (int blk = sl; blk < P / a.B; blk += lpk) erow[blk] = e;
+        for (int i = c + sl; i < P; i += lpk) srow[i] = a.numel;
+      }
+    }
   }
   __syncthreads();
   for (int key = tid; key < a.LE; key += blockDim.x) off[key] -= sb[key / a.E];
@@ -158,27 +181,33 @@ __global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
   }
 }
 
-// Per key: exclusive prefix of the tile counts over tiles, and the total.
-__global__ void __launch_bounds__(256) align_tile_prefix_kernel(AlignParams a) {
-  const int key = blockIdx.x * blockDim.x + threadIdx.x;
-  if (key >= a.LE) return;
-  int run = 0;
-#pragma unroll 8
-  for (int t = 0; t < a.ntiles; ++t) {
-    int* c = a.tile_cnt + t * a.LE + key;
-    const int v = *c;
-    *c = run;
-    run += v;
-  }
-  a.key_tot[key] = run;
-}
-
+// One workgroup: per key, the exclusive prefix of the tile counts over tiles
+// (written back in place) and the total, then the layout of all groups.  The
+// counts of kPrefixBatch tiles are loaded before any is summed.  The totals
+// pass through key_off, each read back only by the thread that wrote it,
+// before key_off receives the group starts.
+constexpr int kPrefixBatch = 32;
 __global__ void __launch_bounds__(1024) align_meta_kernel(AlignParams a) {
   extern __shared__ int smem[];
   int* off = smem;            // [LE]
   int* sb = off + a.LE;       // [L + 1]
   int* wtot = sb + a.L + 1;   // [17]
-  layout_groups(a, a.key_tot, off, sb, wtot);
+  for (int key = threadIdx.x; key < a.LE; key += blockDim.x) {
+    int run = 0;
+    for (int t0 = 0; t0 < a.ntiles; t0 += kPrefixBatch) {
+      int v[kPrefixBatch];
+#pragma unroll
+      for (int i = 0; i < kPrefixBatch; ++i)
+        v[i] = t0 + i < a.ntiles ? a.tile_cnt[(t0 + i) * a.LE + key] : 0;
+#pragma unroll
+      for (int i = 0; i < kPrefixBatch; ++i) {
+        if (t0 + i < a.ntiles) a.tile_cnt[(t0 + i) * a.LE + key] = run;
+        run += v[i];
+      }
+    }
+    a.key_off[key] = run;
+  }
+  layout_groups(a, a.key_off, off, sb, wtot);
   for (int key = threadIdx.x; key < a.LE; key += blockDim.x) a.key_off[key] = off[key];
 }
 
@@ -221,8 +250,7 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
     pl.W = int(W);
     pl.seg = int(seg);
     pl.ntiles = 1;
-    const int64_t waves = std::min<int64_t>(16, std::max<int64_t>(W, cdiv(LE, kWave)));
-    pl.threads = int(waves * kWave);
+    pl.threads = 16 * kWave;  // all waves help with the layout and the padding
     pl.lds_bytes = size_t((W * LE + fixed) * 4);
     pl.ws_bytes = 0;
     return pl;
@@ -240,7 +268,7 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   pl.threads = int(W * kWave);
   pl.lds_bytes = size_t(W * LE * 4);
   pl.meta_lds_bytes = size_t((LE + L + 1 + 17) * 4);
-  pl.ws_bytes = (ntiles * LE + 2 * LE) * 4;
+  pl.ws_bytes = (ntiles * LE + LE) * 4;
   return pl;
 }
 
@@ -250,8 +278,6 @@ hipError_t launch_align(const AlignPlan& pl, const AlignParams& a, hipStream_t s
     return hipGetLastError();
   }
   hipLaunchKernelGGL(align_tile_count_kernel, dim3(pl.ntiles), dim3(pl.threads), pl.lds_bytes,
-                     st, a);
-  hipLaunchKernelGGL(align_tile_prefix_kernel, dim3(unsigned(cdiv(a.LE, 256))), dim3(256), 0,
                      st, a);
   hipLaunchKernelGGL(align_meta_kernel, dim3(1), dim3(1024), pl.meta_lds_bytes, st, a);
   hipLaunchKernelGGL(align_tile_scatter_kernel, dim3(pl.ntiles), dim3(pl.threads),

@@ -51,12 +51,12 @@ bool mfma_ok(int64_t M, int64_t numel, int64_t K, int64_t Ns, int r, int block_m
 int pick_variant(int64_t M, int64_t numel, int64_t K, int64_t Ns, int64_t E, int64_t L, int r,
                  int block_m, int x_per_pair, int variant) {
   if (variant != MOE_LORA_VARIANT_AUTO) return variant;
-  // expected valid rows per block: pairs over the groups they can fill.
-  // MFMA pays off once blocks are dense and the rank is large enough that
-  // the contraction, not the X / Y streams, carries the work (measured).
-  const int64_t groups = std::min<int64_t>(numel, L * E);
-  const int64_t rows_per_group = numel / std::max<int64_t>(groups, 1);
-  const bool mfma = mfma_ok(M, numel, K, Ns, r, block_m, x_per_pair) && rows_per_group >= 8 && r >= 64;
+  // Expected valid rows per (slot, expert) group: below one half, most
+  // blocks hold one or two rows and the vector kernel, which streams A and B
+  // with no padded rows, is faster; from there on the MFMA kernel is
+  // (measured on MI355X: gpt-oss-20b-like w13 at 0.33 rows per group 28 vs
+  // 33 us, at 1.3 rows per group 82 vs 60 us).
+  const bool mfma = mfma_ok(M, numel, K, Ns, r, block_m, x_per_pair) && 2 * numel >= L * E;
   return mfma ? MOE_LORA_VARIANT_MFMA : MOE_LORA_VARIANT_VALU;
 }
 
@@ -155,8 +155,7 @@ int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, i
   if (!plan.single) {
     int32_t* ws = static_cast<int32_t*>(workspace);
     a.tile_cnt = ws;
-    a.key_tot = ws + int64_t(plan.ntiles) * a.LE;
-    a.key_off = a.key_tot + a.LE;
+    a.key_off = ws + int64_t(plan.ntiles) * a.LE;
   }
   const hipError_t err = launch_align(plan, a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;

@@ -153,6 +153,10 @@ def test_variant_query_resolves_auto():
     assert fv(8192, 8, 2048, 768, 128, 8, 128, 64) == "mfma"
     # MFMA needs r % 8 == 0, so AUTO never picks it otherwise
     assert fv(8192, 8, 2048, 768, 128, 8, 100, 64) == "valu"
+    # from half a row per (slot, expert) group on, small ranks take MFMA too
+    assert fv(2048, 4, 2880, 2880, 128, 4, 16, 64) == "mfma"
+    assert fv(64, 4, 2880, 2880, 128, 4, 16, 64) == "mfma"
+    assert fv(63, 4, 2880, 2880, 128, 4, 16, 64) == "valu"
     # an x above 2 GiB keeps AUTO on the vector kernel
     assert fv(262145, 8, 4096, 768, 128, 8, 128, 64) == "valu"
     assert fv(16, 4, 2880, 2880, 32, 6, 64, 16, variant="mfma") == "mfma"
