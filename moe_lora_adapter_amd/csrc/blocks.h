@@ -19,6 +19,31 @@ __device__ __forceinline__ int count_blocks(const FusedParams& p) {
   return run;
 }
 
+// Block counts of the first 64 slots, read once and kept in registers: the
+// block count over all slots and the slot lookup then need no second read of
+// num_tokens_post_padded (more than 64 slots fall back to the loops above and
+// below).
+struct BlockScan {
+  int nbk;    // blocks of slot lane_id()
+  int incl;   // inclusive prefix of nbk over the lanes
+  int total;  // blocks over all slots
+};
+
+__device__ __forceinline__ BlockScan scan_blocks(const FusedParams& p) {
+  BlockScan sc;
+  if (p.L <= kWave) {
+    const int sl = lane_id();
+    sc.nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
+    sc.incl = wave_incl_scan(sc.nbk);
+    sc.total = __shfl(sc.incl, kWave - 1);
+  } else {
+    sc.nbk = sc.incl = 0;
+    sc.total = count_blocks(p);
+  }
+  sc.total = __builtin_amdgcn_readfirstlane(sc.total);
+  return sc;
+}
+
 // Block g (g < total) -> slot l and block b inside the slot.  Every lane of
 // the wavefront gets the same answer.
 __device__ __forceinline__ void find_block(const FusedParams& p, int g, int& l, int& b) {
@@ -51,6 +76,21 @@ __device__ __forceinline__ bool map_unit_xcd(int id, int units, int n_split, int
   split = slot - local * n_split;
   unit = lo + local;
   return unit < hi;
+}
+
+// The same lookup from the registers of scan_blocks.
+__device__ __forceinline__ void find_block(const FusedParams& p, const BlockScan& sc, int g, int& l,
+                                           int& b) {
+  if (p.L <= kWave) {
+    const uint64_t hit = __ballot(sc.incl > g);
+    const int first = hit ? __builtin_ctzll(hit) : 0;
+    l = first;
+    b = g - (__shfl(sc.incl, first) - __shfl(sc.nbk, first));
+  } else {
+    find_block(p, g, l, b);
+  }
+  l = __builtin_amdgcn_readfirstlane(l);
+  b = __builtin_amdgcn_readfirstlane(b);
 }
 
 }  // namespace mlr

@@ -36,6 +36,7 @@
 
 #include "blocks.h"
 #include "common.h"
+#include "dma.h"
 #include "internal.h"
 
 namespace mlr {
@@ -44,7 +45,6 @@ namespace {
 constexpr int kThreadsM = 256;
 constexpr int kWavesM = kThreadsM / kWave;
 constexpr int kPassRows = 64;
-constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: loads 0
 constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 
 #ifndef MLR_MFMA_MIN_COLS
@@ -56,56 +56,10 @@ constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// Buffer resource (raw, 32-bit elements, no stride) as four scalar words, for
-// the inline DMA below.
-__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
-  r.y = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane(int(bytes));
-  r.w = 0x00020000;
-  return r;
-}
-
-// One 16-byte-per-lane buffer load written straight to LDS: lane i's chunk
-// lands at byte lds + 16 i.  Written as inline assembly so that the compiler
-// does not see an LDS store in flight; it would otherwise wait for every
-// outstanding stage before each LDS read.  The waits for these loads are the
-// explicit ones in stage_barrier.  M0 (the LDS base) is saved and restored.
-__device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(r)
-      : "memory");
-}
-
-// Wait until at most VM vector memory operations of this wavefront are
-// outstanding and its LDS operations are done, then meet the workgroup.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier; no release fence is used, since one would also wait for
-// the stages still in flight.
-template <int VM>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt is a 6-bit field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Shrink layout of a pass with MT row tiles and RT rank tiles (16 each).
@@ -418,7 +372,8 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   // units = (block, slice); the split count gives every working workgroup a
   // slot (MLR_MFMA_OCCUPANCY per compute unit), at least MLR_MFMA_MIN_COLS
   // columns each
-  const int total = __builtin_amdgcn_readfirstlane(count_blocks(p));
+  const BlockScan sc = scan_blocks(p);
+  const int total = sc.total;
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
@@ -431,9 +386,7 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   const int n1 = min(p.Ns, n0 + nsz);
   const int g = unit / p.S, s = unit - g * p.S;
   int l, b;
-  find_block(p, g, l, b);
-  l = __builtin_amdgcn_readfirstlane(l);
-  b = __builtin_amdgcn_readfirstlane(b);
+  find_block(p, sc, g, l, b);
   const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
 
@@ -443,7 +396,7 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   c.ar = dma_rsrc(p.a + wsel * p.r * p.K, uint32_t(p.r * p.K * 2));
   c.br = make_rsrc(p.b + wsel * p.Ns * p.r, uint32_t(p.Ns * p.r * 2));
   c.ring = ring;
-  c.ring_lds = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_u8_t*)ring)));
+  c.ring_lds = lds_address(ring);
   c.s_row = s_row;
   c.s_pair = s_pair;
   c.s_wt = s_wt;

@@ -1,0 +1,332 @@
+// Fused shrink + expand for decode-sized blocks as one continuous stream.
+//
+// One 1024-thread workgroup handles one (block, slice, column split) and up
+// to four rows at a time.  Its whole weight traffic -- the A matrix (r x K),
+// then the split's B columns (cols x r) -- flows through one ring of LDS
+// slots filled by direct-to-LDS buffer loads, 16 KiB per stage, NS - 1 stages
+// in flight.  The B stages start loading while the last A stages are being
+// multiplied, so the weight stream does not stop between shrink and expand
+// (loading A in register batches and then B leaves HBM idle between the two
+// bursts).  The arithmetic is on v_mfma_f32_16x16x32_bf16: with one MFMA per
+// wavefront and stage the vector ALUs stay out of the way of the stream (the
+// same loop with v_dot2 products was bound by their issue).
+//
+//   before the ring  X rows (rows x K) and the Y values of the split
+//                    (rows x cols) are loaded into LDS the same way.
+//   A stage          K range [t KT, (t+1) KT) of all r rows: 16 (rank tile,
+//                    k-step) products, one per wavefront, V^T[16 ranks x 16
+//                    rows] += A[16 x 32] X^T[32 x 16] (rows >= 4 are zero).
+//   after A          the k-step partials of each rank tile are added through
+//                    LDS and v is rounded to bf16 into LDS; never to memory.
+//   B stage          NCS consecutive columns of B: D^T[16 cols x 16 rows] =
+//                    B[16 x 32 ranks] V^T, so a lane ends with four
+//                    consecutive columns of one row, which it scales by the
+//                    routed weight, adds to the Y values held in LDS and
+//                    rounds to bf16 there.
+//   epilogue         the Y rows of the split go back to memory in 16-byte
+//                    pieces.
+// Staged rows keep their 16-byte chunks XOR-permuted by the row (A) or
+// column (B) index so the 16 rows of an MFMA operand read spread over the
+// LDS banks.
+//
+// The prhub summary of vLLM PR #42290 (implementation steps) describes the
+// one-shot kernel this follows: x loaded once, multiplied by lora_a, the
+// rank-sized result kept on chip and multiplied by lora_b, written over or
+// added onto the output.
+#include <algorithm>
+
+#include "blocks.h"
+#include "common.h"
+#include "dma.h"
+#include "internal.h"
+
+namespace mlr {
+namespace {
+
+constexpr int kST = 1024;                   // threads
+constexpr int kRows = 4;                    // X rows per pass
+constexpr int kStage = 16384;               // bytes per ring stage
+constexpr int kStageChunks = kStage / 16;   // 1024
+constexpr int kIPS = kStageChunks / kST;    // DMA instructions per thread and stage
+static_assert(kIPS == 1, "a stage is one 16-byte chunk per thread");
+constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
+constexpr int kMaxCols = 2048;              // output columns per workgroup
+constexpr int kYBytes = kRows * kMaxCols * 2;
+constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
+
+#ifndef MLR_STREAM_SLOTS
+#define MLR_STREAM_SLOTS 4
+#endif
+constexpr int kSlots = MLR_STREAM_SLOTS;
+static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
+
+#ifndef MLR_STREAM_MIN_COLS
+#define MLR_STREAM_MIN_COLS 256
+#endif
+
+// Wait for the ring stage whose loads were followed by `later` stages.
+template <int L>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (L < 0) {
+    stage_barrier<0>();
+  } else {
+    if (later == L) stage_barrier<L * kIPS>();
+    else wait_stage<L - 1>(later);
+  }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Stage geometry for rank R (16..128).
+template <int R>
+struct Geo {
+  static constexpr int KT = kStage / 2 / R;     // K per A stage
+  static constexpr int CPRK = KT / 8;           // chunks per A row in a stage (>= 8)
+  static constexpr int RT = R / 16;             // rank tiles
+  static constexpr int KSA = KT / 32 / 1;       // k-steps per A stage
+  static constexpr int NCS = kStage / 2 / R;    // columns per B stage
+  static constexpr int CPR = R / 8;             // chunks per B column
+  static constexpr int SW = CPR < 8 ? CPR : 8;  // B chunk permutation width
+  static constexpr int CT = NCS / 16;           // column tiles per B stage
+  static constexpr int KS = (R + 31) / 32;      // expand k-steps (ranks padded to 32)
+  static_assert(RT * KSA == kST / kWave, "one (rank tile, k-step) per wavefront");
+  static_assert(CPRK >= 8, "A chunk permutation needs 8 chunks per row");
+};
+
+// Loads of ring stage t (A stages first, then B stages) into slot `lds`.
+template <int R>
+__device__ __forceinline__ void issue_stage(const FusedParams& p, i32x4_t ar, i32x4_t br, int t,
+                                            int nA, int ncols, uint32_t lds) {
+  using G = Geo<R>;
+  const int q = threadIdx.x;  // one 16-byte chunk per thread and stage
+  const uint32_t dst = lds + wave_id() * kWave * 16;
+  if (t < nA) {
+    const int j = q / G::CPRK, cs = q % G::CPRK;
+    const int kk = t * G::KT + 8 * (cs ^ (j & 7));
+    dma16(ar, dst, kk < p.K ? uint32_t(j * p.K + kk) * 2u : kOob);
+  } else {
+    const int col = q / G::CPR, js = q % G::CPR;
+    const int n = (t - nA) * G::NCS + col;
+    const int jc = js ^ (col & (G::SW - 1));
+    dma16(br, dst, n < ncols ? uint32_t(n * R + 8 * jc) * 2u : kOob);
+  }
+}
+
+template <int R>
+__global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
+  using G = Geo<R>;
+  constexpr int VP = 32 * G::KS + 8;  // bf16 pitch of the v rows
+  __shared__ __align__(16) uint8_t ring[kSlots * kStage];
+  __shared__ __align__(16) uint8_t xs[kXBytes];
+  __shared__ __align__(16) uint8_t ys[kYBytes];
+  __shared__ __align__(16) uint16_t s_vb[kRows * VP];
+  __shared__ int s_pair[kRows];
+  __shared__ int s_row[kRows];
+  __shared__ float s_w[kRows];
+  static_assert(kST * 4 * 4 <= kXBytes, "k-step partials reuse the X buffer");
+
+  // units = (block, slice); split count: a compute unit per working
+  // workgroup, at least MLR_STREAM_MIN_COLS and at most kMaxCols columns each
+  const BlockScan sc = scan_blocks(p);
+  const int total = sc.total;
+  const int units = total * p.S;
+  const int per_xcd = (units + kXcds - 1) / kXcds;
+  const int need = (p.Ns + kMaxCols - 1) / kMaxCols;
+  const int max_split = max(need, p.Ns / MLR_STREAM_MIN_COLS);
+  const int n_split = min(max_split, max(need, p.xcd_cus / max(per_xcd, 1)));
+  int unit, split;
+  if (!map_unit_xcd(blockIdx.x, units, n_split, unit, split)) return;
+  const int nsz = ((p.Ns + n_split - 1) / n_split + 7) / 8 * 8;
+  const int n0 = split * nsz;
+  if (n0 >= p.Ns) return;
+  const int n1 = min(p.Ns, n0 + nsz);
+  const int ncols = n1 - n0;
+  const int g = unit / p.S, s = unit - g * p.S;
+  int l, b;
+  find_block(p, sc, g, l, b);
+  // the first pass's pair ids are loaded before the expert id is waited for
+  const int32_t* srow = p.sorted + l * p.cap + b * p.B;
+  const int id0 = (threadIdx.x < kRows && int(threadIdx.x) < p.B) ? srow[threadIdx.x] : p.numel;
+  const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
+  const i32x4_t ar = dma_rsrc(p.a + wsel * R * p.K, uint32_t(R * p.K * 2));
+  const i32x4_t br = dma_rsrc(p.b + wsel * p.Ns * R + int64_t(n0) * R, uint32_t(ncols * R * 2));
+  const int64_t x_rows = p.x_per_pair ? int64_t(p.numel) : int64_t(p.numel / p.topk);
+  const i32x4_t xr = dma_rsrc(p.x, uint32_t(x_rows * p.K * 2));
+  const int64_t col0 = int64_t(s) * p.Ns + n0;
+  const i32x4_t yr = dma_rsrc(p.y + col0, uint32_t((int64_t(p.numel) * p.N - col0) * 2));
+  const uint32_t ring_lds = lds_address(ring);
+  const uint32_t xs_lds = lds_address(xs);
+  const uint32_t ys_lds = lds_address(ys);
+
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int lr = lane & 15, lq = lane >> 4;
+  const int K8 = p.K / 8, c8 = ncols / 8;
+  const int nA = (p.K + G::KT - 1) / G::KT, nB = (ncols + G::NCS - 1) / G::NCS, T = nA + nB;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  for (int g0 = 0; g0 < p.B; g0 += kRows) {
+    if (tid < kRows) {
+      int pid = p.numel, xrow = -1;
+      float wv = 1.f;
+      if (g0 + tid < p.B) {
+        const int id = g0 == 0 ? id0 : srow[g0 + tid];
+        if (id < p.numel) {
+          pid = id;
+          xrow = p.x_per_pair ? id : id / p.topk;
+          if (p.mul) wv = p.w[id];
+        }
+      }
+      s_pair[tid] = pid;
+      s_row[tid] = xrow;
+      s_w[tid] = wv;
+    }
+    for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = 0;
+    // valid rows are a prefix of the block (sentinels only pad a group's end)
+    const int nr = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kRows && s_row[tid] >= 0));
+    if (nr == 0) break;
+
+    // X rows (row stride K / 8 chunks) and the split's Y values (row stride
+    // ncols / 8 chunks) into LDS: 64 chunks per instruction, only
+    // instructions that start inside the data (both buffers are multiples
+    // of 64 chunks, so a last partial instruction still fits)
+    for (int q0 = w * kWave; q0 < kRows * K8; q0 += kST) {
+      const int q = q0 + lane, i = q / K8, c = q % K8;
+      const int xrow = i < kRows ? s_row[i] : -1;
+      const uint32_t off = (q < kRows * K8 && xrow >= 0) ? uint32_t(xrow * p.K + 8 * c) * 2u : kOob;
+      dma16(xr, xs_lds + q0 * 16, off);
+    }
+    for (int q0 = w * kWave; q0 < kRows * c8; q0 += kST) {
+      const int q = q0 + lane, i = q / c8, c = q % c8;
+      const int pid = i < kRows ? s_pair[i] : p.numel;
+      const uint32_t off = (q < kRows * c8 && p.add && pid < p.numel)
+                               ? uint32_t(int64_t(pid) * p.N + 8 * c) * 2u : kOob;
+      dma16(yr, ys_lds + q0 * 16, off);
+    }
+    for (int t = 0; t < kSlots - 1 && t < T; ++t)
+      issue_stage<R>(p, ar, br, t, nA, ncols, ring_lds + t * kStage);
+
+    // wavefront w: A rank tile rt and k-step ka of every A stage
+    const int rt = w % G::RT, ka = w / G::RT;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 vop[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
+    const float wrow = lr < kRows ? s_w[lr] : 0.f;
+
+    for (int t = 0; t < T; ++t) {
+      if (t == 0) stage_barrier<0>();  // X, Y and the first stages
+      else wait_stage<kSlots - 2>(min(kSlots - 2, T - 1 - t));
+      if (t + kSlots - 1 < T)
+        issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ncols,
+                       ring_lds + ((t + kSlots - 1) % kSlots) * kStage);
+      const uint4* st = reinterpret_cast<const uint4*>(ring + (t % kSlots) * kStage);
+      if (t < nA) {
+        // ---- shrink: V^T[rank tile rt] += A[16 ranks x 32 k] . X^T
+        const int j = 16 * rt + lr, c = 4 * ka + lq;
+        const uint4 a = st[j * G::CPRK + (c ^ (j & 7))];
+        const int xc = t * (G::KT / 8) + c;
+        const uint4 x = (lr < kRows && xc < K8)
+                            ? reinterpret_cast<const uint4*>(xs)[lr * K8 + xc] : zero4;
+        acc = mfma16(a, x, acc);
+        if (t == nA - 1) {
+          // k-step partials through the X buffer (X is no longer needed)
+          float* part = reinterpret_cast<float*>(xs);
+          stage_barrier<63>();
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part[(w * 4 + i) * kWave + lane] = acc[i];
+          stage_barrier<63>();
+          if (w < G::RT) {
+#pragma unroll
+            for (int k = 1; k < G::KSA; ++k)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i] += part[((w + k * G::RT) * 4 + i) * kWave + lane];
+            // lane (lr, lq) holds v[row lr][16 w + 4 lq + i]
+            if (lr < kRows) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) s_vb[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i]);
+            }
+          }
+        }
+      } else {
+        // ---- expand: D^T[16 cols x 16 rows] = B[16 cols x 32 ranks] . V^T
+        const int u = t - nA;
+        if (u == 0) {
+#pragma unroll
+          for (int ks = 0; ks < G::KS; ++ks)
+            vop[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vb + lr * VP + 32 * ks + 8 * lq)
+                                 : zero4;
+        }
+        for (int ct = w; ct < G::CT; ct += kST / kWave) {
+          const int col = 16 * ct + lr;
+          f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < G::KS; ++ks) {
+            const int jc = 4 * ks + lq;
+            const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
+            dt = mfma16(bb, vop[ks], dt);
+          }
+          // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage
+          const int n = u * G::NCS + 16 * ct + 4 * lq;
+          if (lr < nr && n < ncols) {
+            uint2* yp = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(ys) + lr * ncols + n);
+            const uint2 yv = *yp;
+            float o[4] = {dt[0] * wrow, dt[1] * wrow, dt[2] * wrow, dt[3] * wrow};
+            if (p.add) {
+              o[0] += bf16_lo(yv.x);
+              o[1] += bf16_hi(yv.x);
+              o[2] += bf16_lo(yv.y);
+              o[3] += bf16_hi(yv.y);
+            }
+            *yp = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
+                             uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- epilogue: Y rows of the split, 16 bytes per thread and step
+    for (int q = tid; q < nr * c8; q += kST) {
+      const int i = q / c8, c = q % c8;
+      const uint4 v = reinterpret_cast<const uint4*>(ys)[i * c8 + c];
+      *reinterpret_cast<uint4*>(p.y + int64_t(s_pair[i]) * p.N + col0 + 8 * c) = v;
+    }
+    __syncthreads();  // s_* tables, xs, ys and the ring are reused by the next pass
+  }
+}
+
+}  // namespace
+
+// The stream kernel takes r in {16, 32, 64, 128}, X rows of a pass that fit
+// kXBytes, and buffers below 2 GiB (kOob must lie past each of them).
+bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair) {
+  if (r != 16 && r != 32 && r != 64 && r != 128) return false;
+  if (int64_t(kRows) * K * 2 > kXBytes) return false;
+  const int64_t x_bytes = (x_per_pair ? numel : M) * K * 2;
+  return x_bytes <= kMaxBufBytes && numel * N * 2 <= kMaxBufBytes && r * K * 2 <= kMaxBufBytes;
+}
+
+hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
+  // grid: 8 XCD ranges of ceil(units / 8) units times the split count, which
+  // the kernel keeps within xcd_cus per XCD unless the column limit needs more
+  const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
+  const int64_t need = (p.Ns + kMaxCols - 1) / kMaxCols;
+  const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
+  const dim3 grid(unsigned(kXcds * slots));
+  switch (p.r) {
+    case 16: hipLaunchKernelGGL(fused_stream_kernel<16>, grid, dim3(kST), 0, st, p); break;
+    case 32: hipLaunchKernelGGL(fused_stream_kernel<32>, grid, dim3(kST), 0, st, p); break;
+    case 64: hipLaunchKernelGGL(fused_stream_kernel<64>, grid, dim3(kST), 0, st, p); break;
+    case 128: hipLaunchKernelGGL(fused_stream_kernel<128>, grid, dim3(kST), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlr

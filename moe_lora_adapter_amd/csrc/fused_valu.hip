@@ -45,6 +45,9 @@ namespace mlr {
 #ifndef MLR_VALU_MIN_COLS    // fewest output columns per split
 #define MLR_VALU_MIN_COLS 256
 #endif
+#ifndef MLR_VALU_OCC         // workgroups per compute unit the split count plans for
+#define MLR_VALU_OCC 1
+#endif
 constexpr int kThreads = MLR_VALU_THREADS;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxB = 128;
@@ -194,7 +197,9 @@ __device__ __forceinline__ void load_y(const FusedParams& p, const int* s_pair, 
 // always sees the same eight ranks.  The row sums land in LDS (s_d), and the
 // epilogue then reads Y and writes it back in 16-byte pieces (8 columns per
 // thread), the Y reads issued before the B chunks are consumed.
-constexpr int kRowsPerBatch = 2048;
+constexpr int kRowsPerBatch = 2 * kThreads;
+// one epilogue task (one row, 8 columns) per thread covers a batch
+static_assert(kMaxRG * kRowsPerBatch / 8 <= kThreads, "epilogue tasks exceed the threads");
 
 template <int RG, int CPR>
 __device__ __forceinline__ void expand_stream(const FusedParams& p, const uint16_t* __restrict__ Bm,
@@ -319,7 +324,7 @@ __device__ __forceinline__ void valu_rows(const FusedParams& p, const uint16_t* 
 // Blocks of up to two valid rows take 2-row groups; larger blocks take
 // 4-row groups (one pass over A and B per group).
 template <int JW, int CPR>
-__global__ void __launch_bounds__(kThreads) fused_valu_kernel(FusedParams p, ShrinkShape sh) {
+__global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused_valu_kernel(FusedParams p, ShrinkShape sh) {
   constexpr int RG = 4;  // LDS sized for the larger group
   __shared__ int s_pair[kMaxB];
   __shared__ int s_row[kMaxB];
@@ -332,12 +337,13 @@ __global__ void __launch_bounds__(kThreads) fused_valu_kernel(FusedParams p, Shr
   // unit of its own.  Unit u goes to XCD u % 8, so an XCD holds
   // ceil(units / 8) * n_split of them; a second workgroup on a compute unit
   // was measured to cost far more than a split saves.
-  const int total = __builtin_amdgcn_readfirstlane(count_blocks(p));
+  const BlockScan sc = scan_blocks(p);
+  const int total = sc.total;
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int u8 = per_xcd * kXcds;
   const int max_split = max(1, p.Ns / MLR_VALU_MIN_COLS);
-  const int n_split = min(max_split, max(1, p.xcd_cus / max(per_xcd, 1)));
+  const int n_split = min(max_split, max(1, p.xcd_cus * MLR_VALU_OCC / max(per_xcd, 1)));
   // workgroup -> (split, unit), split-major; equal unit residue mod 8 = same XCD
   const int id = blockIdx.x;
   const int split = id / max(u8, 1), unit = id - split * u8;
@@ -348,9 +354,7 @@ __global__ void __launch_bounds__(kThreads) fused_valu_kernel(FusedParams p, Shr
   const int n1 = min(p.Ns, n0 + nsz);
   const int g = unit / p.S, s = unit - g * p.S;
   int l, b;
-  find_block(p, g, l, b);
-  l = __builtin_amdgcn_readfirstlane(l);
-  b = __builtin_amdgcn_readfirstlane(b);
+  find_block(p, sc, g, l, b);
   const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
   const uint16_t* A = p.a + wsel * p.r * p.K;
@@ -378,7 +382,14 @@ static void launch(const FusedParams& p, ShrinkShape sh, dim3 grid, hipStream_t 
   hipLaunchKernelGGL((fused_valu_kernel<JW, CPR>), grid, dim3(kThreads), 0, st, p, sh);
 }
 
+#ifndef MLR_VALU_STREAM  // decode shapes the stream kernel supports go there
+#define MLR_VALU_STREAM 1
+#endif
+
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
+  if (MLR_VALU_STREAM &&
+      stream_supported(p.numel / p.topk, p.numel, p.K, p.N, p.r, p.x_per_pair))
+    return launch_fused_stream(p, st);
   // rows of A per wavefront and the wave arrangement
   int jw = 1;
   while (jw < p.r && jw < 16) jw <<= 1;
@@ -386,9 +397,9 @@ hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
   sh.rgw = std::min(kWaves, (p.r + jw - 1) / jw);
   sh.kp = std::max(1, kWaves / sh.rgw);
   // grid: covers split * u8 + unit for every split count the kernel can pick:
-  // u8 <= units_pad with one split, and n_split * u8 <= 8 * xcd_cus with more.
+  // u8 <= units_pad with one split, and n_split * u8 <= 8 * xcd_cus * OCC with more.
   const int64_t units_pad = (int64_t(p.units) + kXcds - 1) / kXcds * kXcds;
-  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus);
+  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus * MLR_VALU_OCC);
   const int cpr = (p.r % 8 == 0 && ((p.r / 8) & (p.r / 8 - 1)) == 0) ? p.r / 8 : 0;
 #define MLR_CASE(JW_, CPR_) \
   if (jw == JW_ && cpr == CPR_) { launch<JW_, CPR_>(p, sh, dim3(unsigned(grid)), st); return hipGetLastError(); }
