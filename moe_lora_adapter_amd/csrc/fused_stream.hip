@@ -83,7 +83,7 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Stage geometry for rank R (16..128).
+// Stage geometry for rank R (32, 64 or 128).
 template <int R>
 struct Geo {
   static constexpr int KT = kStage / 2 / R;     // K per A stage
@@ -303,10 +303,10 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
 
 }  // namespace
 
-// The stream kernel takes r in {16, 32, 64, 128}, X rows of a pass that fit
+// The stream kernel takes r in {32, 64, 128}, X rows of a pass that fit
 // kXBytes, and buffers below 2 GiB (kOob must lie past each of them).
 bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair) {
-  if (r != 16 && r != 32 && r != 64 && r != 128) return false;
+  if (r != 32 && r != 64 && r != 128) return false;
   if (int64_t(kRows) * K * 2 > kXBytes) return false;
   const int64_t x_bytes = (x_per_pair ? numel : M) * K * 2;
   return x_bytes <= kMaxBufBytes && numel * N * 2 <= kMaxBufBytes && r * K * 2 <= kMaxBufBytes;
@@ -320,7 +320,6 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
   const dim3 grid(unsigned(kXcds * slots));
   switch (p.r) {
-    case 16: hipLaunchKernelGGL(fused_stream_kernel<16>, grid, dim3(kST), 0, st, p); break;
     case 32: hipLaunchKernelGGL(fused_stream_kernel<32>, grid, dim3(kST), 0, st, p); break;
     case 64: hipLaunchKernelGGL(fused_stream_kernel<64>, grid, dim3(kST), 0, st, p); break;
     case 128: hipLaunchKernelGGL(fused_stream_kernel<128>, grid, dim3(kST), 0, st, p); break;

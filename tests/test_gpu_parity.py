@@ -241,6 +241,9 @@ EDGE = [
     dict(K=320, Ns=96, r=96, block_m=32, M=64, E=2, topk=2, L=1, active=1, p_neg=0.0),
     dict(K=128, Ns=48, r=120, block_m=64, M=100, E=2, topk=1, L=1, active=1, mul=True),
     dict(K=136, Ns=64, r=56, block_m=16, M=50, E=3, topk=2, L=2, active=2, x_per_pair=True),
+    # K beyond what the decode stream kernel stages in LDS (4 rows x K):
+    # the register-batch vector kernel takes it
+    dict(K=4104, Ns=136, r=64, block_m=16, M=24, E=2, topk=2, L=2, active=2),
 ]
 
 
