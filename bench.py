@@ -327,7 +327,7 @@ def main(argv=None):
 
 def _uses_mfma(s, variant):
     import moe_lora_adapter_amd as mla
-    return mla.fused_variant(s.M, s.topk, s.K, s.Ns, s.E, s.L, s.r, s.block_m, s.x_per_pair,
+    return mla.fused_variant(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r, s.block_m, s.x_per_pair,
                              variant) == "mfma"
 
 

@@ -165,11 +165,11 @@ MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
  * or MOE_LORA_VARIANT_MFMA, AUTO resolved the way fused_moe_lora resolves
  * it.  Returns a negative status when fused_moe_lora would reject the sizes,
  * x_per_pair or the variant (MOE_LORA_ERR_UNSUPPORTED for MFMA when r is not
- * a multiple of 8 in [8, 128], block_m > 128, or x, an A matrix or a B matrix
- * exceeds 2 GiB).
+ * a multiple of 8 in [8, 128], block_m > 128, or x, y, an A matrix or a B
+ * matrix exceeds 2 GiB).
  */
 MOE_LORA_API int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns,
-                   int32_t E, int32_t L, int32_t r, int32_t block_m,
+                   int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
                    int32_t x_per_pair, int32_t variant);
 
 #ifdef __cplusplus

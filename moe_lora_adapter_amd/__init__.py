@@ -36,7 +36,7 @@ SIGNATURES = {
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
     "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
-                                              _I32, _I32]),
+                                              _I32, _I32, _I32]),
 }
 
 
@@ -84,11 +84,12 @@ def align_workspace_bytes(M: int, topk: int, E: int, L: int, block_m: int) -> in
     return int(v)
 
 
-def fused_variant(M: int, topk: int, K: int, Ns: int, E: int, L: int, r: int, block_m: int,
-                  x_per_pair: bool = False, variant: str | int = "auto") -> str:
+def fused_variant(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int, r: int,
+                  block_m: int, x_per_pair: bool = False, variant: str | int = "auto") -> str:
     """Name of the kernel ("valu" or "mfma") fused_moe_lora runs for these sizes."""
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    rc = lib().fused_moe_lora_variant(M, topk, K, Ns, E, L, r, block_m, int(bool(x_per_pair)), v)
+    rc = lib().fused_moe_lora_variant(M, topk, K, Ns, S, E, L, r, block_m, int(bool(x_per_pair)),
+                                      v)
     if rc < 0:
         raise MoeLoraError(rc, "fused_moe_lora_variant")
     return {VARIANT_VALU: "valu", VARIANT_MFMA: "mfma"}[rc]

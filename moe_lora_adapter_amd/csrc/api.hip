@@ -42,21 +42,22 @@ int check_sizes(int64_t M, int64_t topk, int64_t E, int64_t L, int64_t block_m,
 
 // Whether the MFMA kernel can take these sizes (rank, block size and the
 // byte ranges its buffer resources address).
-bool mfma_ok(int64_t M, int64_t numel, int64_t K, int64_t Ns, int r, int block_m, int x_per_pair) {
+bool mfma_ok(int64_t M, int64_t numel, int64_t K, int64_t Ns, int64_t N, int r, int block_m,
+             int x_per_pair) {
   const int64_t x_bytes = (x_per_pair ? numel : M) * K * 2;
-  return mfma_supported(r, block_m) && mfma_fits(x_bytes, r, K, Ns);
+  return mfma_supported(r, block_m) && mfma_fits(x_bytes, numel * N * 2, r, K, Ns);
 }
 
 // The kernel that runs; the sizes have been checked.
-int pick_variant(int64_t M, int64_t numel, int64_t K, int64_t Ns, int64_t E, int64_t L, int r,
-                 int block_m, int x_per_pair, int variant) {
+int pick_variant(int64_t M, int64_t numel, int64_t K, int64_t Ns, int64_t N, int64_t E, int64_t L,
+                 int r, int block_m, int x_per_pair, int variant) {
   if (variant != MOE_LORA_VARIANT_AUTO) return variant;
   // Expected valid rows per (slot, expert) group: below one half, most
   // blocks hold one or two rows and the vector kernel, which streams A and B
   // with no padded rows, is faster; from there on the MFMA kernel is
   // (measured on MI355X: gpt-oss-20b-like w13 at 0.33 rows per group 28 vs
   // 33 us, at 1.3 rows per group 82 vs 60 us).
-  const bool mfma = mfma_ok(M, numel, K, Ns, r, block_m, x_per_pair) && 2 * numel >= L * E;
+  const bool mfma = mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair) && 2 * numel >= L * E;
   return mfma ? MOE_LORA_VARIANT_MFMA : MOE_LORA_VARIANT_VALU;
 }
 
@@ -178,7 +179,7 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
   if (r > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
   const int64_t N = int64_t(S) * Ns;
   if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
-  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, r, block_m, x_per_pair))
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair))
     return MOE_LORA_ERR_UNSUPPORTED;
   if (numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
   if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
@@ -218,23 +219,26 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
   p.xcd_cus = xcd_compute_units();
 
   const bool use_mfma =
-      pick_variant(M, numel, K, Ns, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
+      pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 
-int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t E, int32_t L,
-                           int32_t r, int32_t block_m, int32_t x_per_pair, int32_t variant) {
+int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                           int32_t L, int32_t r, int32_t block_m, int32_t x_per_pair,
+                           int32_t variant) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
   if (rc != MOE_LORA_OK) return rc;
-  if (K < 8 || Ns < 8 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
+  if (K < 8 || Ns < 8 || S < 1 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
+  const int64_t N = int64_t(S) * Ns;
+  if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
   if ((x_per_pair != 0 && x_per_pair != 1) || variant < 0 || variant > 2) return MOE_LORA_ERR_INVALID;
   if (r > kMaxRank) return MOE_LORA_ERR_UNSUPPORTED;
-  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, r, block_m, x_per_pair))
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair))
     return MOE_LORA_ERR_UNSUPPORTED;
-  return pick_variant(M, numel, K, Ns, E, L, r, block_m, x_per_pair, variant);
+  return pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant);
 }
 
 }  // extern "C"

@@ -50,6 +50,9 @@ constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 #ifndef MLR_MFMA_MIN_COLS
 #define MLR_MFMA_MIN_COLS 256
 #endif
+#ifndef MLR_MFMA_STAGE_BYTES  // most bytes of X and A rows per ring stage
+#define MLR_MFMA_STAGE_BYTES 24576
+#endif
 #ifndef MLR_MFMA_OCCUPANCY  // workgroups per compute unit the split count assumes
 #define MLR_MFMA_OCCUPANCY 2
 #endif
@@ -72,7 +75,13 @@ struct Shrink {
   static constexpr int WR = RT < kWavesM / MT ? RT : kWavesM / MT;  // rank groups
   static constexpr int WK = kWavesM / (MT * WR);                    // K parts
   static constexpr int TR = (RT + WR - 1) / WR;                     // rank tiles per wave
-  static constexpr int KT = WK == 4 ? 128 : 64;                     // K per stage
+  // K per stage: the largest power of two (at least 32 per K part) whose
+  // stage of X and A rows stays within MLR_MFMA_STAGE_BYTES; small stages
+  // leave a pass bound by the fixed cost of each ring step
+  static constexpr int kt(int k) {
+    return (k < 512 && (RB + RP) * 2 * k * 2 <= MLR_MFMA_STAGE_BYTES) ? kt(2 * k) : k;
+  }
+  static constexpr int KT = kt(WK == 4 ? 128 : 64);
   static constexpr int CPR = KT / 8;                                // chunks per staged row
   static constexpr int KSW = KT / WK / 32;                          // k-steps per wave, stage
   static constexpr int XI = RB * CPR / kWave;                       // DMA instrs for X
@@ -439,9 +448,11 @@ bool mfma_supported(int r, int B) {
 }
 
 // Every buffer the kernel reads through a buffer resource stays below 2 GiB,
-// so that one offset past the end (kOob) is out of range for all of them.
-bool mfma_fits(int64_t x_bytes, int64_t r, int64_t K, int64_t Ns) {
-  return x_bytes <= kMaxXBytes && r * K * 2 <= kMaxXBytes && r * Ns * 2 <= kMaxXBytes;
+// so that one offset past the end (kOob) is out of range for all of them (y
+// is held to the same limit).
+bool mfma_fits(int64_t x_bytes, int64_t y_bytes, int64_t r, int64_t K, int64_t Ns) {
+  return x_bytes <= kMaxXBytes && y_bytes <= kMaxXBytes && r * K * 2 <= kMaxXBytes &&
+         r * Ns * 2 <= kMaxXBytes;
 }
 
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st) {

@@ -135,32 +135,36 @@ def test_fused_rejects(kw, status):
     (dict(variant=mla.VARIANT_MFMA, r=12), mla.ERR_UNSUPPORTED),
     # x above 2 GiB: M * K * 2 = 2^31 + 2^14 bytes
     (dict(variant=mla.VARIANT_MFMA, M=262145, K=4096), mla.ERR_UNSUPPORTED),
+    (dict(S=0), mla.ERR_INVALID),
 ])
 def test_variant_query_rejects_like_fused(kw, status):
-    a = dict(M=16, topk=4, K=2880, Ns=2880, E=32, L=6, r=64, B=16, xpp=0, variant=0)
+    a = dict(M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, xpp=0, variant=0)
     a.update(kw)
     assert status != mla.OK  # fused_call below must not reach a launch
-    assert mla.lib().fused_moe_lora_variant(a["M"], a["topk"], a["K"], a["Ns"], a["E"], a["L"],
-                                            a["r"], a["B"], a["xpp"], a["variant"]) == status
+    assert mla.lib().fused_moe_lora_variant(a["M"], a["topk"], a["K"], a["Ns"], a["S"], a["E"],
+                                            a["L"], a["r"], a["B"], a["xpp"],
+                                            a["variant"]) == status
     assert fused_call(**a) == status
 
 
 def test_variant_query_resolves_auto():
     fv = mla.fused_variant
     # decode: about two rows per (slot, expert) group -> vector kernel
-    assert fv(16, 4, 2880, 2880, 32, 6, 64, 16) == "valu"
+    assert fv(16, 4, 2880, 2880, 2, 32, 6, 64, 16) == "valu"
     # dense prefill blocks with a large rank -> MFMA kernel
-    assert fv(8192, 8, 2048, 768, 128, 8, 128, 64) == "mfma"
+    assert fv(8192, 8, 2048, 768, 2, 128, 8, 128, 64) == "mfma"
     # MFMA needs r % 8 == 0, so AUTO never picks it otherwise
-    assert fv(8192, 8, 2048, 768, 128, 8, 100, 64) == "valu"
+    assert fv(8192, 8, 2048, 768, 2, 128, 8, 100, 64) == "valu"
     # from half a row per (slot, expert) group on, small ranks take MFMA too
-    assert fv(2048, 4, 2880, 2880, 128, 4, 16, 64) == "mfma"
-    assert fv(64, 4, 2880, 2880, 128, 4, 16, 64) == "mfma"
-    assert fv(63, 4, 2880, 2880, 128, 4, 16, 64) == "valu"
+    assert fv(2048, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
+    assert fv(64, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
+    assert fv(63, 4, 2880, 2880, 2, 128, 4, 16, 64) == "valu"
     # an x above 2 GiB keeps AUTO on the vector kernel
-    assert fv(262145, 8, 4096, 768, 128, 8, 128, 64) == "valu"
-    assert fv(16, 4, 2880, 2880, 32, 6, 64, 16, variant="mfma") == "mfma"
-    assert fv(8192, 8, 2048, 768, 128, 8, 128, 64, variant="valu") == "valu"
+    assert fv(262145, 8, 4096, 768, 2, 128, 8, 128, 64) == "valu"
+    # so does a y above 2 GiB (M * topk * S * Ns * 2 = 2^31 + 2^16 bytes)
+    assert fv(65537, 8, 256, 1024, 2, 128, 8, 128, 64) == "valu"
+    assert fv(16, 4, 2880, 2880, 2, 32, 6, 64, 16, variant="mfma") == "mfma"
+    assert fv(8192, 8, 2048, 768, 2, 128, 8, 128, 64, variant="valu") == "valu"
 
 
 def test_binding_checks_dtypes_before_calling():
