@@ -285,7 +285,7 @@ def main(argv=None):
 
     gbps = work["fused_bytes"] / (fused_avg * 1e-6) / 1e9
     tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
-    kname = "fused_mfma_kernel" if _uses_mfma(s, variant) else "fused_valu_kernel"
+    kname = _kernel_name(s, variant)
     traffic, _rec = load_traffic(kname, s.name)
     out = {
         "metric": METRIC,
@@ -325,10 +325,10 @@ def main(argv=None):
     return 0
 
 
-def _uses_mfma(s, variant):
+def _kernel_name(s, variant):
     import moe_lora_adapter_amd as mla
-    return mla.fused_variant(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r, s.block_m, s.x_per_pair,
-                             variant) == "mfma"
+    return mla.fused_kernel_name(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r, s.block_m,
+                                 s.x_per_pair, variant)
 
 
 if __name__ == "__main__":

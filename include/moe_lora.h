@@ -172,6 +172,19 @@ MOE_LORA_API int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int3
                    int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
                    int32_t x_per_pair, int32_t variant);
 
+/*
+ * fused_moe_lora_kernel_name -- [host, no HIP call] name of the GPU kernel
+ * that fused_moe_lora launches for these sizes and `variant` (as profilers
+ * print it, without template arguments): "fused_stream_kernel" (decode
+ * blocks: A and B streamed through one LDS ring), "fused_valu_kernel"
+ * (decode blocks, other ranks or K) or "fused_mfma_kernel" (prefill
+ * blocks).  A static string; NULL when fused_moe_lora_variant would return a
+ * negative status.
+ */
+MOE_LORA_API const char *fused_moe_lora_kernel_name(int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
+                   int32_t x_per_pair, int32_t variant);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,8 @@ SIGNATURES = {
                                       _I32, _P]),
     "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _I32]),
+    "fused_moe_lora_kernel_name": (ctypes.c_char_p, [_I64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                     _I32, _I32, _I32, _I32]),
 }
 
 
@@ -93,6 +95,17 @@ def fused_variant(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int, r:
     if rc < 0:
         raise MoeLoraError(rc, "fused_moe_lora_variant")
     return {VARIANT_VALU: "valu", VARIANT_MFMA: "mfma"}[rc]
+
+
+def fused_kernel_name(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int, r: int,
+                      block_m: int, x_per_pair: bool = False, variant: str | int = "auto") -> str:
+    """Name of the GPU kernel fused_moe_lora launches for these sizes."""
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    args = (M, topk, K, Ns, S, E, L, r, block_m, int(bool(x_per_pair)), v)
+    name = lib().fused_moe_lora_kernel_name(*args)
+    if name is None:
+        raise MoeLoraError(lib().fused_moe_lora_variant(*args), "fused_moe_lora_kernel_name")
+    return name.decode()
 
 
 @dataclass

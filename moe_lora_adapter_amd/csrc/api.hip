@@ -241,4 +241,15 @@ int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32
   return pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant);
 }
 
+const char* fused_moe_lora_kernel_name(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S,
+                                       int32_t E, int32_t L, int32_t r, int32_t block_m,
+                                       int32_t x_per_pair, int32_t variant) {
+  const int v = fused_moe_lora_variant(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
+  if (v < 0) return nullptr;
+  if (v == MOE_LORA_VARIANT_MFMA) return "fused_mfma_kernel";
+  const int64_t numel = M * topk, N = int64_t(S) * Ns;
+  return valu_takes_stream(M, numel, K, N, r, x_per_pair) ? "fused_stream_kernel"
+                                                          : "fused_valu_kernel";
+}
+
 }  // extern "C"

@@ -386,13 +386,16 @@ static void launch(const FusedParams& p, ShrinkShape sh, dim3 grid, hipStream_t 
 #define MLR_VALU_STREAM 1
 #endif
 
+// r = 16 stays here: the stream has few stages per workgroup and the
+// register-batch kernel was measured faster (gpt-oss-120b-like decode w13
+// 12.4 vs 13.4 us); from r = 32 on the stream kernel is (20b-like a2..a4:
+// 27.8 vs 33.8 us).  stream_supported() admits r in {32, 64, 128}.
+bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair) {
+  return MLR_VALU_STREAM && stream_supported(M, numel, K, N, r, x_per_pair);
+}
+
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
-  // r = 16: the stream has few stages per workgroup and the register-batch
-  // kernel below was measured faster (gpt-oss-120b-like decode w13 12.4 vs
-  // 13.4 us); from r = 32 on the stream kernel is (20b-like a2..a4: 27.8 vs
-  // 33.8 us).
-  if (MLR_VALU_STREAM &&
-      stream_supported(p.numel / p.topk, p.numel, p.K, p.N, p.r, p.x_per_pair))
+  if (valu_takes_stream(p.numel / p.topk, p.numel, p.K, p.N, p.r, p.x_per_pair))
     return launch_fused_stream(p, st);
   // rows of A per wavefront and the wave arrangement
   int jw = 1;

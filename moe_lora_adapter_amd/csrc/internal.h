@@ -67,6 +67,8 @@ hipError_t launch_fused_valu(FusedParams p, hipStream_t st);
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st);
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st);
 bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);
+// Whether the vector variant runs the stream kernel for these sizes.
+bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);
 bool mfma_supported(int r, int B);
 bool mfma_fits(int64_t x_bytes, int64_t y_bytes, int64_t r, int64_t K, int64_t Ns);
 

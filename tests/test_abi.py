@@ -167,6 +167,17 @@ def test_variant_query_resolves_auto():
     assert fv(8192, 8, 2048, 768, 2, 128, 8, 128, 64, variant="valu") == "valu"
 
 
+def test_kernel_name_query():
+    kn = mla.fused_kernel_name
+    # 20b-like decode (r = 64, K = 2880): the stream kernel
+    assert kn(16, 4, 2880, 2880, 2, 32, 6, 64, 16) == "fused_stream_kernel"
+    # r = 16 decode and K past the stream kernel's X staging: register batches
+    assert kn(8, 4, 2880, 2880, 2, 128, 4, 16, 16) == "fused_valu_kernel"
+    assert kn(16, 4, 4104, 2880, 2, 32, 6, 64, 16) == "fused_valu_kernel"
+    assert kn(8192, 8, 2048, 768, 2, 128, 8, 128, 64) == "fused_mfma_kernel"
+    assert mla.lib().fused_moe_lora_kernel_name(16, 4, 2880, 2880, 2, 32, 6, 129, 16, 0, 0) is None
+
+
 def test_binding_checks_dtypes_before_calling():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
