@@ -42,7 +42,10 @@
 namespace mlr {
 namespace {
 
-constexpr int kThreadsM = 256;
+#ifndef MLR_MFMA_THREADS
+#define MLR_MFMA_THREADS 256
+#endif
+constexpr int kThreadsM = MLR_MFMA_THREADS;
 constexpr int kWavesM = kThreadsM / kWave;
 constexpr int kPassRows = 64;
 constexpr int64_t kMaxXBytes = int64_t(1) << 31;
@@ -81,7 +84,7 @@ struct Shrink {
   static constexpr int kt(int k) {
     return (k < 512 && (RB + RP) * 2 * k * 2 <= MLR_MFMA_STAGE_BYTES) ? kt(2 * k) : k;
   }
-  static constexpr int KT = kt(WK == 4 ? 128 : 64);
+  static constexpr int KT = kt(32 * WK > 64 ? 32 * WK : 64);
   static constexpr int CPR = KT / 8;                                // chunks per staged row
   static constexpr int KSW = KT / WK / 32;                          // k-steps per wave, stage
   static constexpr int XI = RB * CPR / kWave;                       // DMA instrs for X
@@ -219,7 +222,7 @@ __device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx&
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < CTW; ++i) {
-    const int n = nb + 16 * (w + 4 * i) + lr;
+    const int n = nb + 16 * (w + kWavesM * i) + lr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int j = 32 * ks + 8 * lq;
@@ -230,7 +233,7 @@ __device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx&
   if (p.add) {
 #pragma unroll
     for (int i = 0; i < CTW; ++i) {
-      const int n = nb + 16 * (w + 4 * i) + 4 * lq;
+      const int n = nb + 16 * (w + kWavesM * i) + 4 * lq;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int64_t at = n < c.n1 ? yrow[m] + n : 0;
@@ -250,7 +253,7 @@ __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx
   const int lq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < CTW; ++i) {
-    const int n = nb + 16 * (w + 4 * i) + 4 * lq;
+    const int n = nb + 16 * (w + kWavesM * i) + 4 * lq;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -336,11 +339,11 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   stage_barrier<0>();
 
   // ---------------- expand
-  // wavefront w: all MT row tiles, column tiles w + 4 i (i < CTW) of each
-  // group of 64 * CTW columns
+  // wavefront w: all MT row tiles, column tiles w + kWavesM i (i < CTW) of
+  // each group of 16 kWavesM CTW columns
   constexpr int CTW0 = 8 / (MT * KS);
   constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);
-  constexpr int NCG = 64 * CTW;
+  constexpr int NCG = 16 * kWavesM * CTW;
   ExpandRegs<MT, KS, CTW> cur, nxt;
   uint4 va[MT][KS];
 #pragma unroll
