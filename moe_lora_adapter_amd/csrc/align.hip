@@ -65,13 +65,28 @@ __device__ void scatter_segment(const AlignParams& a, int s0, int s1, int* row, 
   }
 }
 
+// Expert ids and padding sentinels of group `key`, which starts at o within
+// its slot and holds c pairs.  Both runs are consecutive, so lpk lanes share
+// a group (block_m / 4 of them: at most three stores each) and a store
+// instruction touches a few cache lines instead of one per lane.
+__device__ __forceinline__ void fill_group(const AlignParams& a, int key, int o, int c, int sl,
+                                           int lpk) {
+  const int l = key / a.E, e = key - l * a.E;
+  const int P = (c + a.B - 1) / a.B * a.B;
+  int32_t* srow = a.sorted + l * a.cap + o;
+  int32_t* erow = a.eids + l * a.nb + o / a.B;
+  for (int blk = sl; blk < P / a.B; blk += lpk) erow[blk] = e;
+  for (int i = c + sl; i < P; i += lpk) srow[i] = a.numel;
+}
+
 // From per-key pair counts: padded group starts (within the slot) in off[],
 // slot starts in sb[0..L], and the outputs num_tokens_post_padded,
-// expert_ids, padding sentinels, lora_ids and num_active.  All threads of the
-// workgroup call it (barriers inside).  tot may live in LDS or in global
-// memory written by this workgroup before the call (the barriers order it).
+// lora_ids, num_active and (with `fill`) expert_ids and padding sentinels.
+// All threads of the workgroup call it (barriers inside).  tot may live in
+// LDS or in global memory written by this workgroup before the call (the
+// barriers order it).
 __device__ void layout_groups(const AlignParams& a, const int* tot, int* off, int* sb,
-                              int* wtot) {
+                              int* wtot, bool fill) {
   const int tid = threadIdx.x;
   for (int key = tid; key < a.LE; key += blockDim.x) {
     const int c = tot[key];
@@ -81,39 +96,14 @@ __device__ void layout_groups(const AlignParams& a, const int* tot, int* off, in
   const int total = block_excl_scan(off, a.LE, wtot);
   for (int l = tid; l <= a.L; l += blockDim.x) sb[l] = l < a.L ? off[l * a.E] : total;
   __syncthreads();
-  // a group's expert ids and padding sentinels are consecutive: block_m / 4
-  // lanes share a group (at most three stores each), so a store instruction
-  // touches a few cache lines instead of one per lane.  The counts of
-  // kFillBatch rounds are loaded before any is used (tot may be global).
-  constexpr int kFillBatch = 8;
-  const int lpk = a.B / 4;
-  const int kpw = kWave / lpk;
-  const int lane = lane_id(), nw = blockDim.x / kWave;
-  const int sub = lane / lpk, sl = lane % lpk;
-  const int stride = nw * kpw;
-  for (int key0 = wave_id() * kpw + sub; key0 < a.LE; key0 += kFillBatch * stride) {
-    int cs[kFillBatch];
-#pragma unroll
-    for (int j = 0; j < kFillBatch; ++j) {
-      const int key = key0 + j * stride;
-      cs[j] = key < a.LE ? tot[key] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kFillBatch; ++j) {
-      const int key = key0 + j * stride;
-      if (key < a.LE) {
-        const int l = key / a.E, e = key - l * a.E;
-        const int o = off[key] - sb[l];
-        const int c = cs[j];
-        const int P = (c + a.B - 1) / a.B * a.B;
-        int32_t* srow = a.sorted + l * a.cap + o;
-        int32_t* erow = a.eids + l * a.nb + o / a.B;
-        for (int blk = sl; blk < P / a.B; blk += lpk) erow[blk] = e;
-        for (int i = c + sl; i < P; i += lpk) srow[i] = a.numel;
-      }
-    }
+  if (fill) {
+    const int lpk = a.B / 4;
+    const int sub = lane_id() / lpk, sl = lane_id() % lpk;
+    const int stride = (blockDim.x / kWave) * (kWave / lpk);
+    for (int key = wave_id() * (kWave / lpk) + sub; key < a.LE; key += stride)
+      fill_group(a, key, off[key] - sb[key / a.E], tot[key], sl, lpk);
+    __syncthreads();
   }
-  __syncthreads();
   for (int key = tid; key < a.LE; key += blockDim.x) off[key] -= sb[key / a.E];
   for (int l = tid; l < a.L; l += blockDim.x) a.ntpp[l] = sb[l + 1] - sb[l];
   if (wave_id() == 0 && (a.lora_ids || a.nact)) {
@@ -158,7 +148,7 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
     tot[key] = run;
   }
   __syncthreads();
-  layout_groups(a, tot, off, sb, wtot);
+  layout_groups(a, tot, off, sb, wtot, true);
   for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] += off[i % a.LE];
   __syncthreads();
   if (w < a.W) scatter_segment(a, s0, s1, cnt + w * a.LE, keys);
@@ -182,10 +172,11 @@ __global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
 }
 
 // One workgroup: per key, the exclusive prefix of the tile counts over tiles
-// (written back in place) and the total, then the layout of all groups.  The
-// counts of kPrefixBatch tiles are loaded before any is summed.  The totals
-// pass through key_off, each read back only by the thread that wrote it,
-// before key_off receives the group starts.
+// (written back in place) and the total (key_tot), then the layout of all
+// groups; the expert ids and padding sentinels are left to the tile
+// scatter, spread over its workgroups (one workgroup issuing every group's
+// stores was the slow part here).  The counts of kPrefixBatch tiles are
+// loaded before any is summed.
 constexpr int kPrefixBatch = 32;
 __global__ void __launch_bounds__(1024) align_meta_kernel(AlignParams a) {
   extern __shared__ int smem[];
@@ -205,9 +196,9 @@ __global__ void __launch_bounds__(1024) align_meta_kernel(AlignParams a) {
         run += v[i];
       }
     }
-    a.key_off[key] = run;
+    a.key_tot[key] = run;
   }
-  layout_groups(a, a.key_off, off, sb, wtot);
+  layout_groups(a, a.key_tot, off, sb, wtot, false);
   for (int key = threadIdx.x; key < a.LE; key += blockDim.x) a.key_off[key] = off[key];
 }
 
@@ -230,6 +221,14 @@ __global__ void __launch_bounds__(1024) align_tile_scatter_kernel(AlignParams a)
   }
   __syncthreads();
   if (s0 < s1) scatter_segment(a, s0, s1, cnt + w * a.LE, nullptr);
+  // expert ids and padding sentinels of this tile's share of the groups
+  const int per = (a.LE + a.ntiles - 1) / a.ntiles;
+  const int k0 = t * per, k1 = min(a.LE, k0 + per);
+  const int lpk = a.B / 4;
+  const int sub = lane_id() / lpk, sl = lane_id() % lpk;
+  const int stride = (blockDim.x / kWave) * (kWave / lpk);
+  for (int key = k0 + w * (kWave / lpk) + sub; key < k1; key += stride)
+    fill_group(a, key, a.key_off[key], a.key_tot[key], sl, lpk);
 }
 
 // ---------------------------------------------------------------- host
@@ -268,7 +267,7 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   pl.threads = int(W * kWave);
   pl.lds_bytes = size_t(W * LE * 4);
   pl.meta_lds_bytes = size_t((LE + L + 1 + 17) * 4);
-  pl.ws_bytes = (ntiles * LE + LE) * 4;
+  pl.ws_bytes = (ntiles * LE + 2 * LE) * 4;
   return pl;
 }
 

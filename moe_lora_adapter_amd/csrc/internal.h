@@ -16,6 +16,7 @@ struct AlignParams {
   int32_t* lora_ids;  // [L] or null
   int32_t* nact;      // [1] or null
   int32_t* tile_cnt;  // [ntiles, LE]  (multi-workgroup path)
+  int32_t* key_tot;   // [LE]
   int32_t* key_off;   // [LE]
   int32_t numel, topk, E, L, LE, B, nbits;
   int32_t cap, nb;
