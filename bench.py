@@ -48,10 +48,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
+# The sources each fused kernel is built from (its own file, the shared
+# device headers and the host code that sizes its launch); counters recorded
+# for a kernel stay valid while these are unchanged.
+KERNEL_SOURCES = {
+    "fused_stream_kernel": ["fused_stream.hip", "fused_valu.hip"],
+    "fused_valu_kernel": ["fused_valu.hip"],
+    "fused_mfma_kernel": ["fused_mfma.hip"],
+}
+SHARED_SOURCES = ["api.hip", "blocks.h", "common.h", "dma.h", "internal.h"]
+
+
+def kernel_sources_sha(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_lora_adapter_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -223,7 +234,7 @@ def load_traffic(kernel, workload):
             rec = json.load(f).get(f"{kernel}/{workload}")
     except (OSError, ValueError):
         return None, None
-    if not rec or rec.get("src_sha") != kernel_sources_sha():
+    if not rec or rec.get("src_sha") != kernel_sources_sha(kernel):
         return None, rec
     return rec.get("traffic_bytes_per_launch"), rec
 
