@@ -52,8 +52,8 @@ def log(msg):
 # device headers and the host code that sizes its launch); counters recorded
 # for a kernel stay valid while these are unchanged.
 KERNEL_SOURCES = {
-    "fused_stream_kernel": ["fused_stream.hip", "fused_valu.hip"],
-    "fused_valu_kernel": ["fused_valu.hip"],
+    "fused_stream_kernel": ["fused_stream.hip", "fused_valu.hip", "groups.h"],
+    "fused_valu_kernel": ["fused_valu.hip", "groups.h"],
     "fused_mfma_kernel": ["fused_mfma.hip"],
 }
 SHARED_SOURCES = ["api.hip", "blocks.h", "common.h", "dma.h", "internal.h"]
@@ -89,9 +89,13 @@ def algorithmic_work(case):
     fused_bytes = w_bytes + x_bytes + y_bytes + meta
     flops = 2.0 * P * s.S * s.r * (s.K + s.Ns)
     align_bytes = s.numel * 4 + s.M * 4 + padded * 4 + (padded // s.block_m) * 4 + 2 * s.L * 4
+    # the align-free path reads the routing (topk_ids, mapping) instead of the
+    # align outputs
+    naive_bytes = w_bytes + x_bytes + y_bytes + s.numel * 4 + s.M * 4 + (P * 4 if s.mul else 0)
     return dict(valid_pairs=P, active_groups=len(keys), fused_bytes=int(fused_bytes),
                 weight_bytes=int(w_bytes), x_bytes=int(x_bytes), y_bytes=int(y_bytes),
-                meta_bytes=int(meta), fused_flops=flops, align_bytes=int(align_bytes))
+                meta_bytes=int(meta), fused_flops=flops, align_bytes=int(align_bytes),
+                naive_bytes=int(naive_bytes))
 
 
 # ----------------------------------------------------------------- device inputs
@@ -127,25 +131,34 @@ def run_fused(ds, s, variant):
                        add_inputs=s.add, x_per_pair=s.x_per_pair, variant=variant)
 
 
+def run_naive(ds, s, block_m):
+    import moe_lora_adapter_amd as mla
+    mla.fused_moe_lora_naive(ds.x, ds.a, ds.b, ds.topk_ids, ds.mapping, ds.w, ds.y,
+                             mul_routed_weight=s.mul, add_inputs=s.add, block_m=block_m,
+                             x_per_pair=s.x_per_pair)
+
+
 def step(ds, s, variant):
     run_align(ds, s)
     run_fused(ds, s, variant)
 
 
 # ----------------------------------------------------------------- measurements
-def time_steps_graph(sets, s, variant, steps):
-    """Capture `steps` steps (rotating over the copies) in one graph; replay."""
+def time_steps_graph(sets, s, variant, steps, fn=None):
+    """Capture `steps` steps (rotating over the copies) in one graph; replay.
+    `fn(ds)` replaces the align + fused step when given."""
     import torch
+    fn = fn or (lambda ds: step(ds, s, variant))
     g = torch.cuda.CUDAGraph()
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        step(sets[0], s, variant)  # stream warm-up outside the capture
+        fn(sets[0])  # stream warm-up outside the capture
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
         for i in range(steps):
-            step(sets[i % len(sets)], s, variant)
+            fn(sets[i % len(sets)])
     torch.cuda.synchronize()
     g.replay()  # untimed replay: first-launch costs of the graph
     torch.cuda.synchronize()
@@ -168,7 +181,9 @@ def time_kernel_events(sets, s, variant, which, launches):
     e0.record()
     for i in range(launches):
         ds = sets[i % len(sets)]
-        if which == "fused":
+        if callable(which):
+            which(ds)
+        elif which == "fused":
             run_fused(ds, s, variant)
         else:
             run_align(ds, s)
@@ -253,6 +268,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 256 MiB device copies (rocprofv3 counter scaling)")
+    ap.add_argument("--path", default="sorted", choices=["sorted", "naive"],
+                    help="naive: time fused_moe_lora_naive (no align step) as the step")
+    ap.add_argument("--naive-block-m", type=int, default=None,
+                    help="block_m of the align-free path (default: the workload's)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -280,24 +299,41 @@ def main(argv=None):
     for _ in range(copies - 1):
         sets.append(DeviceSet(case, dev, proto=sets[0]))
     variant = args.variant
+    naive_ok = s.numel <= mla.NAIVE_MAX_PAIRS
+    naive_bm = args.naive_block_m or s.block_m
+    if args.path == "naive":
+        if not naive_ok:
+            print(f"bench.py: the align-free path takes at most {mla.NAIVE_MAX_PAIRS} pairs",
+                  file=sys.stderr)
+            return 2
+        variant = "valu"  # the kernel the align-free path runs
+    naive_fn = lambda ds: run_naive(ds, s, naive_bm)  # noqa: E731
+    step_fn = naive_fn if args.path == "naive" else (lambda ds: step(ds, s, variant))
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
-        step(sets[i % copies], s, variant)
+        step_fn(sets[i % copies])
     torch.cuda.synchronize()
     if args.calibrate_copy:
         copy_calibration(dev)
 
     log(f"timing {args.steps} steps (one graph)")
-    sec_per_step = time_steps_graph(sets, s, variant, args.steps)
+    sec_per_step = time_steps_graph(sets, s, variant, args.steps, fn=step_fn)
     log("timing kernels with events")
-    fused_avg = time_kernel_events(sets, s, variant, "fused", args.steps)
-    align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
+    if args.path == "naive":
+        fused_avg = time_kernel_events(sets, s, variant, naive_fn, args.steps)
+        align_avg = None
+        kbytes = work["naive_bytes"]
+    else:
+        fused_avg = time_kernel_events(sets, s, variant, "fused", args.steps)
+        align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
+        kbytes = work["fused_bytes"]
 
-    gbps = work["fused_bytes"] / (fused_avg * 1e-6) / 1e9
+    gbps = kbytes / (fused_avg * 1e-6) / 1e9
     tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
     kname = _kernel_name(s, variant)
-    traffic, _rec = load_traffic(kname, s.name)
+    traffic, _rec = load_traffic(kname, s.name if args.path == "sorted" else
+                                 f"{s.name}/naive_b{naive_bm}")
     out = {
         "metric": METRIC,
         "value": round(sec_per_step * 1e6, 3),
@@ -314,7 +350,9 @@ def main(argv=None):
         "config": {"workload": s.name, "M": s.M, "K": s.K, "N": s.N, "slices": s.S, "E": s.E,
                    "topk": s.topk, "L": s.L, "active_slots": s.active, "r": s.r,
                    "block_m": s.block_m, "mul_routed_weight": s.mul, "add_inputs": s.add,
-                   "x_per_pair": s.x_per_pair, "step": "moe_lora_align + fused_moe_lora",
+                   "x_per_pair": s.x_per_pair,
+                   "step": ("moe_lora_align + fused_moe_lora" if args.path == "sorted" else
+                            f"fused_moe_lora_naive (no align step), block_m={naive_bm}"),
                    "timing": "one HIP graph of K steps",
                    "cache": ("warm" if args.warm else
                              f"cold: {copies} rotated input copies, "
@@ -322,13 +360,30 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": work["fused_bytes"],
+                     "algorithmic_bytes_per_launch": kbytes,
                      "kernel_us_avg": round(fused_avg, 3)},
         "fused_tflops": round(tflops, 3),
         "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
-        "align_kernel_us_avg": round(align_avg, 3),
+        "align_kernel_us_avg": round(align_avg, 3) if align_avg is not None else None,
         "work": work,
     }
+    if args.path == "sorted" and naive_ok:
+        # the align-free path on the same inputs: no align launch, blocks
+        # formed on chip (block_m of the workload, and one pair per block)
+        out["align_free"] = []
+        for bm in sorted({s.block_m, 1}, reverse=True):
+            fn = lambda ds, bm=bm: run_naive(ds, s, bm)  # noqa: E731
+            log(f"align-free path, block_m={bm}")
+            for i in range(args.warmup):
+                fn(sets[i % copies])
+            us = time_steps_graph(sets, s, "valu", args.steps, fn=fn) * 1e6
+            kus = time_kernel_events(sets, s, "valu", fn, args.steps)
+            g = work["naive_bytes"] / (kus * 1e-6) / 1e9
+            out["align_free"].append({
+                "block_m": bm, "us_per_call": round(us, 3), "kernel": _kernel_name(s, "valu"),
+                "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
+                "frac": round(g / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_launch": work["naive_bytes"]})
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -185,6 +185,44 @@ MOE_LORA_API const char *fused_moe_lora_kernel_name(int64_t M, int32_t topk, int
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
                    int32_t x_per_pair, int32_t variant);
 
+/* Most (token, k) pairs fused_moe_lora_naive takes (M * topk). */
+#define MOE_LORA_NAIVE_MAX_PAIRS 1024
+
+/*
+ * fused_moe_lora_naive -- fused_moe_lora without the align step, for decode
+ * batches: the naive block assignment of the one-shot kernel (prhub summary
+ * of vLLM PR #42290, the dispatch fragment: a grid over tokens x top-k,
+ * slices and active slots, chosen instead of sorted_token_ids).
+ *
+ * Computes exactly the function of fused_moe_lora, with each pair's slot and
+ * expert read from token_lora_mapping and topk_ids as moe_lora_align reads
+ * them (pairs whose slot is outside [0, L) or whose expert is outside [0, E)
+ * are skipped; their Y rows are not touched).  Every workgroup forms the
+ * (slot, expert) groups on chip and cuts each into blocks of block_m pairs,
+ * ascending: the blocks moe_lora_align would produce for this block_m, so
+ * for block_m in {16, 32, 64, 128} the result is bit-identical to
+ * moe_lora_align followed by fused_moe_lora with MOE_LORA_VARIANT_VALU.
+ * block_m = 1 gives every valid pair its own block (the weights of a group
+ * are then read once per pair).
+ *
+ * Inputs  [device]:
+ *   x, lora_a, lora_b, topk_weights, y: as for fused_moe_lora.
+ *   topk_ids             int32 [M, topk]
+ *   token_lora_mapping   int32 [M]
+ * Sizes: as for fused_moe_lora, except block_m, a power of two in [1, 128].
+ * Runs the kernel fused_moe_lora_kernel_name names for MOE_LORA_VARIANT_VALU.
+ * Returns MOE_LORA_ERR_UNSUPPORTED when M * topk > MOE_LORA_NAIVE_MAX_PAIRS
+ * (larger batches go through moe_lora_align); other errors as for
+ * fused_moe_lora.  No workspace; deterministic.
+ */
+MOE_LORA_API int fused_moe_lora_naive(const uint16_t *x, int32_t x_per_pair,
+                   const uint16_t *lora_a, const uint16_t *lora_b,
+                   const int32_t *topk_ids, const int32_t *token_lora_mapping,
+                   const float *topk_weights, int32_t mul_routed_weight,
+                   int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, uint16_t *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

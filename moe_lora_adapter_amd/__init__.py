@@ -39,7 +39,12 @@ SIGNATURES = {
                                               _I32, _I32, _I32]),
     "fused_moe_lora_kernel_name": (ctypes.c_char_p, [_I64, _I32, _I32, _I32, _I32, _I32, _I32,
                                                      _I32, _I32, _I32, _I32]),
+    "fused_moe_lora_naive": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                            _P]),
 }
+
+NAIVE_MAX_PAIRS = 1024  # MOE_LORA_NAIVE_MAX_PAIRS
 
 
 class MoeLoraError(RuntimeError):
@@ -175,10 +180,8 @@ def moe_lora_align(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *
     return out
 
 
-def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
-                   mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
-                   variant: str | int = "auto", stream=None):
-    """Y (+)= (X A^T) B^T per routed pair and slice, in place on y; see moe_lora.h."""
+def _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair):
+    """Checks the tensors of a fused call; returns (M, topk, K, Ns, S, E, L, r)."""
     import torch
     dev = y.device
     _check(x, "x", torch.bfloat16, dev)
@@ -201,6 +204,14 @@ def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
         raise ValueError(f"x must be [{rows}, {K}]")
     if topk_weights is not None and tuple(topk_weights.shape) != (M, topk):
         raise ValueError("topk_weights must be [M, topk]")
+    return M, topk, K, Ns, S, E, L, r
+
+
+def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
+                   mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
+                   variant: str | int = "auto", stream=None):
+    """Y (+)= (X A^T) B^T per routed pair and slice, in place on y; see moe_lora.h."""
+    M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
     if align.sorted_token_ids.shape[0] != L:
         raise ValueError("align output was made for another L")
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
@@ -212,4 +223,24 @@ def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
         align.block_m, _dptr(y), v, _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora")
+    return y
+
+
+def fused_moe_lora_naive(x, lora_a, lora_b, topk_ids, token_lora_mapping, topk_weights, y, *,
+                         mul_routed_weight: bool, add_inputs: bool, block_m: int = 16,
+                         x_per_pair: bool = False, stream=None):
+    """fused_moe_lora without the align step (M * topk <= NAIVE_MAX_PAIRS); see moe_lora.h."""
+    import torch
+    M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
+    _check(topk_ids, "topk_ids", torch.int32, y.device)
+    _check(token_lora_mapping, "token_lora_mapping", torch.int32, y.device)
+    if tuple(topk_ids.shape) != (M, topk) or tuple(token_lora_mapping.shape) != (M,):
+        raise ValueError("topk_ids must be [M, topk] and token_lora_mapping [M]")
+    rc = lib().fused_moe_lora_naive(
+        _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b), _dptr(topk_ids),
+        _dptr(token_lora_mapping), _dptr(topk_weights), int(bool(mul_routed_weight)),
+        int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r, block_m, _dptr(y),
+        _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "fused_moe_lora_naive")
     return y

@@ -20,14 +20,17 @@ constexpr int64_t kMaxRank = 128;
 constexpr int64_t kInt32Max = 2147483647;
 
 bool block_m_ok(int64_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+bool naive_block_m_ok(int64_t b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shared size checks of both calls.  On success fills numel and cap.
+// Shared size checks of the calls.  On success fills numel and cap.
+// `naive`: the block sizes of the align-free path.
 int check_sizes(int64_t M, int64_t topk, int64_t E, int64_t L, int64_t block_m,
-                int64_t* numel_out, int64_t* cap_out) {
+                int64_t* numel_out, int64_t* cap_out, bool naive = false) {
   if (M < 0 || topk < 1 || E < 1 || L < 1) return MOE_LORA_ERR_INVALID;
-  if (E > kMaxE || L > kMaxL || L * E > kMaxLE || !block_m_ok(block_m))
+  if (E > kMaxE || L > kMaxL || L * E > kMaxLE ||
+      !(naive ? naive_block_m_ok(block_m) : block_m_ok(block_m)))
     return MOE_LORA_ERR_UNSUPPORTED;
   if (topk > kInt32Max || M > kInt32Max / topk) return MOE_LORA_ERR_UNSUPPORTED;
   const int64_t numel = M * topk;
@@ -223,6 +226,60 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
       pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
+  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                         const uint16_t* lora_b, const int32_t* topk_ids,
+                         const int32_t* token_lora_mapping, const float* topk_weights,
+                         int32_t mul_routed_weight, int32_t add_inputs, int64_t M, int32_t topk,
+                         int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                         int32_t block_m, uint16_t* y, void* stream) {
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap, true);
+  if (rc != MOE_LORA_OK) return rc;
+  if (K < 8 || Ns < 8 || S < 1 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
+  if ((x_per_pair != 0 && x_per_pair != 1) || (mul_routed_weight != 0 && mul_routed_weight != 1) ||
+      (add_inputs != 0 && add_inputs != 1))
+    return MOE_LORA_ERR_INVALID;
+  if (r > kMaxRank || numel > kNaiveMaxPairs) return MOE_LORA_ERR_UNSUPPORTED;
+  const int64_t N = int64_t(S) * Ns;
+  if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
+  if (numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
+  if (!x || !lora_a || !lora_b || !topk_ids || !token_lora_mapping || !y ||
+      (mul_routed_weight && !topk_weights))
+    return MOE_LORA_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y))
+    return MOE_LORA_ERR_INVALID;
+  const int64_t units = max_total_blocks(numel, int64_t(L) * E, block_m) * S;
+  if (units * 64 > kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;
+
+  FusedParams p{};
+  p.x = x;
+  p.a = lora_a;
+  p.b = lora_b;
+  p.topk_ids = topk_ids;
+  p.mapping = token_lora_mapping;
+  p.w = topk_weights;
+  p.y = y;
+  p.x_per_pair = x_per_pair;
+  p.mul = mul_routed_weight;
+  p.add = add_inputs;
+  p.numel = int32_t(numel);
+  p.topk = topk;
+  p.K = K;
+  p.Ns = Ns;
+  p.S = S;
+  p.E = E;
+  p.L = L;
+  p.r = r;
+  p.B = block_m;
+  p.N = int32_t(N);
+  p.units = int32_t(units);
+  p.xcd_cus = xcd_compute_units();
+  p.naive = 1;
+  p.nbits = nbits_for(int64_t(L) * E);
+  const hipError_t err = launch_fused_valu(p, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 

@@ -38,6 +38,7 @@
 #include "blocks.h"
 #include "common.h"
 #include "dma.h"
+#include "groups.h"
 #include "internal.h"
 
 namespace mlr {
@@ -52,6 +53,7 @@ static_assert(kIPS == 1, "a stage is one 16-byte chunk per thread");
 constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
 constexpr int kMaxCols = 2048;              // output columns per workgroup
 constexpr int kYBytes = kRows * kMaxCols * 2;
+constexpr int kMaxIds = 128;                // largest block_m
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
 #ifndef MLR_STREAM_SLOTS
@@ -118,7 +120,9 @@ __device__ __forceinline__ void issue_stage(const FusedParams& p, i32x4_t ar, i3
   }
 }
 
-template <int R>
+// NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
+// align-free path) instead of being read from the align outputs.
+template <int R, bool NAIVE>
 __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   using G = Geo<R>;
   constexpr int VP = 32 * G::KS + 8;  // bf16 pitch of the v rows
@@ -129,12 +133,23 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ int s_pair[kRows];
   __shared__ int s_row[kRows];
   __shared__ float s_w[kRows];
+  __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials reuse the X buffer");
+  static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
+  static_assert(!NAIVE || kST == kGroupThreads, "one pair per thread");
 
   // units = (block, slice); split count: a compute unit per working
   // workgroup, at least MLR_STREAM_MIN_COLS and at most kMaxCols columns each
-  const BlockScan sc = scan_blocks(p);
-  const int total = sc.total;
+  GroupLds& gl = *reinterpret_cast<GroupLds*>(ring);  // free until the first stage is loaded
+  PairGroup pg;
+  BlockScan sc;
+  int total;
+  if constexpr (NAIVE) {
+    total = group_pairs(p, gl, pg);
+  } else {
+    sc = scan_blocks(p);
+    total = sc.total;
+  }
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int need = (p.Ns + kMaxCols - 1) / kMaxCols;
@@ -148,12 +163,19 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const int n1 = min(p.Ns, n0 + nsz);
   const int ncols = n1 - n0;
   const int g = unit / p.S, s = unit - g * p.S;
-  int l, b;
-  find_block(p, sc, g, l, b);
-  // the first pass's pair ids are loaded before the expert id is waited for
-  const int32_t* srow = p.sorted + l * p.cap + b * p.B;
-  const int id0 = (threadIdx.x < kRows && int(threadIdx.x) < p.B) ? srow[threadIdx.x] : p.numel;
-  const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  int l, e;
+  const int32_t* srow = nullptr;
+  int id0 = p.numel;
+  if constexpr (NAIVE) {
+    group_block(p, gl, pg, g, s_ids, l, e);
+  } else {
+    int b;
+    find_block(p, sc, g, l, b);
+    // the first pass's pair ids are loaded before the expert id is waited for
+    srow = p.sorted + l * p.cap + b * p.B;
+    id0 = (threadIdx.x < kRows && int(threadIdx.x) < p.B) ? srow[threadIdx.x] : p.numel;
+    e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  }
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
   const i32x4_t ar = dma_rsrc(p.a + wsel * R * p.K, uint32_t(R * p.K * 2));
   const i32x4_t br = dma_rsrc(p.b + wsel * p.Ns * R + int64_t(n0) * R, uint32_t(ncols * R * 2));
@@ -176,7 +198,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       int pid = p.numel, xrow = -1;
       float wv = 1.f;
       if (g0 + tid < p.B) {
-        const int id = g0 == 0 ? id0 : srow[g0 + tid];
+        const int id = NAIVE ? s_ids[g0 + tid] : (g0 == 0 ? id0 : srow[g0 + tid]);
         if (id < p.numel) {
           pid = id;
           xrow = p.x_per_pair ? id : id / p.topk;
@@ -319,12 +341,18 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t need = (p.Ns + kMaxCols - 1) / kMaxCols;
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
   const dim3 grid(unsigned(kXcds * slots));
+#define MLR_STREAM_CASE(R_)                                                                  \
+  case R_:                                                                                   \
+    if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true>), grid, dim3(kST), 0, st, p); \
+    else hipLaunchKernelGGL((fused_stream_kernel<R_, false>), grid, dim3(kST), 0, st, p);       \
+    break;
   switch (p.r) {
-    case 32: hipLaunchKernelGGL(fused_stream_kernel<32>, grid, dim3(kST), 0, st, p); break;
-    case 64: hipLaunchKernelGGL(fused_stream_kernel<64>, grid, dim3(kST), 0, st, p); break;
-    case 128: hipLaunchKernelGGL(fused_stream_kernel<128>, grid, dim3(kST), 0, st, p); break;
+    MLR_STREAM_CASE(32)
+    MLR_STREAM_CASE(64)
+    MLR_STREAM_CASE(128)
     default: return hipErrorInvalidValue;
   }
+#undef MLR_STREAM_CASE
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 
 #include "blocks.h"
 #include "common.h"
+#include "groups.h"
 #include "internal.h"
 
 namespace mlr {
@@ -323,7 +324,9 @@ __device__ __forceinline__ void valu_rows(const FusedParams& p, const uint16_t* 
 
 // Blocks of up to two valid rows take 2-row groups; larger blocks take
 // 4-row groups (one pass over A and B per group).
-template <int JW, int CPR>
+// NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
+// align-free path) instead of being read from the align outputs.
+template <int JW, int CPR, bool NAIVE>
 __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused_valu_kernel(FusedParams p, ShrinkShape sh) {
   constexpr int RG = 4;  // LDS sized for the larger group
   __shared__ int s_pair[kMaxB];
@@ -331,14 +334,24 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   __shared__ float s_v[kMaxRG * kMaxR];
   __shared__ float s_part[kMaxRG * 256];
   __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
+  __shared__ __align__(16) uint8_t s_grp[NAIVE ? sizeof(GroupLds) : 1];
+  static_assert(!NAIVE || kThreads == kGroupThreads, "one pair per thread");
+  GroupLds& gl = *reinterpret_cast<GroupLds*>(s_grp);
 
   // The blocks present decide the split count: as many column splits (of at
   // least MLR_VALU_MIN_COLS columns) as give every working workgroup a compute
   // unit of its own.  Unit u goes to XCD u % 8, so an XCD holds
   // ceil(units / 8) * n_split of them; a second workgroup on a compute unit
   // was measured to cost far more than a split saves.
-  const BlockScan sc = scan_blocks(p);
-  const int total = sc.total;
+  PairGroup pg;
+  BlockScan sc;
+  int total;
+  if constexpr (NAIVE) {
+    total = group_pairs(p, gl, pg);
+  } else {
+    sc = scan_blocks(p);
+    total = sc.total;
+  }
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int u8 = per_xcd * kXcds;
@@ -353,9 +366,13 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   if (n0 >= p.Ns) return;
   const int n1 = min(p.Ns, n0 + nsz);
   const int g = unit / p.S, s = unit - g * p.S;
-  int l, b;
-  find_block(p, sc, g, l, b);
-  const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  int l, e, b = 0;
+  if constexpr (NAIVE) {
+    group_block(p, gl, pg, g, s_pair, l, e);  // pair ids straight into s_pair
+  } else {
+    find_block(p, sc, g, l, b);
+    e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  }
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
   const uint16_t* A = p.a + wsel * p.r * p.K;
   const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
@@ -363,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   const int tid = threadIdx.x;
   int valid = 0;
   if (tid < p.B) {
-    const int pid = p.sorted[l * p.cap + b * p.B + tid];
+    const int pid = NAIVE ? s_pair[tid] : p.sorted[l * p.cap + b * p.B + tid];
     valid = pid < p.numel;
     s_pair[tid] = pid;
     s_row[tid] = valid ? (p.x_per_pair ? pid : pid / p.topk) : 0;
@@ -379,7 +396,8 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
 
 template <int JW, int CPR>
 static void launch(const FusedParams& p, ShrinkShape sh, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((fused_valu_kernel<JW, CPR>), grid, dim3(kThreads), 0, st, p, sh);
+  if (p.naive) hipLaunchKernelGGL((fused_valu_kernel<JW, CPR, true>), grid, dim3(kThreads), 0, st, p, sh);
+  else hipLaunchKernelGGL((fused_valu_kernel<JW, CPR, false>), grid, dim3(kThreads), 0, st, p, sh);
 }
 
 #ifndef MLR_VALU_STREAM  // decode shapes the stream kernel supports go there

@@ -45,6 +45,8 @@ struct FusedParams {
   const int32_t* sorted;
   const int32_t* eids;
   const int32_t* ntpp;
+  const int32_t* topk_ids;  // align-free path: [numel]
+  const int32_t* mapping;   // align-free path: [numel / topk]
   const float* w;      // [numel] or null
   uint16_t* y;         // [numel, N]
   int32_t x_per_pair, mul, add;
@@ -52,7 +54,12 @@ struct FusedParams {
   int32_t cap, nb;
   int32_t units;       // upper bound on blocks, times S
   int32_t xcd_cus;     // compute units per XCD of the current device
+  int32_t naive;       // 1: blocks formed on chip from topk_ids and mapping (no align outputs)
+  int32_t nbits;       // align-free path: bits of a key l * E + e
 };
+
+// Most pairs the align-free path groups (one per thread of a workgroup).
+constexpr int64_t kNaiveMaxPairs = 1024;
 
 // Upper bound on the number of blocks over all slots: every non-empty
 // (slot, expert) group adds at most block_m - 1 padding entries.

@@ -92,6 +92,20 @@ class DeviceCase:
         return y
 
 
+    def naive(self, block_m=None, y=None, add=None, mul=None, b=None, a=None):
+        """The align-free path (fused_moe_lora_naive) on the same inputs."""
+        s = self.s
+        y = self.y_in.clone() if y is None else y
+        mla.fused_moe_lora_naive(self.x, self.a if a is None else a, self.b if b is None else b,
+                                 self.topk_ids, self.mapping, self.w, y,
+                                 mul_routed_weight=s.mul if mul is None else mul,
+                                 add_inputs=s.add if add is None else add,
+                                 block_m=s.block_m if block_m is None else block_m,
+                                 x_per_pair=s.x_per_pair)
+        torch.cuda.synchronize()
+        return y
+
+
 def valid_pairs(case) -> np.ndarray:
     s = case.shape
     slot = np.repeat(case.token_lora_mapping, s.topk)

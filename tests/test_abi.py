@@ -147,6 +147,70 @@ def test_variant_query_rejects_like_fused(kw, status):
     assert fused_call(**a) == status
 
 
+def naive_call(**kw):
+    a = dict(x=P16, xpp=0, la=P16, lb=P16, ids=P16, mapping=P16, w=None, mul=0, add=1, M=16,
+             topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16)
+    a.update(kw)
+    return mla.lib().fused_moe_lora_naive(a["x"], a["xpp"], a["la"], a["lb"], a["ids"],
+                                          a["mapping"], a["w"], a["mul"], a["add"], a["M"],
+                                          a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"],
+                                          a["r"], a["B"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.ERR_INVALID),
+    (dict(la=None), mla.ERR_INVALID),
+    (dict(lb=None), mla.ERR_INVALID),
+    (dict(ids=None), mla.ERR_INVALID),
+    (dict(mapping=None), mla.ERR_INVALID),
+    (dict(y=None), mla.ERR_INVALID),
+    (dict(mul=1, w=None), mla.ERR_INVALID),
+    (dict(mul=2), mla.ERR_INVALID),
+    (dict(add=3), mla.ERR_INVALID),
+    (dict(xpp=-1), mla.ERR_INVALID),
+    (dict(K=2884), mla.ERR_INVALID),
+    (dict(Ns=4), mla.ERR_INVALID),
+    (dict(S=0), mla.ERR_INVALID),
+    (dict(r=0), mla.ERR_INVALID),
+    (dict(M=-1), mla.ERR_INVALID),
+    (dict(topk=0), mla.ERR_INVALID),
+    (dict(r=129), mla.ERR_UNSUPPORTED),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
+    # block sizes: powers of two from 1 to 128
+    (dict(B=0), mla.ERR_UNSUPPORTED),
+    (dict(B=3), mla.ERR_UNSUPPORTED),
+    (dict(B=24), mla.ERR_UNSUPPORTED),
+    (dict(B=256), mla.ERR_UNSUPPORTED),
+    # more pairs than one workgroup groups
+    (dict(M=257, topk=4), mla.ERR_UNSUPPORTED),
+    (dict(M=1025, topk=1), mla.ERR_UNSUPPORTED),
+    (dict(x=V(24)), mla.ERR_INVALID),
+    (dict(la=V(40)), mla.ERR_INVALID),
+    (dict(M=0), mla.OK),
+    (dict(M=0, x=None, y=None, ids=None, mapping=None), mla.OK),
+])
+def test_naive_rejects(kw, status):
+    assert naive_call(**kw) == status
+
+
+def test_naive_binding_checks_before_calling():
+    torch = pytest.importorskip("torch")
+    bf = dict(dtype=torch.bfloat16)
+    x, y = torch.zeros((4, 64), **bf), torch.zeros((4, 2, 32), **bf)
+    a, b = torch.zeros((1, 2, 8, 8, 64), **bf), torch.zeros((1, 2, 8, 32, 8), **bf)
+    ids, mp = torch.zeros((4, 2), dtype=torch.int32), torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        mla.fused_moe_lora_naive(x, a, b, ids.long(), mp, None, y, mul_routed_weight=False,
+                                 add_inputs=True)
+    with pytest.raises(ValueError):
+        mla.fused_moe_lora_naive(x, a, b, ids[:, :1].contiguous(), mp, None, y,
+                                 mul_routed_weight=False, add_inputs=True)
+    with pytest.raises(ValueError):
+        mla.fused_moe_lora_naive(x, a, b, ids, mp[:3].contiguous(), None, y,
+                                 mul_routed_weight=False, add_inputs=True)
+
+
 def test_variant_query_resolves_auto():
     fv = mla.fused_variant
     # decode: about two rows per (slot, expert) group -> vector kernel
