@@ -131,11 +131,17 @@ def run_fused(ds, s, variant):
                        add_inputs=s.add, x_per_pair=s.x_per_pair, variant=variant)
 
 
-def run_naive(ds, s, block_m):
+def run_naive(ds, s, block_m, variant):
     import moe_lora_adapter_amd as mla
     mla.fused_moe_lora_naive(ds.x, ds.a, ds.b, ds.topk_ids, ds.mapping, ds.w, ds.y,
                              mul_routed_weight=s.mul, add_inputs=s.add, block_m=block_m,
-                             x_per_pair=s.x_per_pair)
+                             x_per_pair=s.x_per_pair, variant=variant)
+
+
+def naive_kernel_name(s, block_m, variant):
+    """The kernel of the align-free path: the sorted path's choice for
+    block_m >= 16, the vector kernels below that."""
+    return _kernel_name(s, variant if block_m >= 16 else "valu")
 
 
 def step(ds, s, variant):
@@ -306,8 +312,7 @@ def main(argv=None):
             print(f"bench.py: the align-free path takes at most {mla.NAIVE_MAX_PAIRS} pairs",
                   file=sys.stderr)
             return 2
-        variant = "valu"  # the kernel the align-free path runs
-    naive_fn = lambda ds: run_naive(ds, s, naive_bm)  # noqa: E731
+    naive_fn = lambda ds: run_naive(ds, s, naive_bm, variant)  # noqa: E731
     step_fn = naive_fn if args.path == "naive" else (lambda ds: step(ds, s, variant))
 
     log(f"warmup {args.warmup} steps")
@@ -331,7 +336,8 @@ def main(argv=None):
 
     gbps = kbytes / (fused_avg * 1e-6) / 1e9
     tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
-    kname = _kernel_name(s, variant)
+    kname = (_kernel_name(s, variant) if args.path == "sorted" else
+             naive_kernel_name(s, naive_bm, variant))
     traffic, _rec = load_traffic(kname, s.name if args.path == "sorted" else
                                  f"{s.name}/naive_b{naive_bm}")
     out = {
@@ -372,15 +378,16 @@ def main(argv=None):
         # formed on chip (block_m of the workload, and one pair per block)
         out["align_free"] = []
         for bm in sorted({s.block_m, 1}, reverse=True):
-            fn = lambda ds, bm=bm: run_naive(ds, s, bm)  # noqa: E731
+            fn = lambda ds, bm=bm: run_naive(ds, s, bm, variant)  # noqa: E731
             log(f"align-free path, block_m={bm}")
             for i in range(args.warmup):
                 fn(sets[i % copies])
-            us = time_steps_graph(sets, s, "valu", args.steps, fn=fn) * 1e6
-            kus = time_kernel_events(sets, s, "valu", fn, args.steps)
+            us = time_steps_graph(sets, s, variant, args.steps, fn=fn) * 1e6
+            kus = time_kernel_events(sets, s, variant, fn, args.steps)
             g = work["naive_bytes"] / (kus * 1e-6) / 1e9
             out["align_free"].append({
-                "block_m": bm, "us_per_call": round(us, 3), "kernel": _kernel_name(s, "valu"),
+                "block_m": bm, "us_per_call": round(us, 3),
+                "kernel": naive_kernel_name(s, bm, variant),
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})

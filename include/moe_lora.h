@@ -201,7 +201,7 @@ MOE_LORA_API const char *fused_moe_lora_kernel_name(int64_t M, int32_t topk, int
  * (slot, expert) groups on chip and cuts each into blocks of block_m pairs,
  * ascending: the blocks moe_lora_align would produce for this block_m, so
  * for block_m in {16, 32, 64, 128} the result is bit-identical to
- * moe_lora_align followed by fused_moe_lora with MOE_LORA_VARIANT_VALU.
+ * moe_lora_align followed by fused_moe_lora with the same variant.
  * block_m = 1 gives every valid pair its own block (the weights of a group
  * are then read once per pair).
  *
@@ -209,8 +209,10 @@ MOE_LORA_API const char *fused_moe_lora_kernel_name(int64_t M, int32_t topk, int
  *   x, lora_a, lora_b, topk_weights, y: as for fused_moe_lora.
  *   topk_ids             int32 [M, topk]
  *   token_lora_mapping   int32 [M]
- * Sizes: as for fused_moe_lora, except block_m, a power of two in [1, 128].
- * Runs the kernel fused_moe_lora_kernel_name names for MOE_LORA_VARIANT_VALU.
+ * Sizes: as for fused_moe_lora, except block_m, a power of two in [1, 128]
+ * (the MFMA variant takes block_m >= 16; AUTO picks it under the same rule as
+ * fused_moe_lora, and fused_moe_lora_kernel_name / fused_moe_lora_variant
+ * answer for block_m >= 16; smaller blocks always run the vector variant).
  * Returns MOE_LORA_ERR_UNSUPPORTED when M * topk > MOE_LORA_NAIVE_MAX_PAIRS
  * (larger batches go through moe_lora_align); other errors as for
  * fused_moe_lora.  No workspace; deterministic.
@@ -221,7 +223,7 @@ MOE_LORA_API int fused_moe_lora_naive(const uint16_t *x, int32_t x_per_pair,
                    const float *topk_weights, int32_t mul_routed_weight,
                    int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
-                   int32_t block_m, uint16_t *y, void *stream);
+                   int32_t block_m, uint16_t *y, int32_t variant, void *stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ SIGNATURES = {
                                                      _I32, _I32, _I32, _I32]),
     "fused_moe_lora_naive": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                             _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
-                                            _P]),
+                                            _I32, _P]),
 }
 
 NAIVE_MAX_PAIRS = 1024  # MOE_LORA_NAIVE_MAX_PAIRS
@@ -228,7 +228,7 @@ def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
 
 def fused_moe_lora_naive(x, lora_a, lora_b, topk_ids, token_lora_mapping, topk_weights, y, *,
                          mul_routed_weight: bool, add_inputs: bool, block_m: int = 16,
-                         x_per_pair: bool = False, stream=None):
+                         x_per_pair: bool = False, variant: str | int = "auto", stream=None):
     """fused_moe_lora without the align step (M * topk <= NAIVE_MAX_PAIRS); see moe_lora.h."""
     import torch
     M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
@@ -240,7 +240,7 @@ def fused_moe_lora_naive(x, lora_a, lora_b, topk_ids, token_lora_mapping, topk_w
         _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b), _dptr(topk_ids),
         _dptr(token_lora_mapping), _dptr(topk_weights), int(bool(mul_routed_weight)),
         int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r, block_m, _dptr(y),
-        _stream_ptr(stream))
+        VARIANTS[variant] if isinstance(variant, str) else int(variant), _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora_naive")
     return y

@@ -234,17 +234,19 @@ int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* 
                          const int32_t* token_lora_mapping, const float* topk_weights,
                          int32_t mul_routed_weight, int32_t add_inputs, int64_t M, int32_t topk,
                          int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
-                         int32_t block_m, uint16_t* y, void* stream) {
+                         int32_t block_m, uint16_t* y, int32_t variant, void* stream) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap, true);
   if (rc != MOE_LORA_OK) return rc;
   if (K < 8 || Ns < 8 || S < 1 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
   if ((x_per_pair != 0 && x_per_pair != 1) || (mul_routed_weight != 0 && mul_routed_weight != 1) ||
-      (add_inputs != 0 && add_inputs != 1))
+      (add_inputs != 0 && add_inputs != 1) || variant < 0 || variant > 2)
     return MOE_LORA_ERR_INVALID;
   if (r > kMaxRank || numel > kNaiveMaxPairs) return MOE_LORA_ERR_UNSUPPORTED;
   const int64_t N = int64_t(S) * Ns;
   if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
+  if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair))
+    return MOE_LORA_ERR_UNSUPPORTED;
   if (numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
   if (!x || !lora_a || !lora_b || !topk_ids || !token_lora_mapping || !y ||
       (mul_routed_weight && !topk_weights))
@@ -279,7 +281,10 @@ int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* 
   p.xcd_cus = xcd_compute_units();
   p.naive = 1;
   p.nbits = nbits_for(int64_t(L) * E);
-  const hipError_t err = launch_fused_valu(p, static_cast<hipStream_t>(stream));
+  const bool use_mfma =
+      pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 

@@ -37,6 +37,7 @@
 #include "blocks.h"
 #include "common.h"
 #include "dma.h"
+#include "groups.h"
 #include "internal.h"
 
 namespace mlr {
@@ -48,6 +49,7 @@ namespace {
 constexpr int kThreadsM = MLR_MFMA_THREADS;
 constexpr int kWavesM = kThreadsM / kWave;
 constexpr int kPassRows = 64;
+constexpr int kMaxIdsM = 128;  // largest block_m
 constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 
 #ifndef MLR_MFMA_MIN_COLS
@@ -374,18 +376,30 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   stage_barrier<0>();  // V (slot 0) and the row tables are reused by the next pass
 }
 
-template <int RT>
+// NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
+// align-free path) instead of being read from the align outputs.
+template <int RT, bool NAIVE>
 __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   __shared__ __align__(16) uint8_t ring[3 * Slots<RT>::BYTES];
   __shared__ int s_row[kPassRows];
   __shared__ int s_pair[kPassRows];
   __shared__ float s_wt[kPassRows];
+  __shared__ int s_ids[NAIVE ? kMaxIdsM : 1];  // pair ids of the block (align-free path)
+  static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
   // units = (block, slice); the split count gives every working workgroup a
   // slot (MLR_MFMA_OCCUPANCY per compute unit), at least MLR_MFMA_MIN_COLS
   // columns each
-  const BlockScan sc = scan_blocks(p);
-  const int total = sc.total;
+  GroupLds& gl = *reinterpret_cast<GroupLds*>(ring);  // free until the first stage is loaded
+  PairGroup<kThreadsM> pg;
+  BlockScan sc;
+  int total;
+  if constexpr (NAIVE) {
+    total = group_pairs(p, gl, pg);
+  } else {
+    sc = scan_blocks(p);
+    total = sc.total;
+  }
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
@@ -397,9 +411,13 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
   if (n0 >= p.Ns) return;
   const int n1 = min(p.Ns, n0 + nsz);
   const int g = unit / p.S, s = unit - g * p.S;
-  int l, b;
-  find_block(p, sc, g, l, b);
-  const int e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  int l, e, b = 0;
+  if constexpr (NAIVE) {
+    group_block(p, gl, pg, g, s_ids, l, e);
+  } else {
+    find_block(p, sc, g, l, b);
+    e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+  }
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
 
   PassCtx c;
@@ -422,7 +440,7 @@ __global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
       int pid = p.numel, xr = -1;
       float wv = 1.f;
       if (r0 + tid < p.B) {
-        pid = p.sorted[l * p.cap + b * p.B + r0 + tid];
+        pid = NAIVE ? s_ids[r0 + tid] : p.sorted[l * p.cap + b * p.B + r0 + tid];
         if (pid < p.numel) {
           xr = p.x_per_pair ? pid : pid / p.topk;
           if (p.mul) wv = p.w[pid];
@@ -465,16 +483,23 @@ hipError_t launch_fused_mfma(FusedParams p, hipStream_t st) {
   const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
   const int64_t slots = std::max<int64_t>(per_xcd, int64_t(p.xcd_cus) * MLR_MFMA_OCCUPANCY);
   const dim3 grid(unsigned(kXcds * slots));
+#define MLR_MFMA_CASE(RT_)                                                                       \
+  case RT_:                                                                                      \
+    if (p.naive) hipLaunchKernelGGL((fused_mfma_kernel<RT_, true>), grid, dim3(kThreadsM), 0, st, p); \
+    else hipLaunchKernelGGL((fused_mfma_kernel<RT_, false>), grid, dim3(kThreadsM), 0, st, p);       \
+    break;
   switch (rt) {
-    case 1: hipLaunchKernelGGL(fused_mfma_kernel<1>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 2: hipLaunchKernelGGL(fused_mfma_kernel<2>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 3: hipLaunchKernelGGL(fused_mfma_kernel<3>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 4: hipLaunchKernelGGL(fused_mfma_kernel<4>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 5: hipLaunchKernelGGL(fused_mfma_kernel<5>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 6: hipLaunchKernelGGL(fused_mfma_kernel<6>, grid, dim3(kThreadsM), 0, st, p); break;
-    case 7: hipLaunchKernelGGL(fused_mfma_kernel<7>, grid, dim3(kThreadsM), 0, st, p); break;
-    default: hipLaunchKernelGGL(fused_mfma_kernel<8>, grid, dim3(kThreadsM), 0, st, p); break;
+    MLR_MFMA_CASE(1)
+    MLR_MFMA_CASE(2)
+    MLR_MFMA_CASE(3)
+    MLR_MFMA_CASE(4)
+    MLR_MFMA_CASE(5)
+    MLR_MFMA_CASE(6)
+    MLR_MFMA_CASE(7)
+    MLR_MFMA_CASE(8)
+    default: return hipErrorInvalidValue;
   }
+#undef MLR_MFMA_CASE
   return hipGetLastError();
 }
 

@@ -136,12 +136,11 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials reuse the X buffer");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
-  static_assert(!NAIVE || kST == kGroupThreads, "one pair per thread");
 
   // units = (block, slice); split count: a compute unit per working
   // workgroup, at least MLR_STREAM_MIN_COLS and at most kMaxCols columns each
   GroupLds& gl = *reinterpret_cast<GroupLds*>(ring);  // free until the first stage is loaded
-  PairGroup pg;
+  PairGroup<kST> pg;
   BlockScan sc;
   int total;
   if constexpr (NAIVE) {

@@ -335,7 +335,6 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   __shared__ float s_part[kMaxRG * 256];
   __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
   __shared__ __align__(16) uint8_t s_grp[NAIVE ? sizeof(GroupLds) : 1];
-  static_assert(!NAIVE || kThreads == kGroupThreads, "one pair per thread");
   GroupLds& gl = *reinterpret_cast<GroupLds*>(s_grp);
 
   // The blocks present decide the split count: as many column splits (of at
@@ -343,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   // unit of its own.  Unit u goes to XCD u % 8, so an XCD holds
   // ceil(units / 8) * n_split of them; a second workgroup on a compute unit
   // was measured to cost far more than a split saves.
-  PairGroup pg;
+  PairGroup<kThreads> pg;
   BlockScan sc;
   int total;
   if constexpr (NAIVE) {

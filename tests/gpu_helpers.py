@@ -92,7 +92,7 @@ class DeviceCase:
         return y
 
 
-    def naive(self, block_m=None, y=None, add=None, mul=None, b=None, a=None):
+    def naive(self, block_m=None, y=None, add=None, mul=None, b=None, a=None, variant="auto"):
         """The align-free path (fused_moe_lora_naive) on the same inputs."""
         s = self.s
         y = self.y_in.clone() if y is None else y
@@ -101,7 +101,7 @@ class DeviceCase:
                                  mul_routed_weight=s.mul if mul is None else mul,
                                  add_inputs=s.add if add is None else add,
                                  block_m=s.block_m if block_m is None else block_m,
-                                 x_per_pair=s.x_per_pair)
+                                 x_per_pair=s.x_per_pair, variant=variant)
         torch.cuda.synchronize()
         return y
 

@@ -149,12 +149,12 @@ def test_variant_query_rejects_like_fused(kw, status):
 
 def naive_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, ids=P16, mapping=P16, w=None, mul=0, add=1, M=16,
-             topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16)
+             topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16, variant=0)
     a.update(kw)
     return mla.lib().fused_moe_lora_naive(a["x"], a["xpp"], a["la"], a["lb"], a["ids"],
                                           a["mapping"], a["w"], a["mul"], a["add"], a["M"],
                                           a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"],
-                                          a["r"], a["B"], a["y"], None)
+                                          a["r"], a["B"], a["y"], a["variant"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -187,6 +187,11 @@ def naive_call(**kw):
     (dict(M=1025, topk=1), mla.ERR_UNSUPPORTED),
     (dict(x=V(24)), mla.ERR_INVALID),
     (dict(la=V(40)), mla.ERR_INVALID),
+    (dict(variant=3), mla.ERR_INVALID),
+    (dict(variant=-1), mla.ERR_INVALID),
+    # the MFMA kernel: r a multiple of 8, blocks of at least 16 pairs
+    (dict(variant=mla.VARIANT_MFMA, r=12), mla.ERR_UNSUPPORTED),
+    (dict(variant=mla.VARIANT_MFMA, B=8), mla.ERR_UNSUPPORTED),
     (dict(M=0), mla.OK),
     (dict(M=0, x=None, y=None, ids=None, mapping=None), mla.OK),
 ])

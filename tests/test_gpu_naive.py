@@ -2,7 +2,7 @@
 
 Against the CPU oracle: |gpu - oracle| <= 1e-2 * (1 + |oracle|) elementwise,
 rows of pairs in no slot bit-identical to the input.  Against the sorted
-path (moe_lora_align + fused_moe_lora, vector variant) at the same block_m:
+path (moe_lora_align + fused_moe_lora) with the same variant and block_m:
 bit-identical, since both hand the same blocks to the same kernel.
 """
 import sys
@@ -39,20 +39,27 @@ def _ref(orc, c):
                      c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
 
 
-def _check(orc, c, dc, block_m, what, sorted_too=True):
+def _variants(s, block_m):
+    """The variants the align-free path takes for these sizes (MFMA needs
+    r % 8 == 0 and blocks of at least 16 pairs)."""
+    ok = s.r % 8 == 0 and block_m >= 16
+    return ["valu"] + (["mfma"] if ok else [])
+
+
+def _check(orc, c, dc, block_m, what, variant="auto", ref=None):
     s = c.shape
-    y = dc.naive(block_m=block_m)
+    y = dc.naive(block_m=block_m, variant=variant)
     got = gh.bf16_host_f64(y).reshape(s.numel, s.N)
-    gh.assert_fused_close(got, _ref(orc, c), what)
+    gh.assert_fused_close(got, _ref(orc, c) if ref is None else ref, f"{what}/{variant}")
     base = gh.bf16_host_f64(dc.y_in).reshape(s.numel, s.N)
     inval = ~gh.valid_pairs(c)
     assert np.array_equal(got[inval], base[inval]), f"{what}: rows of unmapped pairs changed"
-    if sorted_too and block_m in (16, 32, 64, 128):
+    if block_m in (16, 32, 64, 128):
         dc.s = s.replace(block_m=block_m)
-        ys = dc.fused(variant="valu")
+        ys = dc.fused(variant=variant)
         dc.s = s
         assert torch.equal(y.view(torch.int16), ys.view(torch.int16)), \
-            f"{what}: differs from the sorted path"
+            f"{what}/{variant}: differs from the sorted path"
     return y
 
 
@@ -62,9 +69,11 @@ def test_naive_decode_workloads(orc, name, dist):
     s = synth.shape(name, dist=dist)
     c = synth.draw(s)
     dc = gh.DeviceCase(c)
+    ref = _ref(orc, c)
     for bm in (s.block_m, 1):
-        _log(f"naive {name} {dist} block_m={bm}")
-        _check(orc, c, dc, bm, f"{name}/{dist}/B{bm}")
+        for v in ["auto"] + _variants(s, bm):
+            _log(f"naive {name} {dist} block_m={bm} {v}")
+            _check(orc, c, dc, bm, f"{name}/{dist}/B{bm}", v, ref)
 
 
 NAIVE_EDGE = [
@@ -80,6 +89,9 @@ NAIVE_EDGE = [
     dict(K=64, Ns=64, r=32, block_m=16, M=1024, E=1, topk=1, L=1, active=1, p_neg=0.0),
     dict(K=64, Ns=64, r=16, block_m=16, M=1024, E=1024, topk=1, L=8, active=8, p_neg=0.1),
     dict(K=64, Ns=64, r=64, block_m=1, M=256, E=64, topk=4, L=4, active=4, p_neg=0.1),
+    # just past one wavefront of pairs, and a dense decode batch (MFMA by AUTO)
+    dict(K=128, Ns=64, r=32, block_m=16, M=65, E=4, topk=1, L=2, active=2, p_neg=0.1),
+    dict(K=256, Ns=192, r=16, block_m=32, M=200, E=1, topk=1, L=3, active=3, p_neg=0.0),
     # L * E = 1: zero key bits
     dict(K=72, Ns=40, r=24, block_m=16, M=30, E=1, topk=1, L=1, active=1, p_neg=0.3),
     # keys whose bits are all ones (L * E a power of two) next to invalid pairs
@@ -98,9 +110,12 @@ NAIVE_EDGE = [
 @pytest.mark.parametrize("i", range(len(NAIVE_EDGE)))
 def test_naive_edge_shapes(orc, i):
     s = synth.shape("tiny", dist="stress", seed=9500 + i, **NAIVE_EDGE[i])
-    _log(f"naive edge {i} {NAIVE_EDGE[i]}")
     c = synth.draw(s)
-    _check(orc, c, gh.DeviceCase(c), s.block_m, f"edge {i}")
+    dc = gh.DeviceCase(c)
+    ref = _ref(orc, c)
+    for v in _variants(s, s.block_m):
+        _log(f"naive edge {i} {NAIVE_EDGE[i]} {v}")
+        _check(orc, c, dc, s.block_m, f"edge {i}", v, ref)
 
 
 def test_naive_out_of_range_ids_and_duplicates(orc):
@@ -113,9 +128,11 @@ def test_naive_out_of_range_ids_and_duplicates(orc):
     c.topk_ids[1::6, 0] = s.E
     c.topk_ids[:, 3] = c.topk_ids[:, 1]     # the same expert twice in a token
     dc = gh.DeviceCase(c)
+    ref = _ref(orc, c)
     for bm in (1, 16):
-        _log(f"naive out-of-range ids block_m={bm}")
-        _check(orc, c, dc, bm, f"out-of-range/B{bm}")
+        for v in _variants(s, bm):
+            _log(f"naive out-of-range ids block_m={bm} {v}")
+            _check(orc, c, dc, bm, f"out-of-range/B{bm}", v, ref)
 
 
 def test_naive_no_valid_pair_and_empty_batch():
@@ -123,8 +140,9 @@ def test_naive_no_valid_pair_and_empty_batch():
     c = synth.draw(s)
     dc = gh.DeviceCase(c)
     for bm in (1, 16):
-        y = dc.naive(block_m=bm)
-        assert torch.equal(y.view(torch.int16), dc.y_in.view(torch.int16))
+        for v in _variants(s, bm):
+            y = dc.naive(block_m=bm, variant=v)
+            assert torch.equal(y.view(torch.int16), dc.y_in.view(torch.int16))
     d0 = gh.DeviceCase(synth.draw(synth.shape("tiny", M=0)))
     mla.fused_moe_lora_naive(d0.x, d0.a, d0.b, d0.topk_ids, d0.mapping, d0.w, d0.y_in,
                              mul_routed_weight=True, add_inputs=True)
@@ -148,7 +166,7 @@ def test_naive_metamorphic(name):
     # on the stream kernel a row's arithmetic does not depend on the other
     # rows of its block, so the block size changes nothing; the register-batch
     # kernel folds lane partials in an order set by its 2- or 4-row groups
-    y1, y16 = dc.naive(block_m=1), dc.naive(block_m=16)
+    y1, y16 = dc.naive(block_m=1, variant="valu"), dc.naive(block_m=16, variant="valu")
     kernel = mla.fused_kernel_name(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r, s.block_m,
                                    s.x_per_pair, "valu")
     if kernel == "fused_stream_kernel":
