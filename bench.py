@@ -17,6 +17,9 @@ Timing:
     the X rows it reads, the Y rows it reads and writes, routed weights and
     block metadata).
   * cpu_baseline: the CPU oracle (plain C, fp64) on the same inputs.
+  * align_free (batches of at most 1024 pairs): fused_moe_lora_naive on the
+    same inputs -- the decode path with no align launch -- at the workload's
+    block_m and at block_m = 1.  ``--path naive`` times it as the step instead.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
