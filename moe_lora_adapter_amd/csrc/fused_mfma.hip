@@ -13,10 +13,13 @@
 //           XOR-permuted by the row index, so the MFMA operand reads of 16
 //           rows spread over the LDS banks.  Loads past the end of a buffer
 //           return zero, which pads invalid rows, ranks >= r and the K tail.
-//   v       rounded to bf16 into LDS; it never leaves the chip.
-//   expand  every wavefront holds V of all rows of the pass as MFMA operands
-//           and takes a share of the output columns.  The product is formed
-//           transposed, D^T = B[cols] . V^T, so that a lane ends with four
+//   v       goes to LDS as two bf16 parts, V = V_hi + V_lo (V_hi = bf16(V),
+//           V_lo = bf16(V - V_hi)); it never leaves the chip.
+//   expand  every wavefront holds both parts of V for all rows of the pass as
+//           MFMA operands and takes a share of the output columns.  The
+//           product is formed transposed, D^T = B[cols] . (V_hi + V_lo)^T (two
+//           MFMAs per k-step, so v enters with about 16 significant bits
+//           rather than bf16's 8), so that a lane ends with four
 //           consecutive output columns of one row: the routed weight, the
 //           add onto Y and the bf16 rounding happen in registers and Y is
 //           read and written 8 bytes per lane.  B and Y of the next column
@@ -250,6 +253,7 @@ template <int MT, int KS, int CTW>
 __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx& c, int nb,
                                              const int64_t (&yrow)[MT], const bool (&rv)[MT],
                                              const float (&wt)[MT], const uint4 (&va)[MT][KS],
+                                             const uint4 (&vl)[MT][KS],
                                              const ExpandRegs<MT, KS, CTW>& r) {
   const int w = wave_id(), lane = lane_id();
   const int lq = lane >> 4;
@@ -260,7 +264,10 @@ __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx
     for (int m = 0; m < MT; ++m) {
       f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dt = mfma16(r.b[i][ks], va[m][ks], dt);
+      for (int ks = 0; ks < KS; ++ks) {
+        dt = mfma16(r.b[i][ks], va[m][ks], dt);
+        dt = mfma16(r.b[i][ks], vl[m][ks], dt);
+      }
       float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = dt[e] * wt[m];
@@ -321,8 +328,10 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
       }
     }
   }
-  // V -> bf16 rows of slot 0, zero from RP up to RK
+  // V -> bf16 rows: the high parts in slot 0, the low parts in slot 2 (slot 1
+  // may still be read for partials), both zero from RP up to RK
   uint16_t* s_v = reinterpret_cast<uint16_t*>(c.ring);
+  uint16_t* s_vl = reinterpret_cast<uint16_t*>(c.ring + 2 * SS::BYTES);
   if (owner) {
     const int mt = w % MT, wr = (w / MT) % S::WR;
 #pragma unroll
@@ -330,13 +339,21 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
       const int rt = wr + i * S::WR;
       if (rt < RT) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_v[(16 * mt + 4 * lq + e) * VP + 16 * rt + lr] = f32_to_bf16(acc[i][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int at = (16 * mt + 4 * lq + e) * VP + 16 * rt + lr;
+          const uint16_t hi = f32_to_bf16(acc[i][e]);
+          s_v[at] = hi;
+          s_vl[at] = f32_to_bf16(acc[i][e] - bf16_to_f32(hi));
+        }
       }
     }
   }
   if constexpr (SS::RK > S::RP) {
-    for (int i = tid; i < S::RB * (SS::RK - S::RP); i += kThreadsM)
-      s_v[(i / (SS::RK - S::RP)) * VP + S::RP + i % (SS::RK - S::RP)] = 0;
+    for (int i = tid; i < S::RB * (SS::RK - S::RP); i += kThreadsM) {
+      const int at = (i / (SS::RK - S::RP)) * VP + S::RP + i % (SS::RK - S::RP);
+      s_v[at] = 0;
+      s_vl[at] = 0;
+    }
   }
   stage_barrier<0>();
 
@@ -347,12 +364,15 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);
   constexpr int NCG = 16 * kWavesM * CTW;
   ExpandRegs<MT, KS, CTW> cur, nxt;
-  uint4 va[MT][KS];
+  uint4 va[MT][KS], vl[MT][KS];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      va[m][ks] = *reinterpret_cast<const uint4*>(s_v + (16 * m + lr) * VP + 32 * ks + 8 * lq);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int at = (16 * m + lr) * VP + 32 * ks + 8 * lq;
+      va[m][ks] = *reinterpret_cast<const uint4*>(s_v + at);
+      vl[m][ks] = *reinterpret_cast<const uint4*>(s_vl + at);
+    }
   // per row tile: this lane's output row as an element offset into y (row 0
   // for an invalid row, which is then neither stored nor used) and its weight
   int64_t yrow[MT];
@@ -368,10 +388,10 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   expand_load<MT, KS, CTW>(p, c, c.n0, yrow, cur);
   for (int nb = c.n0; nb < c.n1; nb += 2 * NCG) {
     if (nb + NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + NCG, yrow, nxt);
-    expand_store<MT, KS, CTW>(p, c, nb, yrow, rv, wt, va, cur);
+    expand_store<MT, KS, CTW>(p, c, nb, yrow, rv, wt, va, vl, cur);
     if (nb + NCG >= c.n1) break;
     if (nb + 2 * NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + 2 * NCG, yrow, cur);
-    expand_store<MT, KS, CTW>(p, c, nb + NCG, yrow, rv, wt, va, nxt);
+    expand_store<MT, KS, CTW>(p, c, nb + NCG, yrow, rv, wt, va, vl, nxt);
   }
   stage_barrier<0>();  // V (slot 0) and the row tables are reused by the next pass
 }
@@ -379,7 +399,7 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
 // NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
 // align-free path) instead of being read from the align outputs.
 template <int RT, bool NAIVE>
-__global__ void __launch_bounds__(kThreadsM) fused_mfma_kernel(FusedParams p) {
+__global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2))) fused_mfma_kernel(FusedParams p) {
   __shared__ __align__(16) uint8_t ring[3 * Slots<RT>::BYTES];
   __shared__ int s_row[kPassRows];
   __shared__ int s_pair[kPassRows];

@@ -17,9 +17,12 @@
 //                    k-step) products, one per wavefront, V^T[16 ranks x 16
 //                    rows] += A[16 x 32] X^T[32 x 16] (rows >= 4 are zero).
 //   after A          the k-step partials of each rank tile are added through
-//                    LDS and v is rounded to bf16 into LDS; never to memory.
+//                    LDS and v goes to LDS as two bf16 parts, v = hi + lo
+//                    (hi = bf16(v), lo = bf16(v - hi)); never to memory.
 //   B stage          NCS consecutive columns of B: D^T[16 cols x 16 rows] =
-//                    B[16 x 32 ranks] V^T, so a lane ends with four
+//                    B[16 x 32 ranks] (V_hi + V_lo)^T, two MFMAs per k-step,
+//                    so v enters the product with about 16 significant bits
+//                    instead of bf16's 8; a lane ends with four
 //                    consecutive columns of one row, which it scales by the
 //                    routed weight, adds to the Y values held in LDS and
 //                    rounds to bf16 there.
@@ -129,7 +132,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ __align__(16) uint8_t ring[kSlots * kStage];
   __shared__ __align__(16) uint8_t xs[kXBytes];
   __shared__ __align__(16) uint8_t ys[kYBytes];
-  __shared__ __align__(16) uint16_t s_vb[kRows * VP];
+  __shared__ __align__(16) uint16_t s_vb[kRows * VP];  // v, bf16 high part
+  __shared__ __align__(16) uint16_t s_vl[kRows * VP];  // v, bf16 low part
   __shared__ int s_pair[kRows];
   __shared__ int s_row[kRows];
   __shared__ float s_w[kRows];
@@ -208,7 +212,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       s_row[tid] = xrow;
       s_w[tid] = wv;
     }
-    for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = 0;
+    for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = s_vl[i] = 0;
     // valid rows are a prefix of the block (sentinels only pad a group's end)
     const int nr = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kRows && s_row[tid] >= 0));
     if (nr == 0) break;
@@ -236,9 +240,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     // wavefront w: A rank tile rt and k-step ka of every A stage
     const int rt = w % G::RT, ka = w / G::RT;
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 vop[G::KS];
+    uint4 vop[G::KS], vlo[G::KS];
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
+    for (int ks = 0; ks < G::KS; ++ks) vop[ks] = vlo[ks] = zero4;
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
     for (int t = 0; t < T; ++t) {
@@ -271,7 +275,11 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
             // lane (lr, lq) holds v[row lr][16 w + 4 lq + i]
             if (lr < kRows) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) s_vb[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i]);
+              for (int i = 0; i < 4; ++i) {
+                const uint16_t hi = f32_to_bf16(acc[i]);
+                s_vb[lr * VP + 16 * w + 4 * lq + i] = hi;
+                s_vl[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i] - bf16_to_f32(hi));
+              }
             }
           }
         }
@@ -280,9 +288,11 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
         const int u = t - nA;
         if (u == 0) {
 #pragma unroll
-          for (int ks = 0; ks < G::KS; ++ks)
-            vop[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vb + lr * VP + 32 * ks + 8 * lq)
-                                 : zero4;
+          for (int ks = 0; ks < G::KS; ++ks) {
+            const int at = lr * VP + 32 * ks + 8 * lq;
+            vop[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vb + at) : zero4;
+            vlo[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vl + at) : zero4;
+          }
         }
         for (int ct = w; ct < G::CT; ct += kST / kWave) {
           const int col = 16 * ct + lr;
@@ -292,6 +302,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
             const int jc = 4 * ks + lq;
             const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
             dt = mfma16(bb, vop[ks], dt);
+            dt = mfma16(bb, vlo[ks], dt);
           }
           // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage
           const int n = u * G::NCS + 16 * ct + 4 * lq;

@@ -155,10 +155,11 @@ def _sample_pairs(c, rng, n=384):
     return np.unique(np.concatenate([pick, ends]))
 
 
+@pytest.mark.parametrize("dist", ["literal", "stress"])
 @pytest.mark.parametrize("name", LARGE)
-def test_fused_full_size_sampled(orc, name):
-    s = synth.shape(name)
-    _log(f"fused full-size {name}: drawing inputs")
+def test_fused_full_size_sampled(orc, name, dist):
+    s = synth.shape(name, dist=dist)
+    _log(f"fused full-size {name} {dist}: drawing inputs")
     c = synth.draw(s)
     dc = gh.DeviceCase(c)
     align = dc.align()
@@ -167,11 +168,11 @@ def test_fused_full_size_sampled(orc, name):
                     c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair, pairs=pairs)
     inval = torch.from_numpy(~gh.valid_pairs(c)).to(gh.DEV)
     for variant in _variants(s):
-        _log(f"fused full-size {name} {variant}")
+        _log(f"fused full-size {name} {dist} {variant}")
         y = dc.fused(align=align, variant=variant)
         yv = y.view(s.numel, s.N)
         got = gh.bf16_host_f64(yv[torch.from_numpy(pairs).to(gh.DEV)])
-        gh.assert_fused_close(got, ref, f"{name}/{variant}")
+        gh.assert_fused_close(got, ref, f"{name}/{dist}/{variant}")
         same = (yv[inval].view(torch.int16) == dc.y_in.view(s.numel, s.N)[inval].view(torch.int16))
         assert bool(same.all()), "rows of unmapped pairs changed"
 
