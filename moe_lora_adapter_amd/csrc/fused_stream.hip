@@ -19,10 +19,14 @@
 //   after A          the k-step partials of each rank tile are added through
 //                    LDS and v goes to LDS as two bf16 parts, v = hi + lo
 //                    (hi = bf16(v), lo = bf16(v - hi)); never to memory.
-//   B stage          NCS consecutive columns of B: D^T[16 cols x 16 rows] =
-//                    B[16 x 32 ranks] (V_hi + V_lo)^T, two MFMAs per k-step,
-//                    so v enters the product with about 16 significant bits
-//                    instead of bf16's 8; a lane ends with four
+//   B stage          NCS consecutive columns of B: D^T[16 cols x 16 cols'] =
+//                    B[16 x 32 ranks] W^T, where the 16 MFMA columns of W
+//                    carry V_hi of the pass rows in columns 0..3 and V_lo of
+//                    the same rows in columns 4..7 (the rest zero).  Adding
+//                    column i + 4 of the result onto column i (one lane
+//                    shuffle) gives B (V_hi + V_lo)^T: v enters with about 16
+//                    significant bits instead of bf16's 8, at no extra MFMA.
+//                    A lane then ends with four
 //                    consecutive columns of one row, which it scales by the
 //                    routed weight, adds to the Y values held in LDS and
 //                    rounds to bf16 there.
@@ -88,6 +92,14 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Lane i of every 16-lane row gets the value of lane i + kRows of the same
+// row (DPP row shift left; lanes past the row's end get 0): a VALU lane move,
+// with no trip through the LDS crossbar.
+__device__ __forceinline__ float lane_plus_rows(float v) {
+  static_assert(kRows >= 1 && kRows <= 15, "DPP row shift distance");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + kRows, 0xf, 0xf, true));
+}
+
 // Stage geometry for rank R (32, 64 or 128).
 template <int R>
 struct Geo {
@@ -138,7 +150,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ int s_row[kRows];
   __shared__ float s_w[kRows];
   __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
+  __shared__ uint2 s_dummy[kWave];            // stores of lanes with no output
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials reuse the X buffer");
+  static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
   // units = (block, slice); split count: a compute unit per working
@@ -240,9 +254,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     // wavefront w: A rank tile rt and k-step ka of every A stage
     const int rt = w % G::RT, ka = w / G::RT;
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 vop[G::KS], vlo[G::KS];
+    uint4 vop[G::KS];
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) vop[ks] = vlo[ks] = zero4;
+    for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
     for (int t = 0; t < T; ++t) {
@@ -287,38 +301,46 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
         // ---- expand: D^T[16 cols x 16 rows] = B[16 cols x 32 ranks] . V^T
         const int u = t - nA;
         if (u == 0) {
+          // operand column lr: V_hi of row lr (lr < kRows), V_lo of row
+          // lr - kRows (kRows <= lr < 2 kRows), else zero
 #pragma unroll
           for (int ks = 0; ks < G::KS; ++ks) {
-            const int at = lr * VP + 32 * ks + 8 * lq;
-            vop[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vb + at) : zero4;
-            vlo[ks] = lr < kRows ? *reinterpret_cast<const uint4*>(s_vl + at) : zero4;
+            const int row = lr < kRows ? lr : (lr < 2 * kRows ? lr - kRows : 0);
+            const uint16_t* src = lr < kRows ? s_vb : s_vl;
+            vop[ks] = lr < 2 * kRows ? *reinterpret_cast<const uint4*>(src + row * VP + 32 * ks + 8 * lq)
+                                     : zero4;
           }
         }
         for (int ct = w; ct < G::CT; ct += kST / kWave) {
           const int col = 16 * ct + lr;
+          // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage.
+          // Its Y values are read before the products so the read's latency
+          // hides behind them (lanes with nothing to write read row 0,
+          // column 0 and drop it).
+          const int n = u * G::NCS + 16 * ct + 4 * lq;
+          const bool live = lr < nr && n < ncols;
+          uint2* yp = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(ys) +
+                                               (live ? lr * ncols + n : 0));
+          const uint2 yv = *yp;
           f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < G::KS; ++ks) {
             const int jc = 4 * ks + lq;
             const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
             dt = mfma16(bb, vop[ks], dt);
-            dt = mfma16(bb, vlo[ks], dt);
           }
-          // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage
-          const int n = u * G::NCS + 16 * ct + 4 * lq;
-          if (lr < nr && n < ncols) {
-            uint2* yp = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(ys) + lr * ncols + n);
-            const uint2 yv = *yp;
-            float o[4] = {dt[0] * wrow, dt[1] * wrow, dt[2] * wrow, dt[3] * wrow};
-            if (p.add) {
-              o[0] += bf16_lo(yv.x);
-              o[1] += bf16_hi(yv.x);
-              o[2] += bf16_lo(yv.y);
-              o[3] += bf16_hi(yv.y);
-            }
-            *yp = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
-                             uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
-          }
+          // lane (lr, lq) adds the V_lo product of its row, held kRows lanes up
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dt[i] += lane_plus_rows(dt[i]);
+          // every lane forms and stores its result -- lanes with nothing to
+          // write into a dummy LDS slot -- so no branch exists that the Y read
+          // and the arithmetic could be sunk into (below the products)
+          const float ya = p.add ? 1.f : 0.f;
+          const float o[4] = {dt[0] * wrow + ya * bf16_lo(yv.x), dt[1] * wrow + ya * bf16_hi(yv.x),
+                              dt[2] * wrow + ya * bf16_lo(yv.y), dt[3] * wrow + ya * bf16_hi(yv.y)};
+          const uint2 out = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
+                                       uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+          *(live ? yp : &s_dummy[lane]) = out;
         }
       }
     }

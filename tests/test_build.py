@@ -1,0 +1,51 @@
+"""Every gfx950 kernel compiles without register spills (no scratch memory).
+
+A kernel that spills reads and writes per-lane scratch in memory on its hot
+loop; the register budgets here are tight (1024-thread workgroups allow 128
+VGPRs, the MFMA kernel is held to two wavefronts per SIMD), so a change that
+adds live values can push one over without any test failing otherwise.
+Cross-compiles on the host; no GPU needed.
+"""
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from moe_lora_adapter_amd import build
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def _resource_usage(src):
+    flags = [f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [HIPCC, *flags, "-I", os.path.join(build.ROOT, "include"), "--cuda-device-only", "-c",
+           src, "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    kernels, cur = {}, None
+    for line in res.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and cur:
+            kernels[cur][m.group(1).split()[0]] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="no hipcc")
+def test_no_kernel_spills_registers():
+    srcs = build.sources()
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        usage = dict(zip(srcs, ex.map(_resource_usage, srcs)))
+    n = 0
+    for src, kernels in usage.items():
+        for name, u in kernels.items():
+            n += 1
+            assert u.get("ScratchSize", 0) == 0, f"{os.path.basename(src)}: {name} spills: {u}"
+    assert n >= 40, f"expected every kernel instantiation, found {n}"

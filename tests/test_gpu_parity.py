@@ -146,6 +146,41 @@ def test_fused_overwrite_delta(orc, name):
         gh.assert_delta_close(got[v], ref[v], np.zeros_like(ref[v]), f"{name}/{variant}")
 
 
+PRECISION = [
+    ("oss20b_decode_w13_a6", {}, "valu"),          # stream kernel
+    ("oss20b_decode_w13_a6", {}, "mfma"),          # MFMA kernel, one row tile
+    ("tiny", dict(M=256, E=2, topk=2, L=1, active=1, p_neg=0.0, r=128, K=512, Ns=256,
+                  block_m=64), "mfma"),            # MFMA kernel, 64-row passes, r = 128
+    ("oss120b_decode_w13", {}, "valu"),            # register-batch kernel (fp32 v)
+]
+
+
+@pytest.mark.parametrize("i", range(len(PRECISION)))
+def test_fused_rank_vector_precision(orc, i):
+    """The rank vector enters the expand with about 16 significant bits: with
+    add_inputs = 0, Y differs from the exact delta by the bf16 rounding of the
+    output (at most 2^-8 relative) and a small absolute term.  A rank vector
+    rounded once to bf16 misses this bound by about 0.01 of the rms delta."""
+    name, kw, variant = PRECISION[i]
+    s = synth.shape(name, dist="stress", add=False, **kw)
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    v = gh.valid_pairs(c)
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)[v]
+    paths = [("sorted", dc.fused(variant=variant))]
+    if s.numel <= 1024:
+        paths.append(("align-free", dc.naive(variant=variant)))
+    for path, y in paths:
+        _log(f"precision {name} {variant} {path}")
+        got = gh.bf16_host_f64(y).reshape(s.numel, s.N)[v]
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))
+        worst = np.argmax(err - bound)
+        assert (err <= bound).all(), (f"{name}/{variant}/{path}: err {err.flat[worst]:.3e} > "
+                                      f"{bound.flat[worst]:.3e} at |ref| {abs(ref.flat[worst]):.3e}")
+
+
 # ------------------------------------------------------------------ fused, full size sampled
 def _sample_pairs(c, rng, n=384):
     s = c.shape
