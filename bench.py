@@ -17,6 +17,10 @@ Timing:
     the X rows it reads, the Y rows it reads and writes, routed weights and
     block metadata).
   * cpu_baseline: the CPU oracle (plain C, fp64) on the same inputs.
+  * two_kernel: fused_moe_lora_two_kernel (shrink and expand with the rank
+    vectors through memory) on the same inputs, graph-timed with the align
+    step and event-timed for its two kernels; one_shot_speedup is the latter
+    over the fused kernel's time.
   * align_free (batches of at most 1024 pairs): fused_moe_lora_naive on the
     same inputs -- the decode path with no align launch -- at the workload's
     block_m and at block_m = 1.  ``--path naive`` times it as the step instead.
@@ -121,6 +125,7 @@ class DeviceSet:
         self.align = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, dev)
         ws = mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.ws2 = None  # two-kernel workspace, allocated when that path is timed
 
 
 def run_align(ds, s):
@@ -145,6 +150,12 @@ def naive_kernel_name(s, block_m, variant):
     """The kernel of the align-free path: the sorted path's choice for
     block_m >= 16, the vector kernels below that."""
     return _kernel_name(s, variant if block_m >= 16 else "valu")
+
+
+def run_two_kernel(ds, s):
+    import moe_lora_adapter_amd as mla
+    mla.fused_moe_lora_two_kernel(ds.x, ds.a, ds.b, ds.align, ds.w, ds.y, mul_routed_weight=s.mul,
+                                  add_inputs=s.add, x_per_pair=s.x_per_pair, workspace=ds.ws2)
 
 
 def step(ds, s, variant):
@@ -281,6 +292,8 @@ def main(argv=None):
                     help="naive: time fused_moe_lora_naive (no align step) as the step")
     ap.add_argument("--naive-block-m", type=int, default=None,
                     help="block_m of the align-free path (default: the workload's)")
+    ap.add_argument("--no-two-kernel", action="store_true",
+                    help="skip the two-kernel comparator line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -394,6 +407,23 @@ def main(argv=None):
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})
+    if args.path == "sorted" and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
+        # the two-kernel path on the same inputs (rank vectors through memory):
+        # the comparator of the one-shot kernels
+        nb = mla.two_kernel_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                            s.block_m, s.x_per_pair)
+        ws2 = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        for ds in sets:
+            ds.ws2 = ws2  # one workspace: its contents are rewritten by every call
+        log("two-kernel path")
+        fn2 = lambda ds: (run_align(ds, s), run_two_kernel(ds, s))  # noqa: E731
+        for i in range(args.warmup):
+            fn2(sets[i % copies])
+        us2 = time_steps_graph(sets, s, variant, args.steps, fn=fn2) * 1e6
+        kus2 = time_kernel_events(sets, s, variant, lambda ds: run_two_kernel(ds, s), args.steps)
+        out["two_kernel"] = {"us_per_call": round(us2, 3), "kernels_us_avg": round(kus2, 3),
+                             "workspace_bytes": nb,
+                             "one_shot_speedup": round(kus2 / fused_avg, 3)}
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -225,6 +225,53 @@ MOE_LORA_API int fused_moe_lora_naive(const uint16_t *x, int32_t x_per_pair,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
                    int32_t block_m, uint16_t *y, int32_t variant, void *stream);
 
+/* Largest rank fused_moe_lora_two_kernel takes. */
+#define MOE_LORA_TWO_KERNEL_MAX_RANK 512
+
+/*
+ * fused_moe_lora_two_kernel_workspace_bytes -- [host, no HIP call] bytes of
+ * device workspace fused_moe_lora_two_kernel needs for these sizes (the
+ * fp32 rank vectors of every pair and slice, once per K split); a negative
+ * status when fused_moe_lora_two_kernel would reject the sizes.
+ */
+MOE_LORA_API int64_t fused_moe_lora_two_kernel_workspace_bytes(int64_t M, int32_t topk,
+                   int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, int32_t x_per_pair);
+
+/*
+ * fused_moe_lora_two_kernel -- the same function as fused_moe_lora, computed
+ * by two kernels with the rank vectors in memory: the path the one-shot
+ * kernel replaces (prhub summary of vLLM PR #42290: motivation, and the
+ * "two-kernel path for larger ranks" of its key source fragment; the shrink
+ * and expand launches of the PR #32005 diff).  Takes ranks up to
+ * MOE_LORA_TWO_KERNEL_MAX_RANK, past fused_moe_lora's 128.
+ *
+ * A shrink kernel writes, for every valid pair p and slice s, the fp32 rank
+ * vector v[j] = sum_t X[row, t] A[s,l,e,j,t] into the workspace (in K splits,
+ * one workspace slice each); an expand kernel adds the splits in a fixed
+ * order and writes Y[p, s*Ns+n] = bf16(add ? Y + w d[n] : w d[n]) with
+ * d[n] = sum_j v[j] B[s,l,e,n,j] (v enters the bf16 products as a bf16
+ * high / low pair).  Two launches on `stream`, in that order.
+ *
+ * Arguments as for fused_moe_lora (the align outputs of the same M, topk, E,
+ * L, block_m), plus:
+ *   workspace   [device] at least fused_moe_lora_two_kernel_workspace_bytes()
+ *               bytes, 16-byte aligned; contents on entry do not matter,
+ *               contents on return are the rank vectors (unspecified rows for
+ *               pairs in no slot).  MOE_LORA_ERR_WORKSPACE when too small.
+ * MOE_LORA_ERR_UNSUPPORTED for r > MOE_LORA_TWO_KERNEL_MAX_RANK or when x, an
+ * A matrix or a B matrix exceeds 2 GiB.  Deterministic (no atomics).
+ */
+MOE_LORA_API int fused_moe_lora_two_kernel(const uint16_t *x, int32_t x_per_pair,
+                   const uint16_t *lora_a, const uint16_t *lora_b,
+                   const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                   const int32_t *num_tokens_post_padded,
+                   const float *topk_weights, int32_t mul_routed_weight,
+                   int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, uint16_t *y, void *workspace,
+                   int64_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,9 +42,15 @@ SIGNATURES = {
     "fused_moe_lora_naive": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                             _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                             _I32, _P]),
+    "fused_moe_lora_two_kernel_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                         _I32, _I32, _I32]),
+    "fused_moe_lora_two_kernel": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                 _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                 _I32, _P, _P, _I64, _P]),
 }
 
-NAIVE_MAX_PAIRS = 1024  # MOE_LORA_NAIVE_MAX_PAIRS
+NAIVE_MAX_PAIRS = 1024        # MOE_LORA_NAIVE_MAX_PAIRS
+TWO_KERNEL_MAX_RANK = 512     # MOE_LORA_TWO_KERNEL_MAX_RANK
 
 
 class MoeLoraError(RuntimeError):
@@ -243,4 +249,38 @@ def fused_moe_lora_naive(x, lora_a, lora_b, topk_ids, token_lora_mapping, topk_w
         VARIANTS[variant] if isinstance(variant, str) else int(variant), _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora_naive")
+    return y
+
+
+def two_kernel_workspace_bytes(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int, r: int,
+                               block_m: int, x_per_pair: bool = False) -> int:
+    v = lib().fused_moe_lora_two_kernel_workspace_bytes(M, topk, K, Ns, S, E, L, r, block_m,
+                                                        int(bool(x_per_pair)))
+    if v < 0:
+        raise MoeLoraError(v, "fused_moe_lora_two_kernel_workspace_bytes")
+    return int(v)
+
+
+def fused_moe_lora_two_kernel(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
+                              mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
+                              workspace=None, stream=None):
+    """fused_moe_lora as shrink + expand with the rank vectors in `workspace` (ranks up to
+    TWO_KERNEL_MAX_RANK); see moe_lora.h."""
+    import torch
+    M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
+    if align.sorted_token_ids.shape[0] != L:
+        raise ValueError("align output was made for another L")
+    nbytes = two_kernel_workspace_bytes(M, topk, K, Ns, S, E, L, r, align.block_m, x_per_pair)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=y.device)
+    _check(workspace, "workspace", workspace.dtype, y.device)
+    rc = lib().fused_moe_lora_two_kernel(
+        _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
+        _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
+        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
+        align.block_m, _dptr(y), _dptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "fused_moe_lora_two_kernel")
     return y

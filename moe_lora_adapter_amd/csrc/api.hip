@@ -288,6 +288,106 @@ int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* 
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of the two-kernel call; fills the launch plan (kz, kchunk, units,
+// workspace bytes).  Returns a status.
+struct TwoPlan {
+  int64_t numel, cap, N, units, ws_bytes;
+  int kz, kchunk;
+};
+
+int plan_two_kernel(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                    int32_t L, int32_t r, int32_t block_m, int32_t x_per_pair, TwoPlan* t) {
+  const int rc = check_sizes(M, topk, E, L, block_m, &t->numel, &t->cap);
+  if (rc != MOE_LORA_OK) return rc;
+  if (K < 8 || Ns < 8 || S < 1 || r < 1 || (K & 7) || (Ns & 7)) return MOE_LORA_ERR_INVALID;
+  if (x_per_pair != 0 && x_per_pair != 1) return MOE_LORA_ERR_INVALID;
+  if (r > kMaxRankTwoKernel) return MOE_LORA_ERR_UNSUPPORTED;
+  t->N = int64_t(S) * Ns;
+  if (t->N > kInt32Max || t->numel * t->N / t->N != t->numel) return MOE_LORA_ERR_UNSUPPORTED;
+  const int64_t x_bytes = (x_per_pair ? t->numel : M) * K * 2;
+  if (!two_kernel_fits(x_bytes, r, K, Ns)) return MOE_LORA_ERR_UNSUPPORTED;
+  t->units = max_total_blocks(t->numel, int64_t(L) * E, block_m) * S;
+  t->kz = two_kernel_splits(t->units, K, r);
+  const int64_t per = (K + t->kz - 1) / t->kz;
+  t->kchunk = int((per + 31) / 32 * 32);
+  const int64_t groups = (r + kTwoKernelRankGroup - 1) / kTwoKernelRankGroup;
+  if (t->units * groups * t->kz * 64 > kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;
+  t->ws_bytes = int64_t(t->kz) * S * t->numel * r * 4;
+  return MOE_LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fused_moe_lora_two_kernel_workspace_bytes(int64_t M, int32_t topk, int32_t K, int32_t Ns,
+                                                  int32_t S, int32_t E, int32_t L, int32_t r,
+                                                  int32_t block_m, int32_t x_per_pair) {
+  TwoPlan t;
+  const int rc = plan_two_kernel(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, &t);
+  return rc != MOE_LORA_OK ? rc : t.ws_bytes;
+}
+
+int fused_moe_lora_two_kernel(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                              const uint16_t* lora_b, const int32_t* sorted_token_ids,
+                              const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                              const float* topk_weights, int32_t mul_routed_weight,
+                              int32_t add_inputs, int64_t M, int32_t topk, int32_t K, int32_t Ns,
+                              int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
+                              uint16_t* y, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  TwoPlan t;
+  const int rc = plan_two_kernel(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, &t);
+  if (rc != MOE_LORA_OK) return rc;
+  if ((mul_routed_weight != 0 && mul_routed_weight != 1) || (add_inputs != 0 && add_inputs != 1) ||
+      workspace_bytes < 0)
+    return MOE_LORA_ERR_INVALID;
+  if (t.numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
+  if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded || !y || (mul_routed_weight && !topk_weights))
+    return MOE_LORA_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y))
+    return MOE_LORA_ERR_INVALID;
+  if (!workspace || workspace_bytes < t.ws_bytes || !aligned16(workspace))
+    return MOE_LORA_ERR_WORKSPACE;
+
+  FusedParams p{};
+  p.x = x;
+  p.a = lora_a;
+  p.b = lora_b;
+  p.sorted = sorted_token_ids;
+  p.eids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.w = topk_weights;
+  p.y = y;
+  p.x_per_pair = x_per_pair;
+  p.mul = mul_routed_weight;
+  p.add = add_inputs;
+  p.numel = int32_t(t.numel);
+  p.topk = topk;
+  p.K = K;
+  p.Ns = Ns;
+  p.S = S;
+  p.E = E;
+  p.L = L;
+  p.r = r;
+  p.B = block_m;
+  p.N = int32_t(t.N);
+  p.cap = int32_t(t.cap);
+  p.nb = int32_t(t.cap / block_m);
+  p.units = int32_t(t.units);
+  p.xcd_cus = xcd_compute_units();
+  p.ws = static_cast<float*>(workspace);
+  p.kz = t.kz;
+  p.kchunk = t.kchunk;
+  const hipError_t err = launch_two_kernel(p, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
 int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                            int32_t L, int32_t r, int32_t block_m, int32_t x_per_pair,
                            int32_t variant) {

@@ -56,7 +56,14 @@ struct FusedParams {
   int32_t xcd_cus;     // compute units per XCD of the current device
   int32_t naive;       // 1: blocks formed on chip from topk_ids and mapping (no align outputs)
   int32_t nbits;       // align-free path: bits of a key l * E + e
+  float* ws;           // two-kernel path: partial rank vectors, fp32 [kz, S, numel, r]
+  int32_t kz;          // two-kernel path: K splits of the shrink
+  int32_t kchunk;      // two-kernel path: K per split (a multiple of 32)
 };
+
+// Largest rank of the two-kernel path, and the ranks of one shrink workgroup.
+constexpr int kMaxRankTwoKernel = 512;
+constexpr int kTwoKernelRankGroup = 128;
 
 // Most pairs the align-free path groups (one per thread of a workgroup).
 constexpr int64_t kNaiveMaxPairs = 1024;
@@ -78,6 +85,11 @@ bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int
 // Whether the vector variant runs the stream kernel for these sizes.
 bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);
 bool mfma_supported(int r, int B);
+// Two-kernel path: K splits of the shrink for these sizes, and the launch of
+// shrink then expand (p.ws, p.kz, p.kchunk set by the caller).
+int two_kernel_splits(int64_t units_bound, int64_t K, int r);
+hipError_t launch_two_kernel(FusedParams p, hipStream_t st);
+bool two_kernel_fits(int64_t x_bytes, int64_t r, int64_t K, int64_t Ns);
 bool mfma_fits(int64_t x_bytes, int64_t y_bytes, int64_t r, int64_t K, int64_t Ns);
 
 }  // namespace mlr

@@ -216,6 +216,59 @@ def test_naive_binding_checks_before_calling():
                                  mul_routed_weight=False, add_inputs=True)
 
 
+def two_call(**kw):
+    a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
+             add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=256, B=16, y=P16,
+             ws=P16, ws_bytes=1 << 40)
+    a.update(kw)
+    return mla.lib().fused_moe_lora_two_kernel(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"],
+                                               a["eids"], a["ntpp"], a["w"], a["mul"], a["add"],
+                                               a["M"], a["topk"], a["K"], a["Ns"], a["S"],
+                                               a["E"], a["L"], a["r"], a["B"], a["y"], a["ws"],
+                                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.ERR_INVALID),
+    (dict(la=None), mla.ERR_INVALID),
+    (dict(lb=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(y=None), mla.ERR_INVALID),
+    (dict(mul=1, w=None), mla.ERR_INVALID),
+    (dict(add=2), mla.ERR_INVALID),
+    (dict(xpp=5), mla.ERR_INVALID),
+    (dict(K=2884), mla.ERR_INVALID),
+    (dict(r=0), mla.ERR_INVALID),
+    (dict(S=0), mla.ERR_INVALID),
+    (dict(ws_bytes=-1), mla.ERR_INVALID),
+    (dict(r=513), mla.ERR_UNSUPPORTED),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(B=8), mla.ERR_UNSUPPORTED),
+    # an A matrix above 2 GiB: r * K * 2 = 2^31 + 2^13
+    (dict(r=512, K=2 ** 21 + 8, Ns=64), mla.ERR_UNSUPPORTED),
+    (dict(ws=None), mla.ERR_WORKSPACE),
+    (dict(ws_bytes=1024), mla.ERR_WORKSPACE),
+    (dict(ws=V(24)), mla.ERR_WORKSPACE),
+    (dict(x=V(24)), mla.ERR_INVALID),
+    (dict(M=0), mla.OK),
+    (dict(M=0, x=None, y=None, sorted=None, ws=None), mla.OK),
+])
+def test_two_kernel_rejects(kw, status):
+    assert two_call(**kw) == status
+
+
+def test_two_kernel_workspace_query():
+    q = mla.two_kernel_workspace_bytes
+    # fp32 rank vectors of every pair and slice, once per K split
+    b = q(16, 4, 2880, 2880, 2, 32, 6, 256, 16)
+    assert b > 0 and b % (2 * 64 * 256 * 4) == 0 and b // (2 * 64 * 256 * 4) <= 8
+    # a large batch needs no K split
+    assert q(8192, 8, 2048, 768, 2, 128, 8, 128, 64) == 2 * 65536 * 128 * 4
+    assert q(0, 4, 2880, 2880, 2, 32, 6, 64, 16) == 0
+    with pytest.raises(mla.MoeLoraError):
+        q(16, 4, 2880, 2880, 2, 32, 6, 513, 16)
+
+
 def test_variant_query_resolves_auto():
     fv = mla.fused_variant
     # decode: about two rows per (slot, expert) group -> vector kernel
