@@ -63,8 +63,12 @@ constexpr int kYBytes = kRows * kMaxCols * 2;
 constexpr int kMaxIds = 128;                // largest block_m
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
+// Ring depth: slots - 1 stages in flight per workgroup.  Three slots (32 KiB
+// in flight) measured fastest on MI355X: with 228 streaming workgroups,
+// deeper rings only add contention (20b-like decode a6: 3 slots 27.0 us,
+// 4 slots 27.3, 5 slots 28.4, 6 slots 29.3).
 #ifndef MLR_STREAM_SLOTS
-#define MLR_STREAM_SLOTS 4
+#define MLR_STREAM_SLOTS 3
 #endif
 constexpr int kSlots = MLR_STREAM_SLOTS;
 static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
@@ -260,8 +264,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
     for (int t = 0; t < T; ++t) {
-      if (t == 0) stage_barrier<0>();  // X, Y and the first stages
-      else wait_stage<kSlots - 2>(min(kSlots - 2, T - 1 - t));
+      // stage t (and, at t = 0, the X rows and Y values issued before it):
+      // the later stages stay in flight, so the ring never drains to empty
+      wait_stage<kSlots - 2>(min(kSlots - 2, T - 1 - t));
       if (t + kSlots - 1 < T)
         issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ncols,
                        ring_lds + ((t + kSlots - 1) % kSlots) * kStage);

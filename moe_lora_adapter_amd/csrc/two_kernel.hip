@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(kT2) lora_shrink_kernel(FusedParams p) {
 
 // RP: ranks padded to a multiple of 32 that the LDS copy of V is sized for.
 template <int RP>
-__global__ void __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(RP <= 256 ? 2 : 1)))
 lora_expand_kernel(FusedParams p) {
   constexpr int VP = RP + 8;  // bf16 pitch of the V rows
   __shared__ __align__(16) uint16_t s_vh[kPass2 * VP];
