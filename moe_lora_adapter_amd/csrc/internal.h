@@ -26,6 +26,7 @@ struct AlignParams {
 };
 
 struct AlignPlan {
+  bool wave;         // one wavefront does everything (at most 64 pairs and 64 slots)
   bool single;       // one workgroup does everything
   int W, seg, ntiles;
   int threads;       // block size of the single / tile kernels

@@ -97,6 +97,22 @@ def test_align_max_experts_and_many_slots(orc):
         gh.assert_align_equal(gpu, ref, B)
 
 
+@pytest.mark.parametrize("M,topk,E,L,B", [
+    (64, 1, 7, 3, 16), (16, 4, 32, 6, 16), (21, 3, 5, 64, 32), (63, 1, 2, 1, 128),
+    (8, 8, 1024, 8, 64), (1, 1, 1, 1, 16), (0, 4, 32, 6, 16),
+    # just past the one-wavefront path: 65 pairs, 65 slots
+    (65, 1, 7, 3, 16), (16, 4, 32, 65, 16)])
+def test_align_one_wavefront_boundaries(orc, M, topk, E, L, B):
+    rng = np.random.default_rng(M * 131 + L)
+    topk_ids = rng.integers(-1, E + 1, size=(M, topk)).astype(np.int32)
+    topk_ids[::3] = rng.integers(0, max(1, E // 4), size=topk_ids[::3].shape)  # repeated keys
+    mapping = rng.integers(-2, L + 1, size=M).astype(np.int32)
+    _log(f"align boundary M={M} topk={topk} E={E} L={L} B={B}")
+    ref = orc.align(topk_ids, mapping, E, L, B)
+    gpu = gh.align_to_host(gh.run_align(topk_ids, mapping, E, L, B))
+    gh.assert_align_equal(gpu, ref, B)
+
+
 def test_align_deterministic():
     s = synth.shape("align_stress")
     c = synth.draw(s, with_tensors=False)
