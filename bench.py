@@ -216,7 +216,9 @@ def cpu_baseline(case, budget_s):
     import oracle
     o = oracle.load()
     s = case.shape
-    valid = np.nonzero((np.repeat(case.token_lora_mapping, s.topk) >= 0))[0]
+    slot = np.repeat(case.token_lora_mapping, s.topk)
+    ex = case.topk_ids.reshape(-1)
+    valid = np.nonzero((slot >= 0) & (slot < s.L) & (ex >= 0) & (ex < s.E))[0]
     t0 = time.perf_counter()
     o.align(case.topk_ids, case.token_lora_mapping, s.E, s.L, s.block_m)
     t_align = time.perf_counter() - t0

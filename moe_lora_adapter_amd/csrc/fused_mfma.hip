@@ -55,6 +55,9 @@ constexpr int kPassRows = 64;
 constexpr int kMaxIdsM = 128;  // largest block_m
 constexpr int64_t kMaxXBytes = int64_t(1) << 31;
 
+#ifndef MLR_MFMA_CTW_BUDGET  // expand: column tiles per wavefront and group x row tiles x k-steps
+#define MLR_MFMA_CTW_BUDGET 8
+#endif
 #ifndef MLR_MFMA_MIN_COLS
 #define MLR_MFMA_MIN_COLS 256
 #endif
@@ -360,7 +363,7 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   // ---------------- expand
   // wavefront w: all MT row tiles, column tiles w + kWavesM i (i < CTW) of
   // each group of 16 kWavesM CTW columns
-  constexpr int CTW0 = 8 / (MT * KS);
+  constexpr int CTW0 = MLR_MFMA_CTW_BUDGET / (MT * KS);
   constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);
   constexpr int NCG = 16 * kWavesM * CTW;
   ExpandRegs<MT, KS, CTW> cur, nxt;

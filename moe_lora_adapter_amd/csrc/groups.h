@@ -17,7 +17,7 @@
 // forms the groups, their block counts and the block numbering in registers,
 // with no LDS table and no barrier but the one that publishes the block's
 // pair ids.  Beyond that, a workgroup of T threads takes the pairs in
-// 1024 / T rounds of T (pair = round * T + thread, so the 16 wavefront-sized
+// 1024 / T steps of T (pair = step * T + thread, so the 16 wavefront-sized
 // pieces of the pair range are numbered in pair order), and the wavefront
 // leaders (lowest lane of each key in a piece) meet in a small LDS hash
 // table, where the first pair and the size of each group collect by atomic
@@ -46,8 +46,8 @@ struct GroupLds {
   int sel[2];             // the workgroup's block: group key, block within the group
 };
 
-// What a thread keeps about its pairs between the two phases (round c holds
-// pair c * T + thread; with at most 64 pairs only round 0, pair = lane).
+// What a thread keeps about its pairs between the two phases (step c holds
+// pair c * T + thread; with at most 64 pairs only step 0, pair = lane).
 template <int T>
 struct PairGroup {
   static constexpr int R = kGroupPairs / T;

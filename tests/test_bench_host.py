@@ -1,0 +1,71 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic work the roofline is
+computed from, the one-GPU rule, the traffic records, the CPU baseline leg."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bench
+from moe_lora_adapter_amd import synth
+
+
+def _brute_work(c):
+    """The algorithmic bytes and flops, pair by pair (an independent count)."""
+    s = c.shape
+    groups, xrows, P, padded = set(), set(), 0, {}
+    for p in range(s.numel):
+        m, k = divmod(p, s.topk)
+        l, e = int(c.token_lora_mapping[m]), int(c.topk_ids[m, k])
+        if not (0 <= l < s.L and 0 <= e < s.E):
+            continue
+        P += 1
+        groups.add((l, e))
+        xrows.add(p if s.x_per_pair else m)
+        padded[(l, e)] = padded.get((l, e), 0) + 1
+    pad = sum(-(-n // s.block_m) * s.block_m for n in padded.values())
+    w = len(groups) * s.S * (s.r * s.K + s.Ns * s.r) * 2
+    x = len(xrows) * s.K * 2
+    y = P * s.S * s.Ns * 2 * (2 if s.add else 1)
+    meta = pad * 4 + pad // s.block_m * 4 + (P * 4 if s.mul else 0)
+    return dict(valid_pairs=P, active_groups=len(groups), fused_bytes=w + x + y + meta,
+                weight_bytes=w, fused_flops=2.0 * P * s.S * s.r * (s.K + s.Ns),
+                naive_bytes=w + x + y + s.numel * 4 + s.M * 4 + (P * 4 if s.mul else 0))
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("oss20b_decode_w13_a3", {}),
+                                     ("oss120b_decode_w2", {}),
+                                     ("tiny", dict(add=False, x_per_pair=True, M=40, topk=3))])
+def test_algorithmic_work_matches_a_pair_by_pair_count(name, kw):
+    c = synth.draw(synth.shape(name, **kw), with_tensors=False)
+    got, ref = bench.algorithmic_work(c), _brute_work(c)
+    for k, v in ref.items():
+        assert got[k] == v, k
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_traffic_record_goes_stale_with_the_kernel_sources(tmp_path, monkeypatch):
+    for kernel in bench.KERNEL_SOURCES:
+        for f in bench.KERNEL_SOURCES[kernel] + bench.SHARED_SOURCES:
+            assert os.path.exists(os.path.join(bench.ROOT, "moe_lora_adapter_amd", "csrc", f)), f
+    rec = {"fused_stream_kernel/w": {"src_sha": bench.kernel_sources_sha("fused_stream_kernel"),
+                                     "traffic_bytes_per_launch": 123},
+           "fused_mfma_kernel/w": {"src_sha": "0" * 16, "traffic_bytes_per_launch": 456}}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.load_traffic("fused_stream_kernel", "w")[0] == 123
+    assert bench.load_traffic("fused_mfma_kernel", "w")[0] is None      # sources changed since
+    assert bench.load_traffic("fused_valu_kernel", "w")[0] is None      # never recorded
+
+
+def test_cpu_baseline_leg_reports_the_oracle():
+    c = synth.draw(synth.shape("tiny"))
+    out = bench.cpu_baseline(c, 0.2)
+    assert out["kind"] == "oracle" and out["unit"] == "us/call"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert out["value"] == pytest.approx(out["align_us"] + out["fused_us"], abs=0.2)
