@@ -51,7 +51,7 @@ def _full_adapters(s, rng):
     return to16(a), to16(b)
 
 
-@pytest.mark.parametrize("path", ["sorted", "naive"])
+@pytest.mark.parametrize("path", ["sorted", "naive", "two_kernel"])
 @pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "oss120b_decode_w2"])
 def test_one_graph_all_active_counts(name, path):
     s = synth.shape(name, dist="stress")
@@ -64,9 +64,17 @@ def test_one_graph_all_active_counts(name, path):
     al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
     ws = torch.empty(max(16, mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)),
                      dtype=torch.uint8, device=gh.DEV)
+    ws2 = torch.empty(max(16, mla.two_kernel_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E,
+                                                             s.L, s.r, s.block_m, s.x_per_pair)),
+                      dtype=torch.uint8, device=gh.DEV)
 
     def call():
-        if path == "sorted":
+        if path == "two_kernel":
+            mla.moe_lora_align(dc.topk_ids, mapping, s.E, s.L, s.block_m, out=al, workspace=ws)
+            mla.fused_moe_lora_two_kernel(dc.x, dc.a, dc.b, al, dc.w, y, mul_routed_weight=s.mul,
+                                          add_inputs=s.add, x_per_pair=s.x_per_pair,
+                                          workspace=ws2)
+        elif path == "sorted":
             mla.moe_lora_align(dc.topk_ids, mapping, s.E, s.L, s.block_m, out=al, workspace=ws)
             mla.fused_moe_lora(dc.x, dc.a, dc.b, al, dc.w, y, mul_routed_weight=s.mul,
                                add_inputs=s.add, x_per_pair=s.x_per_pair)
