@@ -21,6 +21,10 @@ Timing:
     vectors through memory) on the same inputs, graph-timed with the align
     step and event-timed for its two kernels; one_shot_speedup is the latter
     over the fused kernel's time.
+  * dual_stream (batches of at most 1024 pairs): the LoRA side (align, fused
+    with add_inputs = 0 into a zero buffer, moe_lora_accumulate to join) on an
+    auxiliary stream beside a stand-in base GEMM that streams the same base
+    expert weights a decode step reads; each alone, serial and overlapped.
   * align_free (batches of at most 1024 pairs): fused_moe_lora_naive on the
     same inputs -- the decode path with no align launch -- at the workload's
     block_m and at block_m = 1.  ``--path naive`` times it as the step instead.
@@ -212,6 +216,90 @@ def time_kernel_events(sets, s, variant, which, launches):
     return e0.elapsed_time(e1) * 1e3 / launches
 
 
+def dual_stream_line(sets, s, case, steps, dev):
+    """The dual-stream path against a stand-in base GEMM (graph-timed per step).
+
+    The base MoE w13 GEMM of a decode batch streams the base weights of every
+    expert the batch routes to; the stand-in is one bf16 GEMM of the batch's X
+    rows with a [K, N x distinct experts] matrix, the same bytes.  The LoRA side
+    is align + fused_moe_lora (add_inputs = 0 into a zero-filled buffer); the
+    join is moe_lora_accumulate.  Reported: each alone, both serial on one
+    stream, and the LoRA side on an auxiliary stream beside the base."""
+    import torch
+    import moe_lora_adapter_amd as mla
+    slot = np.repeat(case.token_lora_mapping, s.topk)
+    ex = case.topk_ids.reshape(-1)
+    valid = (slot >= 0) & (slot < s.L) & (ex >= 0) & (ex < s.E)
+    n_exp = max(1, len(np.unique(ex[valid])))
+    x_rows = sets[0].x.shape[0]
+    w = torch.empty((s.K, s.N * n_exp), dtype=torch.bfloat16, device=dev).normal_()
+    xb = sets[0].x[: max(1, x_rows)].contiguous()
+    base_out = torch.empty((xb.shape[0], s.N * n_exp), dtype=torch.bfloat16, device=dev)
+    deltas = [torch.zeros_like(ds.y) for ds in sets]
+    aux = torch.cuda.Stream()
+    evs = [torch.cuda.Event() for _ in range(steps)]
+
+    def base(i):
+        torch.matmul(xb, w, out=base_out)
+
+    def lora(i, stream=None):
+        ds, d = sets[i % len(sets)], deltas[i % len(sets)]
+        d.zero_()
+        mla.moe_lora_align(ds.topk_ids, ds.mapping, s.E, s.L, s.block_m, out=ds.align,
+                           workspace=ds.ws)
+        mla.fused_moe_lora(ds.x, ds.a, ds.b, ds.align, ds.w, d, mul_routed_weight=s.mul,
+                           add_inputs=False, x_per_pair=s.x_per_pair)
+
+    def join(i):
+        ds, d = sets[i % len(sets)], deltas[i % len(sets)]
+        mla.moe_lora_accumulate(ds.y, d)
+
+    def serial(i):
+        base(i)
+        lora(i)
+        join(i)
+
+    def dual(i):
+        main = torch.cuda.current_stream()
+        aux.wait_stream(main)
+        with torch.cuda.stream(aux):
+            lora(i)
+            evs[i].record(aux)
+        base(i)
+        main.wait_event(evs[i])
+        join(i)
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    log("dual-stream line")
+    res = {"base_stand_in": f"bf16 GEMM [{xb.shape[0]} x {s.K}] x [{s.K} x {s.N * n_exp}] "
+                            f"({n_exp} distinct experts' base weights, "
+                            f"{w.numel() * 2 / 1e9:.2f} GB)",
+           "base_us": round(timed(base), 3),
+           "lora_us": round(timed(lambda i: (lora(i), join(i))), 3),
+           "serial_us": round(timed(serial), 3),
+           "dual_stream_us": round(timed(dual), 3)}
+    res["overlap_saving_us"] = round(res["serial_us"] - res["dual_stream_us"], 3)
+    del w, base_out
+    return res
+
+
 def cpu_baseline(case, budget_s):
     import oracle
     o = oracle.load()
@@ -296,6 +384,8 @@ def main(argv=None):
                     help="block_m of the align-free path (default: the workload's)")
     ap.add_argument("--no-two-kernel", action="store_true",
                     help="skip the two-kernel comparator line")
+    ap.add_argument("--no-dual-stream", action="store_true",
+                    help="skip the dual-stream overlap line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -426,6 +516,8 @@ def main(argv=None):
         out["two_kernel"] = {"us_per_call": round(us2, 3), "kernels_us_avg": round(kus2, 3),
                              "workspace_bytes": nb,
                              "one_shot_speedup": round(kus2 / fused_avg, 3)}
+    if args.path == "sorted" and naive_ok and not args.no_dual_stream:
+        out["dual_stream"] = dual_stream_line(sets, s, case, args.steps, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

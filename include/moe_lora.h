@@ -272,6 +272,21 @@ MOE_LORA_API int fused_moe_lora_two_kernel(const uint16_t *x, int32_t x_per_pair
                    int32_t block_m, uint16_t *y, void *workspace,
                    int64_t workspace_bytes, void *stream);
 
+/*
+ * moe_lora_accumulate -- y[i] = bf16(y[i] + delta[i]) for i < n, the sum in
+ * fp32, rounded to nearest even once: the join of the dual-stream path (prhub
+ * summary of vLLM PR #42290, implementation step 2 and the TritonExperts
+ * fragment: the base MoE GEMM on the default stream, fused_moe_lora with
+ * add_inputs = 0 into a zero-filled delta buffer on an auxiliary stream, the
+ * delta added onto the base output once both streams have met).  The caller
+ * orders the streams (an event recorded on the auxiliary stream and waited
+ * for on `stream`).
+ * [device] y, delta: bf16 [n], 16-byte aligned, not overlapping.  n == 0
+ * does nothing; MOE_LORA_ERR_INVALID for n < 0, null or misaligned pointers.
+ */
+MOE_LORA_API int moe_lora_accumulate(uint16_t *y, const uint16_t *delta, int64_t n,
+                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

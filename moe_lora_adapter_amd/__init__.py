@@ -47,6 +47,7 @@ SIGNATURES = {
     "fused_moe_lora_two_kernel": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32,
                                                  _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                  _I32, _P, _P, _I64, _P]),
+    "moe_lora_accumulate": (ctypes.c_int, [_P, _P, _I64, _P]),
 }
 
 NAIVE_MAX_PAIRS = 1024        # MOE_LORA_NAIVE_MAX_PAIRS
@@ -283,4 +284,18 @@ def fused_moe_lora_two_kernel(x, lora_a, lora_b, align: AlignOutput, topk_weight
         _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora_two_kernel")
+    return y
+
+
+def moe_lora_accumulate(y, delta, stream=None):
+    """y += delta (bf16, elementwise, one rounding): the join of the dual-stream path; see
+    moe_lora.h.  Ordering the two streams is the caller's."""
+    import torch
+    _check(y, "y", torch.bfloat16, y.device)
+    _check(delta, "delta", torch.bfloat16, y.device)
+    if y.numel() != delta.numel():
+        raise ValueError("y and delta must have the same number of elements")
+    rc = lib().moe_lora_accumulate(_dptr(y), _dptr(delta), y.numel(), _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "moe_lora_accumulate")
     return y

@@ -1,0 +1,56 @@
+// Y += delta, elementwise in bf16: the join step of the dual-stream path.
+//
+// The prhub summary of vLLM PR #42290 (implementation step 2 and the
+// TritonExperts fragment) runs the base MoE GEMM on the default stream and
+// the LoRA kernel on an auxiliary stream, the LoRA writing its delta with
+// add_inputs = False into a zero-filled buffer; after both streams meet, the
+// delta is added onto the base output.  This kernel is that addition:
+// y[i] = bf16(y[i] + delta[i]), the sum formed in fp32 and rounded to nearest
+// even once.  16-byte vector accesses, a grid-stride loop over the chunks and
+// an element loop for a tail shorter than eight values.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mlr {
+namespace {
+
+constexpr int kTA = 256;
+
+__global__ void __launch_bounds__(kTA) accumulate_kernel(uint16_t* __restrict__ y,
+                                                         const uint16_t* __restrict__ d, int64_t n) {
+  const int64_t chunks = n / 8;
+  const int64_t stride = int64_t(gridDim.x) * kTA;
+  for (int64_t c = int64_t(blockIdx.x) * kTA + threadIdx.x; c < chunks; c += stride) {
+    const uint4 yv = reinterpret_cast<const uint4*>(y)[c];
+    const uint4 dv = reinterpret_cast<const uint4*>(d)[c];
+    const uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w}, ds[4] = {dv.x, dv.y, dv.z, dv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_lo(ys[i]) + bf16_lo(ds[i]);
+      const float hi = bf16_hi(ys[i]) + bf16_hi(ds[i]);
+      o[i] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    }
+    reinterpret_cast<uint4*>(y)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += kTA)
+      y[i] = f32_to_bf16(bf16_to_f32(y[i]) + bf16_to_f32(d[i]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accumulate(uint16_t* y, const uint16_t* d, int64_t n, hipStream_t st) {
+  const int64_t chunks = n / 8;
+  // enough workgroups to fill the chip a few times over, no more than needed
+  const int64_t want = (chunks + kTA - 1) / kTA;
+  const int64_t cap = int64_t(xcd_compute_units()) * kXcds * 4;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(want, std::max<int64_t>(cap, 1)));
+  hipLaunchKernelGGL(accumulate_kernel, dim3(unsigned(grid)), dim3(kTA), 0, st, y, d, n);
+  return hipGetLastError();
+}
+
+}  // namespace mlr

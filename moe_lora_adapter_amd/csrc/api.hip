@@ -388,6 +388,14 @@ int fused_moe_lora_two_kernel(const uint16_t* x, int32_t x_per_pair, const uint1
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 
+int moe_lora_accumulate(uint16_t* y, const uint16_t* delta, int64_t n, void* stream) {
+  if (n < 0) return MOE_LORA_ERR_INVALID;
+  if (n == 0) return MOE_LORA_OK;
+  if (!y || !delta || !aligned16(y) || !aligned16(delta)) return MOE_LORA_ERR_INVALID;
+  const hipError_t err = launch_accumulate(y, delta, n, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
 int fused_moe_lora_variant(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                            int32_t L, int32_t r, int32_t block_m, int32_t x_per_pair,
                            int32_t variant) {

@@ -91,6 +91,9 @@ bool mfma_supported(int r, int B);
 int two_kernel_splits(int64_t units_bound, int64_t K, int r);
 hipError_t launch_two_kernel(FusedParams p, hipStream_t st);
 bool two_kernel_fits(int64_t x_bytes, int64_t r, int64_t K, int64_t Ns);
+
+// ---------------------------------------------------------------- join step
+hipError_t launch_accumulate(uint16_t* y, const uint16_t* d, int64_t n, hipStream_t st);
 bool mfma_fits(int64_t x_bytes, int64_t y_bytes, int64_t r, int64_t K, int64_t Ns);
 
 }  // namespace mlr

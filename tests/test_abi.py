@@ -269,6 +269,20 @@ def test_two_kernel_workspace_query():
         q(16, 4, 2880, 2880, 2, 32, 6, 513, 16)
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, P16, 8), mla.ERR_INVALID),
+    ((P16, None, 8), mla.ERR_INVALID),
+    ((P16, P16, -1), mla.ERR_INVALID),
+    ((V(24), P16, 8), mla.ERR_INVALID),
+    ((P16, V(40), 8), mla.ERR_INVALID),
+    ((P16, P16, 0), mla.OK),
+    ((None, None, 0), mla.OK),
+])
+def test_accumulate_rejects(args, status):
+    y, d, n = args
+    assert mla.lib().moe_lora_accumulate(y, d, n, None) == status
+
+
 def test_variant_query_resolves_auto():
     fv = mla.fused_variant
     # decode: about two rows per (slot, expert) group -> vector kernel
