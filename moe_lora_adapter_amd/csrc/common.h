@@ -112,6 +112,12 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return make_uint4(uint32_t(v.x), uint32_t(v.y), uint32_t(v.z), uint32_t(v.w));
 }
 
+// Stores past the range are dropped.
+__device__ __forceinline__ void buf_st16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const i32x4_t d = {int(v.x), int(v.y), int(v.z), int(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, int(voff), int(soff), 0);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // acc + a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2 on gfx950).

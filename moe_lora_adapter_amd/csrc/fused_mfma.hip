@@ -117,6 +117,7 @@ struct Slots {
 struct PassCtx {
   i32x4_t xr, ar;               // DMA sources: x, A[s,l,e]
   __amdgpu_buffer_rsrc_t br;    // B[s,l,e]
+  __amdgpu_buffer_rsrc_t yr;    // y
   uint8_t* ring;                // three slots of Slots<RT>::BYTES
   uint32_t ring_lds;            // LDS byte address of ring
   const int* s_row;    // X row per pass row, -1 = none
@@ -213,23 +214,70 @@ __device__ __forceinline__ void shrink_step(const FusedParams& p, const PassCtx&
   shrink_compute<MT, RT>(c.ring + cur * SB, acc);
 }
 
-// B chunks and Y values of one column group of the expand.
-template <int MT, int KS, int CTW>
+// Expand geometry of a pass with MT row tiles and KS k-steps: column groups
+// of NCG columns; wavefront w multiplies column tiles w + kWavesM i (i < CTW)
+// of a group for all MT row tiles.  The scaled delta of a group crosses LDS
+// once (fp32, DP floats per row, two buffers) so that Y is read and written
+// in 16-byte chunks of 8 columns laid along the rows: thread t takes chunks
+// t + kThreadsM i (i < YC) of the group, CPRW to a row, and a wavefront
+// instruction covers 64 / CPRW whole rows of NCG columns.  Y pieces of 8 bytes
+// per lane, 16 rows to an instruction (the MFMA result layout), ran at about
+// 60% of the rate of this layout on MI355X.
+template <int MT, int KS>
+struct Expand {
+  static constexpr int CTW0 = MLR_MFMA_CTW_BUDGET / (MT * KS);
+  static constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);  // column tiles per wavefront
+  static constexpr int NCG = 16 * kWavesM * CTW;                     // columns per group
+  static constexpr int RB = 16 * MT;                                 // rows
+  static constexpr int CPRW = NCG / 8;                               // 16-byte chunks per row
+  static constexpr int YC = RB * CPRW / kThreadsM;                   // chunks per thread
+  static constexpr int DP = NCG + 4;                                 // fp32 pitch of a delta row
+  static constexpr int DBYTES = RB * DP * 4;                         // one delta buffer
+  static_assert(YC >= 1 && YC * kThreadsM == RB * CPRW, "whole chunks per thread");
+};
+// the two delta buffers of the largest group (64 rows x 128 or 32 x 256 columns)
+constexpr int kDeltaBytes = 2 * 64 * (128 + 4) * 4;
+
+// 16-byte chunk j of a delta row is stored at chunk j ^ bit 3 of j: the two
+// chunks a thread reads for its 8 columns then fall in different bank groups
+// from those of its neighbours.
+__device__ __forceinline__ int dswz(int j) { return j ^ ((j >> 3) & 1); }
+
+// B chunks (MFMA layout) and Y chunks (row layout) of one column group.
+template <int MT, int KS>
 struct ExpandRegs {
-  uint4 b[CTW][KS];
-  uint2 y[CTW][MT];
+  uint4 b[Expand<MT, KS>::CTW][KS];
+  uint4 y[Expand<MT, KS>::YC];
 };
 
-// Loads of column group nb: every load is issued (out-of-range B chunks read
-// as zero through the buffer resource, Y of an invalid row or column reads
-// row 0 and is not used), so no load sits behind a per-lane branch.
-template <int MT, int KS, int CTW>
+// Row-layout chunks of this thread: Y element offset of the chunk's row
+// (slice column 0), -1 for a row without a pair (y stays below 2 GiB, so
+// offsets fit 32 bits); column of the chunk in a group.
+template <int MT, int KS>
+struct YChunks {
+  int row[Expand<MT, KS>::YC];
+  int col[Expand<MT, KS>::YC];
+};
+
+// Byte offset of a Y chunk in the buffer resource; past its range (reads
+// zero, stores dropped) for a row without a pair or a column past the split.
+template <int MT, int KS>
+__device__ __forceinline__ uint32_t ychunk_off(const PassCtx& c, const YChunks<MT, KS>& yc, int i, int nb) {
+  const int n = nb + yc.col[i];
+  return (yc.row[i] >= 0 && n < c.n1) ? uint32_t(yc.row[i] + n) * 2u : kOob;
+}
+
+// Loads of column group nb: every load is issued (out-of-range B and Y
+// chunks read as zero through the buffer resources), so no load sits behind a
+// per-lane branch.
+template <int MT, int KS>
 __device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx& c, int nb,
-                                            const int64_t (&yrow)[MT], ExpandRegs<MT, KS, CTW>& r) {
+                                            const YChunks<MT, KS>& yc, ExpandRegs<MT, KS>& r) {
+  using X = Expand<MT, KS>;
   const int w = wave_id(), lane = lane_id();
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < CTW; ++i) {
+  for (int i = 0; i < X::CTW; ++i) {
     const int n = nb + 16 * (w + kWavesM * i) + lr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -240,29 +288,23 @@ __device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx&
   }
   if (p.add) {
 #pragma unroll
-    for (int i = 0; i < CTW; ++i) {
-      const int n = nb + 16 * (w + kWavesM * i) + 4 * lq;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int64_t at = n < c.n1 ? yrow[m] + n : 0;
-        r.y[i][m] = *reinterpret_cast<const uint2*>(p.y + at);
-      }
-    }
+    for (int i = 0; i < X::YC; ++i) r.y[i] = buf_ld16(c.yr, ychunk_off(c, yc, i, nb), 0);
   }
 }
 
-// MFMAs and the epilogue of column group nb.
-template <int MT, int KS, int CTW>
-__device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx& c, int nb,
-                                             const int64_t (&yrow)[MT], const bool (&rv)[MT],
-                                             const float (&wt)[MT], const uint4 (&va)[MT][KS],
-                                             const uint4 (&vl)[MT][KS],
-                                             const ExpandRegs<MT, KS, CTW>& r) {
+// MFMAs of column group nb; the delta, scaled by the routed weight, goes to
+// LDS buffer dl.  The MFMA result D^T[16 columns x 16 rows] leaves each lane
+// four consecutive columns of one row: one 16-byte LDS write.
+template <int MT, int KS>
+__device__ __forceinline__ void expand_mfma(const float (&wt)[MT], const uint4 (&va)[MT][KS],
+                                            const uint4 (&vl)[MT][KS], const ExpandRegs<MT, KS>& r,
+                                            float* dl) {
+  using X = Expand<MT, KS>;
   const int w = wave_id(), lane = lane_id();
-  const int lq = lane >> 4;
+  const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < CTW; ++i) {
-    const int n = nb + 16 * (w + kWavesM * i) + 4 * lq;
+  for (int i = 0; i < X::CTW; ++i) {
+    const int j = 4 * (w + kWavesM * i) + lq;  // 16-byte chunk of the delta row
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -271,21 +313,38 @@ __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx
         dt = mfma16(r.b[i][ks], va[m][ks], dt);
         dt = mfma16(r.b[i][ks], vl[m][ks], dt);
       }
-      float o[4];
+      const float4 o = make_float4(dt[0] * wt[m], dt[1] * wt[m], dt[2] * wt[m], dt[3] * wt[m]);
+      *reinterpret_cast<float4*>(dl + (16 * m + lr) * X::DP + 4 * dswz(j)) = o;
+    }
+  }
+}
+
+// Epilogue of column group nb in the row layout: Y (+)= delta, one rounding.
+template <int MT, int KS>
+__device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx& c, int nb,
+                                             const YChunks<MT, KS>& yc, const ExpandRegs<MT, KS>& r,
+                                             const float* dl) {
+  using X = Expand<MT, KS>;
+  const int t = threadIdx.x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = dt[e] * wt[m];
-      if (p.add) {
-        o[0] += bf16_lo(r.y[i][m].x);
-        o[1] += bf16_hi(r.y[i][m].x);
-        o[2] += bf16_lo(r.y[i][m].y);
-        o[3] += bf16_hi(r.y[i][m].y);
-      }
-      if (rv[m] && n < c.n1) {
-        const uint2 out = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
-                                     uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
-        *reinterpret_cast<uint2*>(p.y + yrow[m] + n) = out;
+  for (int i = 0; i < X::YC; ++i) {
+    const int q = t + kThreadsM * i, row = q / X::CPRW, cj = q % X::CPRW;
+    const float4 d0 = *reinterpret_cast<const float4*>(dl + row * X::DP + 4 * dswz(2 * cj));
+    const float4 d1 = *reinterpret_cast<const float4*>(dl + row * X::DP + 4 * dswz(2 * cj + 1));
+    float o[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    if (p.add) {
+      const uint32_t yw[4] = {r.y[i].x, r.y[i].y, r.y[i].z, r.y[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] += bf16_lo(yw[e]);
+        o[2 * e + 1] += bf16_hi(yw[e]);
       }
     }
+    uint32_t ow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ow[e] = uint32_t(f32_to_bf16(o[2 * e])) | (uint32_t(f32_to_bf16(o[2 * e + 1])) << 16);
+    buf_st16(make_uint4(ow[0], ow[1], ow[2], ow[3]), c.yr, ychunk_off(c, yc, i, nb), 0);
   }
 }
 
@@ -361,12 +420,9 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   stage_barrier<0>();
 
   // ---------------- expand
-  // wavefront w: all MT row tiles, column tiles w + kWavesM i (i < CTW) of
-  // each group of 16 kWavesM CTW columns
-  constexpr int CTW0 = MLR_MFMA_CTW_BUDGET / (MT * KS);
-  constexpr int CTW = CTW0 < 1 ? 1 : (CTW0 > 4 ? 4 : CTW0);
-  constexpr int NCG = 16 * kWavesM * CTW;
-  ExpandRegs<MT, KS, CTW> cur, nxt;
+  using X = Expand<MT, KS>;
+  static_assert(2 * X::DBYTES <= kDeltaBytes, "delta buffers");
+  ExpandRegs<MT, KS> cur, nxt;
   uint4 va[MT][KS], vl[MT][KS];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -376,25 +432,34 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
       va[m][ks] = *reinterpret_cast<const uint4*>(s_v + at);
       vl[m][ks] = *reinterpret_cast<const uint4*>(s_vl + at);
     }
-  // per row tile: this lane's output row as an element offset into y (row 0
-  // for an invalid row, which is then neither stored nor used) and its weight
-  int64_t yrow[MT];
-  bool rv[MT];
+  // routed weight of this lane's row in each row tile (MFMA layout)
   float wt[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int pid = c.s_pair[16 * m + lr];
-    rv[m] = pid < p.numel;
-    yrow[m] = rv[m] ? int64_t(pid) * p.N + int64_t(c.s) * p.Ns : 0;
-    wt[m] = c.s_wt[16 * m + lr];
+  for (int m = 0; m < MT; ++m) wt[m] = c.s_wt[16 * m + lr];
+  // row layout: the Y row of each of this thread's chunks
+  YChunks<MT, KS> yc;
+#pragma unroll
+  for (int i = 0; i < X::YC; ++i) {
+    const int q = tid + kThreadsM * i, row = q / X::CPRW;
+    const int pid = c.s_pair[row];
+    yc.row[i] = pid < p.numel ? pid * p.N + c.s * p.Ns : -1;
+    yc.col[i] = 8 * (q % X::CPRW);
   }
-  expand_load<MT, KS, CTW>(p, c, c.n0, yrow, cur);
-  for (int nb = c.n0; nb < c.n1; nb += 2 * NCG) {
-    if (nb + NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + NCG, yrow, nxt);
-    expand_store<MT, KS, CTW>(p, c, nb, yrow, rv, wt, va, vl, cur);
-    if (nb + NCG >= c.n1) break;
-    if (nb + 2 * NCG < c.n1) expand_load<MT, KS, CTW>(p, c, nb + 2 * NCG, yrow, cur);
-    expand_store<MT, KS, CTW>(p, c, nb + NCG, yrow, rv, wt, va, vl, nxt);
+  expand_load<MT, KS>(p, c, c.n0, yc, cur);
+  // the delta buffers take the ring's place: every wavefront holds V in registers
+  stage_barrier<63>();
+  float* dl0 = reinterpret_cast<float*>(c.ring);
+  float* dl1 = reinterpret_cast<float*>(c.ring + X::DBYTES);
+  for (int nb = c.n0; nb < c.n1; nb += 2 * X::NCG) {
+    if (nb + X::NCG < c.n1) expand_load<MT, KS>(p, c, nb + X::NCG, yc, nxt);
+    expand_mfma<MT, KS>(wt, va, vl, cur, dl0);
+    stage_barrier<63>();  // the group's delta is in LDS; loads stay in flight
+    expand_store<MT, KS>(p, c, nb, yc, cur, dl0);
+    if (nb + X::NCG >= c.n1) break;
+    if (nb + 2 * X::NCG < c.n1) expand_load<MT, KS>(p, c, nb + 2 * X::NCG, yc, cur);
+    expand_mfma<MT, KS>(wt, va, vl, nxt, dl1);
+    stage_barrier<63>();
+    expand_store<MT, KS>(p, c, nb + X::NCG, yc, nxt, dl1);
   }
   stage_barrier<0>();  // V (slot 0) and the row tables are reused by the next pass
 }
@@ -403,7 +468,7 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
 // align-free path) instead of being read from the align outputs.
 template <int RT, bool NAIVE>
 __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(2))) fused_mfma_kernel(FusedParams p) {
-  __shared__ __align__(16) uint8_t ring[3 * Slots<RT>::BYTES];
+  __shared__ __align__(16) uint8_t ring[3 * Slots<RT>::BYTES > kDeltaBytes ? 3 * Slots<RT>::BYTES : kDeltaBytes];
   __shared__ int s_row[kPassRows];
   __shared__ int s_pair[kPassRows];
   __shared__ float s_wt[kPassRows];
@@ -448,6 +513,7 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   c.xr = dma_rsrc(p.x, uint32_t(x_rows * p.K * 2));
   c.ar = dma_rsrc(p.a + wsel * p.r * p.K, uint32_t(p.r * p.K * 2));
   c.br = make_rsrc(p.b + wsel * p.Ns * p.r, uint32_t(p.Ns * p.r * 2));
+  c.yr = make_rsrc(p.y, uint32_t(int64_t(p.numel) * p.N * 2));
   c.ring = ring;
   c.ring_lds = lds_address(ring);
   c.s_row = s_row;
