@@ -143,6 +143,14 @@ def run_fused(ds, s, variant):
                        add_inputs=s.add, x_per_pair=s.x_per_pair, variant=variant)
 
 
+def run_fused_ws(ds, s, variant, workspace):
+    """fused_moe_lora_ws: the decode stream kernel with its K split."""
+    import moe_lora_adapter_amd as mla
+    mla.fused_moe_lora_ws(ds.x, ds.a, ds.b, ds.align, ds.w, ds.y, mul_routed_weight=s.mul,
+                          add_inputs=s.add, workspace=workspace, x_per_pair=s.x_per_pair,
+                          variant=variant)
+
+
 def run_naive(ds, s, block_m, variant):
     import moe_lora_adapter_amd as mla
     mla.fused_moe_lora_naive(ds.x, ds.a, ds.b, ds.topk_ids, ds.mapping, ds.w, ds.y,
@@ -386,6 +394,8 @@ def main(argv=None):
                     help="skip the two-kernel comparator line")
     ap.add_argument("--no-dual-stream", action="store_true",
                     help="skip the dual-stream overlap line")
+    ap.add_argument("--no-k-split", action="store_true",
+                    help="skip the K-split (fused_moe_lora_ws) line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -499,6 +509,27 @@ def main(argv=None):
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})
+    if args.path == "sorted" and not args.no_k_split:
+        # the same step with fused_moe_lora_ws: the decode stream kernel's
+        # workgroups of a block split the shrink's K range and exchange
+        # partial rank vectors (only when that kernel runs)
+        nbx = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                                 s.block_m, s.x_per_pair, variant)
+        if nbx > 0:
+            # one zero-filled workspace: the calls run one after another
+            xws = torch.zeros(nbx, dtype=torch.uint8, device=dev)
+            log("K-split path")
+            fnk = lambda ds: (run_align(ds, s), run_fused_ws(ds, s, variant, xws))  # noqa: E731
+            for i in range(args.warmup):
+                fnk(sets[i % copies])
+            usk = time_steps_graph(sets, s, variant, args.steps, fn=fnk) * 1e6
+            kusk = time_kernel_events(sets, s, variant,
+                                      lambda ds: run_fused_ws(ds, s, variant, xws), args.steps)
+            gk = work["fused_bytes"] / (kusk * 1e-6) / 1e9
+            out["k_split"] = {"us_per_call": round(usk, 3), "kernel": kname,
+                              "kernel_us_avg": round(kusk, 3), "achieved_GBps": round(gk, 1),
+                              "frac": round(gk / HBM_PEAK_GBPS, 4), "workspace_bytes": nbx,
+                              "speedup_vs_plain_kernel": round(fused_avg / kusk, 3)}
     if args.path == "sorted" and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
         # the two-kernel path on the same inputs (rank vectors through memory):
         # the comparator of the one-shot kernels

@@ -160,6 +160,56 @@ MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
                    int32_t block_m, uint16_t *y, int32_t variant, void *stream);
 
 /*
+ * fused_moe_lora_ws -- fused_moe_lora with a workspace: the same arguments,
+ * the same function and the same result bit for bit, whatever the timing.
+ * With the workspace the decode stream kernel (VALU variant, r in {32, 64,
+ * 128}) splits the shrink's K range among the workgroups that share a
+ * (block, slice) -- one per column range of the expand -- instead of having
+ * each of them multiply all of A: each multiplies an equal share of the K
+ * stages, publishes its fp32 partial rank vectors in the workspace, and all
+ * of them add the partials in the same order, so the rank vector still
+ * never reaches memory in bf16 and is identical in every workgroup.  (The
+ * split-K shrink of the pages' two-kernel path -- prhub summary of vLLM PR
+ * #42290, implementation steps -- applied inside the one-shot kernel.)
+ *   workspace    [device] fused_moe_lora_workspace_bytes() bytes, 16-byte
+ *                aligned and ZERO-FILLED before its first use.  Every call
+ *                leaves its flag words zero again (in stream order; the
+ *                partial vectors stay behind as scratch), so it is reused as
+ *                it is, also inside a captured graph.  Two calls that may run
+ *                at the same time must not share one.  May be NULL when the
+ *                size is 0 (then this is fused_moe_lora).
+ *   peer_wait    polls (about 0.7 us each) for another workgroup's partial
+ *                before this workgroup computes that partial itself, from A
+ *                in memory and with the same bits; no workgroup waits on
+ *                another beyond that, so the call completes even when the
+ *                workgroups of a unit are not resident together.  Negative:
+ *                the default (64).  0: every workgroup computes every partial.
+ * MOE_LORA_ERR_WORKSPACE when a workspace is needed and is NULL, misaligned
+ * or smaller than the size; other statuses as fused_moe_lora.
+ */
+MOE_LORA_API int fused_moe_lora_ws(const uint16_t *x, int32_t x_per_pair,
+                   const uint16_t *lora_a, const uint16_t *lora_b,
+                   const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                   const int32_t *num_tokens_post_padded,
+                   const float *topk_weights, int32_t mul_routed_weight,
+                   int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, uint16_t *y, int32_t variant,
+                   void *workspace, int64_t workspace_bytes, int32_t peer_wait,
+                   void *stream);
+
+/*
+ * fused_moe_lora_workspace_bytes -- [host, no HIP call] bytes of the
+ * workspace fused_moe_lora_ws uses for these sizes: 0 when its kernel has no
+ * use for one, else the exchange area of the K split (an upper bound over
+ * the blocks these sizes can produce).  Negative status for sizes
+ * fused_moe_lora would reject.
+ */
+MOE_LORA_API int64_t fused_moe_lora_workspace_bytes(int64_t M, int32_t topk, int32_t K,
+                   int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                   int32_t block_m, int32_t x_per_pair, int32_t variant);
+
+/*
  * fused_moe_lora_variant -- [host, no HIP call] the kernel that
  * fused_moe_lora runs for these sizes and `variant`: MOE_LORA_VARIANT_VALU
  * or MOE_LORA_VARIANT_MFMA, AUTO resolved the way fused_moe_lora resolves

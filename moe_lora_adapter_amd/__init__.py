@@ -35,6 +35,11 @@ SIGNATURES = {
     "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
+    "fused_moe_lora_ws": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                         _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                         _I32, _P, _I64, _I32, _P]),
+    "fused_moe_lora_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, _I32]),
     "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _I32]),
     "fused_moe_lora_kernel_name": (ctypes.c_char_p, [_I64, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -230,6 +235,49 @@ def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
         align.block_m, _dptr(y), v, _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora")
+    return y
+
+
+def fused_moe_lora_workspace_bytes(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int,
+                                   r: int, block_m: int, x_per_pair: bool = False,
+                                   variant: str | int = "auto") -> int:
+    """Bytes of the workspace fused_moe_lora_ws uses for these sizes (0: none)."""
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    n = lib().fused_moe_lora_workspace_bytes(M, topk, K, Ns, S, E, L, r, block_m,
+                                             int(bool(x_per_pair)), v)
+    if n < 0:
+        raise MoeLoraError(int(n), "fused_moe_lora_workspace_bytes")
+    return int(n)
+
+
+def alloc_fused_workspace(M: int, topk: int, K: int, Ns: int, S: int, E: int, L: int, r: int,
+                          block_m: int, device, x_per_pair: bool = False,
+                          variant: str | int = "auto"):
+    """A zero-filled workspace for fused_moe_lora_ws (at least 16 bytes)."""
+    import torch
+    n = fused_moe_lora_workspace_bytes(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant)
+    return torch.zeros(max(16, n), dtype=torch.uint8, device=device)
+
+
+def fused_moe_lora_ws(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
+                      mul_routed_weight: bool, add_inputs: bool, workspace,
+                      x_per_pair: bool = False, variant: str | int = "auto",
+                      peer_wait: int = -1, stream=None):
+    """fused_moe_lora with a K-split workspace (zero-filled before first use); see moe_lora.h."""
+    M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
+    if align.sorted_token_ids.shape[0] != L:
+        raise ValueError("align output was made for another L")
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().fused_moe_lora_ws(
+        _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
+        _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
+        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
+        align.block_m, _dptr(y), v, _dptr(workspace), nbytes, int(peer_wait),
+        _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "fused_moe_lora_ws")
     return y
 
 

@@ -166,13 +166,27 @@ int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, i
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
 }
 
-int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
-                   const uint16_t* lora_b, const int32_t* sorted_token_ids,
-                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                   const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
-                   int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
-                   int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
-                   void* stream) {
+// The K-split exchange area the sorted-path call needs (0: its kernel has no
+// use for one), or a negative status for sizes the call would reject.
+static int64_t fused_exchange_bytes(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S,
+                                    int32_t E, int32_t L, int32_t r, int32_t block_m,
+                                    int32_t x_per_pair, int32_t variant) {
+  const int v = fused_moe_lora_variant(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
+  if (v < 0) return v;
+  const int64_t numel = M * topk, N = int64_t(S) * Ns;
+  if (v == MOE_LORA_VARIANT_MFMA || numel == 0 || !valu_takes_stream(M, numel, K, N, r, x_per_pair))
+    return 0;
+  const int64_t units = max_total_blocks(numel, int64_t(L) * E, block_m) * S;
+  return stream_exchange_bytes(units, block_m, r);
+}
+
+static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                        const uint16_t* lora_b, const int32_t* sorted_token_ids,
+                        const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                        const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                        int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                        int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
+                        int32_t* xch, int32_t peer_wait, void* stream) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
   if (rc != MOE_LORA_OK) return rc;
@@ -221,12 +235,51 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
   p.nb = int32_t(cap / block_m);
   p.units = int32_t(units);
   p.xcd_cus = xcd_compute_units();
+  p.xch = xch;
+  p.xch_passes = stream_exchange_passes(block_m);
+  p.peer_wait = peer_wait < 0 ? kDefaultPeerWait : peer_wait;
 
   const bool use_mfma =
       pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                   const uint16_t* lora_b, const int32_t* sorted_token_ids,
+                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                   const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                   int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                   int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
+                   void* stream) {
+  return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
+                      K, Ns, S, E, L, r, block_m, y, variant, nullptr, 0, stream);
+}
+
+int64_t fused_moe_lora_workspace_bytes(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S,
+                                       int32_t E, int32_t L, int32_t r, int32_t block_m,
+                                       int32_t x_per_pair, int32_t variant) {
+  return fused_exchange_bytes(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
+}
+
+int fused_moe_lora_ws(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                      const uint16_t* lora_b, const int32_t* sorted_token_ids,
+                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                      const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                      int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
+                      int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
+                      void* workspace, int64_t workspace_bytes, int32_t peer_wait, void* stream) {
+  const int64_t need = fused_exchange_bytes(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
+  if (need < 0) return int(need);
+  if (workspace_bytes < 0) return MOE_LORA_ERR_INVALID;
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return MOE_LORA_ERR_WORKSPACE;
+  return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
+                      K, Ns, S, E, L, r, block_m, y, variant,
+                      need > 0 ? static_cast<int32_t*>(workspace) : nullptr, peer_wait, stream);
 }
 
 int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,

@@ -61,6 +61,7 @@ constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
 constexpr int kMaxCols = 2048;              // output columns per workgroup
 constexpr int kYBytes = kRows * kMaxCols * 2;
 constexpr int kMaxIds = 128;                // largest block_m
+constexpr int kMaxPeers = 8;                // most workgroups one K split spans
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
 // Ring depth: slots - 1 stages in flight per workgroup.  Three slots (32 KiB
@@ -85,6 +86,18 @@ __device__ __forceinline__ void wait_stage(int later) {
   } else {
     if (later == L) stage_barrier<L * kIPS>();
     else wait_stage<L - 1>(later);
+  }
+}
+
+// Wait until at most n (1 <= n <= N) vector memory operations of this
+// wavefront are outstanding, then meet the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_counts(int n) {
+  if constexpr (N <= 0) {
+    stage_barrier<0>();
+  } else {
+    if (n == N) stage_barrier<N>();
+    else wait_counts<N - 1>(n);
   }
 }
 
@@ -120,16 +133,17 @@ struct Geo {
   static_assert(CPRK >= 8, "A chunk permutation needs 8 chunks per row");
 };
 
-// Loads of ring stage t (A stages first, then B stages) into slot `lds`.
+// Loads of ring stage t into slot `lds`: the workgroup's nA stages of A
+// (K stages ka0, ka0 + 1, ...), then its B stages.
 template <int R>
 __device__ __forceinline__ void issue_stage(const FusedParams& p, i32x4_t ar, i32x4_t br, int t,
-                                            int nA, int ncols, uint32_t lds) {
+                                            int nA, int ka0, int ncols, uint32_t lds) {
   using G = Geo<R>;
   const int q = threadIdx.x;  // one 16-byte chunk per thread and stage
   const uint32_t dst = lds + wave_id() * kWave * 16;
   if (t < nA) {
     const int j = q / G::CPRK, cs = q % G::CPRK;
-    const int kk = t * G::KT + 8 * (cs ^ (j & 7));
+    const int kk = (ka0 + t) * G::KT + 8 * (cs ^ (j & 7));
     dma16(ar, dst, kk < p.K ? uint32_t(j * p.K + kk) * 2u : kOob);
   } else {
     const int col = q / G::CPR, js = q % G::CPR;
@@ -137,6 +151,202 @@ __device__ __forceinline__ void issue_stage(const FusedParams& p, i32x4_t ar, i3
     const int jc = js ^ (col & (G::SW - 1));
     dma16(br, dst, n < ncols ? uint32_t(n * R + 8 * jc) * 2u : kOob);
   }
+}
+
+// Adds the k-step partials of each rank tile through LDS: afterwards the
+// wavefronts w < RT hold, lane (lr, lq), v[row lr][16 w + 4 lq + i] in acc[i]
+// (summed over the A stages this workgroup multiplied).
+template <int R>
+__device__ __forceinline__ void reduce_ksteps(f32x4_t& acc, float* s_part) {
+  using G = Geo<R>;
+  const int w = wave_id(), lane = lane_id();
+  stage_barrier<63>();  // earlier readers of s_part are done
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_part[(w * 4 + i) * kWave + lane] = acc[i];
+  stage_barrier<63>();
+  if (w < G::RT) {
+#pragma unroll
+    for (int k = 1; k < G::KSA; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += s_part[((w + k * G::RT) * 4 + i) * kWave + lane];
+  }
+}
+
+// The MFMAs of A stages [k0, k1) with A read from memory instead of the ring:
+// the same operands in the same order as the ring path, so the partial is
+// the same bit for bit.  Used for a peer whose partial did not arrive.
+template <int R>
+__device__ __forceinline__ f32x4_t a_partial_direct(const FusedParams& p, __amdgpu_buffer_rsrc_t a_rsrc,
+                                                    const uint8_t* xs, int k0, int k1) {
+  using G = Geo<R>;
+  const int w = wave_id(), lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+  const int j = 16 * (w % G::RT) + lr, c = 4 * (w / G::RT) + lq;
+  const int K8 = p.K / 8;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = k0; t < k1; ++t) {
+    const int kk = t * G::KT + 8 * c;
+    const uint4 a = buf_ld16(a_rsrc, kk < p.K ? uint32_t(j * p.K + kk) * 2u : kOob, 0);
+    const int xc = t * (G::KT / 8) + c;
+    const uint4 x = (lr < kRows && xc < K8) ? reinterpret_cast<const uint4*>(xs)[lr * K8 + xc] : zero4;
+    acc = mfma16(a, x, acc);
+  }
+  return acc;
+}
+
+// Exchange area of the K split, for `slots` (unit, pass) slots: generation
+// words [slots] (uint32), departures [slots] (int32), then from a 16-byte
+// boundary the partials, [slots][kMaxPeers][kRows][r] 64-bit words, each an
+// fp32 value in the low half and its call's tag in the high half.  Zero-filled
+// before first use; after that every call leaves it usable as it is.
+__host__ __device__ inline int64_t xch_part_words(int64_t slots) { return (2 * slots + 3) / 4 * 4; }
+
+// The K split of one pass.  The peers -- the C workgroups of a unit, one per
+// column split -- each multiply an equal share of the A stages, publish their
+// partial, and form v = P_0 + P_1 + ... + P_{C-1} in peer order, so all
+// peers hold the same v.  A peer's partial values carry the tag of this call
+// in the slot (the slot's generation + 1; the last peer to leave the slot
+// advances the generation), so a waiting peer polls the values themselves:
+// stale values of an earlier call never carry the current tag, and no flag
+// or completion wait is needed between the data and its announcement.  A
+// partial not complete after `peer_wait` polls is computed here from A in
+// memory (the same bits), so no wait depends on another workgroup being
+// resident.
+//
+// Every access to the exchange area is a device-scope relaxed atomic: a load
+// or store that is coherent across the XCDs' L2 caches by itself.  Device-
+// scope release / acquire fences would order plain accesses instead, but each
+// writes back or invalidates a whole L2: measured on MI355X, 20 to 30 us per
+// exchange instead of about 3.  (Reading the peers' shared L2 first, past
+// this compute unit's L1, measured no faster and sometimes missed the peer's
+// values until the device-scope reads.)
+struct XchSlot {
+  uint32_t* gen;
+  int* depart;
+  uint64_t* parts;  // [kMaxPeers][kRows][R]
+};
+
+template <int R>
+__device__ __forceinline__ XchSlot xch_slot(const FusedParams& p, int slot) {
+  const int64_t slots = int64_t(p.units) * p.xch_passes;
+  XchSlot x;
+  x.gen = reinterpret_cast<uint32_t*>(p.xch) + slot;
+  x.depart = p.xch + slots + slot;
+  x.parts = reinterpret_cast<uint64_t*>(p.xch + xch_part_words(slots)) + int64_t(slot) * kMaxPeers * kRows * R;
+  return x;
+}
+
+template <int R>
+__device__ __forceinline__ void publish_partial(const XchSlot& x, const f32x4_t& acc, int split,
+                                                uint32_t tag) {
+  using G = Geo<R>;
+  const int w = wave_id(), lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+  if (w < G::RT && lr < kRows) {
+    uint64_t* dst = x.parts + (split * kRows + lr) * R + 16 * w + 4 * lq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __hip_atomic_store(dst + i, uint64_t(__float_as_uint(acc[i])) | (uint64_t(tag) << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// s_ok[q][w]: wavefront w < RT found all of its words of peer q's partial.
+template <int R>
+__device__ __forceinline__ void gather_partials(const FusedParams& p, const XchSlot& x, f32x4_t& acc,
+                                                float* s_part, int (*s_ok)[16], const uint8_t* xs,
+                                                __amdgpu_buffer_rsrc_t a_rsrc, int split, int C,
+                                                int nA_all, uint32_t tag) {
+  using G = Geo<R>;
+  const int w = wave_id(), lane = lane_id(), lr = lane & 15, lq = lane >> 4;
+  const bool holder = w < G::RT && lr < kRows;
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int q = 0; q < C; ++q) {
+    f32x4_t pq = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (q == split) {
+      pq = acc;
+    } else {
+      // the wavefronts holding v poll their words of peer q's partial
+      uint64_t wv[4] = {0, 0, 0, 0};
+      if (w < G::RT) {
+        const uint64_t* src = x.parts + (q * kRows + lr) * R + 16 * w + 4 * lq;
+        bool ok = false;
+        for (int n = 0; n < p.peer_wait; ++n) {
+          ok = true;
+          if (holder) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
+          }
+          if (__ballot(!ok) == 0) break;
+          __builtin_amdgcn_s_sleep(8);
+        }
+        if (lane == 0) s_ok[q][w] = __ballot(!ok) == 0;
+      }
+      stage_barrier<63>();
+      bool all_ok = true;
+#pragma unroll
+      for (int k = 0; k < G::RT; ++k) all_ok = all_ok && s_ok[q][k] != 0;
+      if (!all_ok) {
+        stage_barrier<0>();  // X, and everything else in flight, has landed
+        pq = a_partial_direct<R>(p, a_rsrc, xs, q * nA_all / C, (q + 1) * nA_all / C);
+        reduce_ksteps<R>(pq, s_part);
+      } else if (holder) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pq[i] = __uint_as_float(uint32_t(wv[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += pq[i];
+  }
+  acc = v;
+}
+
+// After the pass (every wavefront has used the slot): the last peer out
+// advances the slot's generation, which retires this call's tag.
+__device__ __forceinline__ void depart_slot(const XchSlot& x, int C, uint32_t tag) {
+  if (threadIdx.x == 0) {
+    // every read of the slot by this workgroup has returned (its values were used)
+    const int old = __hip_atomic_fetch_add(x.depart, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == C - 1) {
+      __hip_atomic_store(x.gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(x.depart, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// B stage u of the ring issued by the wavefronts w >= RT alone (at the
+// exchange, where the wavefronts w < RT are busy with the peers): wavefront
+// w loads its own chunks and, for RT <= w < 2 RT, those of wavefront w - RT.
+template <int R>
+__device__ __forceinline__ void issue_stage_cover(const FusedParams& p, i32x4_t br, int u, int ncols,
+                                                  uint32_t lds) {
+  using G = Geo<R>;
+  static_assert(2 * G::RT <= kST / kWave, "the other wavefronts cover the holders' chunks");
+  const int w = wave_id(), lane = lane_id();
+  auto one = [&](int wc) {
+    const int q = wc * kWave + lane;
+    const int col = q / G::CPR, js = q % G::CPR;
+    const int n = u * G::NCS + col;
+    const int jc = js ^ (col & (G::SW - 1));
+    dma16(br, lds + wc * kWave * 16, n < ncols ? uint32_t(n * R + 8 * jc) * 2u : kOob);
+  };
+  one(w);
+  if (w < 2 * G::RT) one(w - G::RT);
+}
+
+// The wait for the first B stage after the exchange: with `later` stages
+// issued after it, a wavefront has later * (its instructions per stage) of
+// them outstanding -- none for w < RT, two for RT <= w < 2 RT, one above.
+template <int R>
+__device__ __forceinline__ void wait_first_b(int later) {
+  using G = Geo<R>;
+  static_assert(kSlots - 2 <= 7, "vmcnt range");
+  const int w = wave_id();
+  const int n = w < G::RT ? 0 : (w < 2 * G::RT ? 2 * later : later);
+  if (n == 0) stage_barrier<0>();
+  else wait_counts<2 * (kSlots - 2)>(n);
 }
 
 // NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
@@ -155,7 +365,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ float s_w[kRows];
   __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
   __shared__ uint2 s_dummy[kWave];            // stores of lanes with no output
-  static_assert(kST * 4 * 4 <= kXBytes, "k-step partials reuse the X buffer");
+  __shared__ __align__(16) float s_part[kST * 4];  // k-step partials
+  __shared__ int s_ok[kMaxPeers][16];         // K split: peer q's words found by wavefront w
+  __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
@@ -211,10 +423,23 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int lr = lane & 15, lq = lane >> 4;
   const int K8 = p.K / 8, c8 = ncols / 8;
-  const int nA = (p.K + G::KT - 1) / G::KT, nB = (ncols + G::NCS - 1) / G::NCS, T = nA + nB;
+  // K split: with an exchange area, the C workgroups of the unit (one per
+  // column split with columns) each multiply stages [ka0, ka0 + nA) of the
+  // nA_all A stages and meet before the expand
+  const int C = (p.Ns + nsz - 1) / nsz;
+  const bool xch = p.xch != nullptr && C > 1 && C <= kMaxPeers;
+  const int nA_all = (p.K + G::KT - 1) / G::KT;
+  const int ka0 = xch ? split * nA_all / C : 0;
+  const int nA = xch ? (split + 1) * nA_all / C - ka0 : nA_all;
+  const int nB = (ncols + G::NCS - 1) / G::NCS, T = nA + nB;
+  const int TA = xch ? nA : T;  // stages issued ahead until the exchange
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a + wsel * R * p.K, uint32_t(R * p.K * 2));
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
   for (int g0 = 0; g0 < p.B; g0 += kRows) {
+    const XchSlot xs_slot = xch ? xch_slot<R>(p, unit * p.xch_passes + g0 / kRows) : XchSlot{};
+    if (xch && tid == 0)
+      s_tag = __hip_atomic_load(xs_slot.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     if (tid < kRows) {
       int pid = p.numel, xrow = -1;
       float wv = 1.f;
@@ -252,8 +477,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
                                ? uint32_t(int64_t(pid) * p.N + 8 * c) * 2u : kOob;
       dma16(yr, ys_lds + q0 * 16, off);
     }
-    for (int t = 0; t < kSlots - 1 && t < T; ++t)
-      issue_stage<R>(p, ar, br, t, nA, ncols, ring_lds + t * kStage);
+    for (int t = 0; t < kSlots - 1 && t < TA; ++t)
+      issue_stage<R>(p, ar, br, t, nA, ka0, ncols, ring_lds + t * kStage);
 
     // wavefront w: A rank tile rt and k-step ka of every A stage
     const int rt = w % G::RT, ka = w / G::RT;
@@ -263,45 +488,52 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
+    const uint32_t tag = xch ? __builtin_amdgcn_readfirstlane(s_tag) : 0u;
     for (int t = 0; t < T; ++t) {
+      if (t == nA) {
+        // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
+        reduce_ksteps<R>(acc, s_part);
+        if (xch) {
+          // the wavefronts holding v publish and poll; the others meanwhile
+          // load the first B stages, the holders' chunks included, so no
+          // wait for a peer's values queues behind a B load (a wavefront's
+          // memory counter retires in order)
+          if (w < G::RT) {
+            publish_partial<R>(xs_slot, acc, split, tag);
+          } else {
+            for (int q = 0; q < kSlots - 1 && nA + q < T; ++q)
+              issue_stage_cover<R>(p, br, nA + q - nA, ncols, ring_lds + ((nA + q) % kSlots) * kStage);
+          }
+          gather_partials<R>(p, xs_slot, acc, s_part, s_ok, xs, a_rsrc, split, C, nA_all, tag);
+        }
+        // lane (lr, lq) of wavefront w < RT holds v[row lr][16 w + 4 lq + i]
+        if (w < G::RT && lr < kRows) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint16_t hi = f32_to_bf16(acc[i]);
+            s_vb[lr * VP + 16 * w + 4 * lq + i] = hi;
+            s_vl[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i] - bf16_to_f32(hi));
+          }
+        }
+      }
       // stage t (and, at t = 0, the X rows and Y values issued before it):
       // the later stages stay in flight, so the ring never drains to empty
-      wait_stage<kSlots - 2>(min(kSlots - 2, T - 1 - t));
-      if (t + kSlots - 1 < T)
-        issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ncols,
+      // (with the K split the A stages drain before the exchange)
+      const int lim = t < nA ? TA : T;
+      if (xch && t == nA) wait_first_b<R>(min(kSlots - 2, T - 1 - t));
+      else wait_stage<kSlots - 2>(min(kSlots - 2, lim - 1 - t));
+      if (t + kSlots - 1 < lim)
+        issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ka0, ncols,
                        ring_lds + ((t + kSlots - 1) % kSlots) * kStage);
       const uint4* st = reinterpret_cast<const uint4*>(ring + (t % kSlots) * kStage);
       if (t < nA) {
         // ---- shrink: V^T[rank tile rt] += A[16 ranks x 32 k] . X^T
         const int j = 16 * rt + lr, c = 4 * ka + lq;
         const uint4 a = st[j * G::CPRK + (c ^ (j & 7))];
-        const int xc = t * (G::KT / 8) + c;
+        const int xc = (ka0 + t) * (G::KT / 8) + c;
         const uint4 x = (lr < kRows && xc < K8)
                             ? reinterpret_cast<const uint4*>(xs)[lr * K8 + xc] : zero4;
         acc = mfma16(a, x, acc);
-        if (t == nA - 1) {
-          // k-step partials through the X buffer (X is no longer needed)
-          float* part = reinterpret_cast<float*>(xs);
-          stage_barrier<63>();
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part[(w * 4 + i) * kWave + lane] = acc[i];
-          stage_barrier<63>();
-          if (w < G::RT) {
-#pragma unroll
-            for (int k = 1; k < G::KSA; ++k)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[i] += part[((w + k * G::RT) * 4 + i) * kWave + lane];
-            // lane (lr, lq) holds v[row lr][16 w + 4 lq + i]
-            if (lr < kRows) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint16_t hi = f32_to_bf16(acc[i]);
-                s_vb[lr * VP + 16 * w + 4 * lq + i] = hi;
-                s_vl[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i] - bf16_to_f32(hi));
-              }
-            }
-          }
-        }
       } else {
         // ---- expand: D^T[16 cols x 16 rows] = B[16 cols x 32 ranks] . V^T
         const int u = t - nA;
@@ -350,6 +582,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       }
     }
     __syncthreads();
+    if (xch) depart_slot(xs_slot, C, tag);
     // ---- epilogue: Y rows of the split, 16 bytes per thread and step
     for (int q = tid; q < nr * c8; q += kST) {
       const int i = q / c8, c = q % c8;
@@ -369,6 +602,14 @@ bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int
   if (int64_t(kRows) * K * 2 > kXBytes) return false;
   const int64_t x_bytes = (x_per_pair ? numel : M) * K * 2;
   return x_bytes <= kMaxBufBytes && numel * N * 2 <= kMaxBufBytes && r * K * 2 <= kMaxBufBytes;
+}
+
+// Exchange area of the K split for a launch: one slot per (unit, pass).
+int stream_exchange_passes(int block_m) { return (block_m + kRows - 1) / kRows; }
+
+int64_t stream_exchange_bytes(int64_t units, int block_m, int r) {
+  const int64_t slots = units * stream_exchange_passes(block_m);
+  return 4 * xch_part_words(slots) + slots * kMaxPeers * kRows * r * 8;
 }
 
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {

@@ -57,6 +57,9 @@ struct FusedParams {
   int32_t xcd_cus;     // compute units per XCD of the current device
   int32_t naive;       // 1: blocks formed on chip from topk_ids and mapping (no align outputs)
   int32_t nbits;       // align-free path: bits of a key l * E + e
+  int32_t* xch;        // stream kernel: K-split exchange area, zero between calls (null: none)
+  int32_t xch_passes;  // stream kernel: passes per block the exchange area holds
+  int32_t peer_wait;   // stream kernel: polls for a peer's partial before computing it here
   float* ws;           // two-kernel path: partial rank vectors, fp32 [kz, S, numel, r]
   int32_t kz;          // two-kernel path: K splits of the shrink
   int32_t kchunk;      // two-kernel path: K per split (a multiple of 32)
@@ -65,6 +68,11 @@ struct FusedParams {
 // Largest rank of the two-kernel path, and the ranks of one shrink workgroup.
 constexpr int kMaxRankTwoKernel = 512;
 constexpr int kTwoKernelRankGroup = 128;
+
+// Polls for a peer's partial in the stream kernel's K split before the
+// workgroup computes it itself (each poll is one round trip plus a short
+// sleep, about 0.7 us).
+constexpr int kDefaultPeerWait = 64;
 
 // Most pairs the align-free path groups (one per thread of a workgroup).
 constexpr int64_t kNaiveMaxPairs = 1024;
@@ -82,6 +90,8 @@ int xcd_compute_units();
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st);
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st);
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st);
+int64_t stream_exchange_bytes(int64_t units, int block_m, int r);
+int stream_exchange_passes(int block_m);
 bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);
 // Whether the vector variant runs the stream kernel for these sizes.
 bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);

@@ -216,6 +216,53 @@ def test_naive_binding_checks_before_calling():
                                  mul_routed_weight=False, add_inputs=True)
 
 
+def ws_call(**kw):
+    a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
+             add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
+             variant=1, ws=P16, ws_bytes=1 << 40, wait=-1)
+    a.update(kw)
+    return mla.lib().fused_moe_lora_ws(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"],
+                                       a["eids"], a["ntpp"], a["w"], a["mul"], a["add"], a["M"],
+                                       a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"],
+                                       a["r"], a["B"], a["y"], a["variant"], a["ws"],
+                                       a["ws_bytes"], a["wait"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(y=V(18)), mla.ERR_INVALID),
+    (dict(r=129), mla.ERR_UNSUPPORTED),
+    (dict(K=2884), mla.ERR_INVALID),
+    (dict(variant=3), mla.ERR_INVALID),
+    (dict(ws_bytes=-1), mla.ERR_INVALID),
+    # the decode stream kernel takes this shape and needs the exchange area
+    (dict(ws=None), mla.ERR_WORKSPACE),
+    (dict(ws_bytes=4096), mla.ERR_WORKSPACE),
+    (dict(ws=V(24)), mla.ERR_WORKSPACE),
+    (dict(M=0), mla.OK),
+    (dict(M=0, x=None, y=None, sorted=None, ws=None, ws_bytes=0), mla.OK),
+])
+def test_fused_ws_rejects(kw, status):
+    assert ws_call(**kw) == status
+
+
+def test_fused_workspace_query():
+    q = mla.fused_moe_lora_workspace_bytes
+    # decode stream kernel: slots of (unit, 4-row pass), 8 peers of 4 x r fp32 each
+    b = q(16, 4, 2880, 2880, 2, 32, 6, 64, 16, False, "valu")
+    assert b > 0 and b % 16 == 0
+    assert q(16, 4, 2880, 2880, 2, 32, 6, 128, 16, False, "valu") > b  # rank 128: larger partials
+    assert q(16, 4, 2880, 2880, 2, 32, 6, 64, 32, False, "valu") > b   # more passes per block
+    # kernels without the K split need none
+    assert q(16, 2, 256, 128, 1, 8, 2, 8, 16) == 0                    # register-batch kernel
+    assert q(16, 4, 2880, 2880, 2, 32, 6, 64, 16, False, "mfma") == 0
+    assert q(8192, 8, 2048, 768, 2, 128, 8, 128, 64) == 0            # MFMA prefill
+    assert q(0, 4, 2880, 2880, 2, 32, 6, 64, 16) == 0
+    with pytest.raises(mla.MoeLoraError):
+        q(16, 4, 2880, 2880, 2, 32, 6, 129, 16)
+
+
 def two_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=256, B=16, y=P16,
