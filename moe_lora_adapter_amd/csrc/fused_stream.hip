@@ -196,9 +196,10 @@ __device__ __forceinline__ f32x4_t a_partial_direct(const FusedParams& p, __amdg
 
 // Exchange area of the K split, for `slots` (unit, pass) slots: generation
 // words [slots] (uint32), departures [slots] (int32), then from a 16-byte
-// boundary the partials, [slots][kMaxPeers][kRows][r] 64-bit words, each an
-// fp32 value in the low half and its call's tag in the high half.  Zero-filled
-// before first use; after that every call leaves it usable as it is.
+// boundary the partials, [slots][2][kMaxPeers][kRows][r] 64-bit words, each
+// an fp32 value in the low half and its call's tag in the high half (copy 0
+// written through the XCD's L2, copy 1 at device scope).  Zero-filled before
+// first use; after that every call leaves it usable as it is.
 __host__ __device__ inline int64_t xch_part_words(int64_t slots) { return (2 * slots + 3) / 4 * 4; }
 
 // The K split of one pass.  The peers -- the C workgroups of a unit, one per
@@ -213,17 +214,24 @@ __host__ __device__ inline int64_t xch_part_words(int64_t slots) { return (2 * s
 // memory (the same bits), so no wait depends on another workgroup being
 // resident.
 //
-// Every access to the exchange area is a device-scope relaxed atomic: a load
-// or store that is coherent across the XCDs' L2 caches by itself.  Device-
-// scope release / acquire fences would order plain accesses instead, but each
+// A partial is written twice: copy 0 with ordinary stores, which land in the
+// L2 of the writer's XCD, and copy 1 with device-scope stores, coherent
+// across the XCDs' L2s.  The peers of a unit are launched on one XCD, so
+// three polls of every four read copy 0 from that shared L2 (dropping this
+// compute unit's L1 copy first) and the fourth reads copy 1 at device scope,
+// which also finds a peer that ran on another XCD.
+// (Device-scope stores go past the L2, so copy 1 alone, read through the L2,
+// can stay stale there; read at device scope it costs a memory round trip
+// under the streaming load, about 3 us.)  None of this decides correctness:
+// a word with this call's tag is this call's value, and a stale read only
+// costs another poll, or at worst the partial computed here.  Device-scope
+// release / acquire fences would order plain accesses instead, but each
 // writes back or invalidates a whole L2: measured on MI355X, 20 to 30 us per
-// exchange instead of about 3.  (Reading the peers' shared L2 first, past
-// this compute unit's L1, measured no faster and sometimes missed the peer's
-// values until the device-scope reads.)
+// exchange.
 struct XchSlot {
   uint32_t* gen;
   int* depart;
-  uint64_t* parts;  // [kMaxPeers][kRows][R]
+  uint64_t* parts;  // [2][kMaxPeers][kRows][R]
 };
 
 template <int R>
@@ -232,7 +240,7 @@ __device__ __forceinline__ XchSlot xch_slot(const FusedParams& p, int slot) {
   XchSlot x;
   x.gen = reinterpret_cast<uint32_t*>(p.xch) + slot;
   x.depart = p.xch + slots + slot;
-  x.parts = reinterpret_cast<uint64_t*>(p.xch + xch_part_words(slots)) + int64_t(slot) * kMaxPeers * kRows * R;
+  x.parts = reinterpret_cast<uint64_t*>(p.xch + xch_part_words(slots)) + int64_t(slot) * 2 * kMaxPeers * kRows * R;
   return x;
 }
 
@@ -244,9 +252,12 @@ __device__ __forceinline__ void publish_partial(const XchSlot& x, const f32x4_t&
   if (w < G::RT && lr < kRows) {
     uint64_t* dst = x.parts + (split * kRows + lr) * R + 16 * w + 4 * lq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __hip_atomic_store(dst + i, uint64_t(__float_as_uint(acc[i])) | (uint64_t(tag) << 32),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t word = uint64_t(__float_as_uint(acc[i])) | (uint64_t(tag) << 32);
+      __hip_atomic_store(dst + i, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(dst + kMaxPeers * kRows * R + i, word, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -273,9 +284,20 @@ __device__ __forceinline__ void gather_partials(const FusedParams& p, const XchS
         bool ok = false;
         for (int n = 0; n < p.peer_wait; ++n) {
           ok = true;
-          if (holder) {
+          if ((n & 3) != 3) {
+            asm volatile("buffer_inv sc0" ::: "memory");  // this compute unit's L1 only
+            if (holder) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int i = 0; i < 4; ++i)
+                wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+          } else if (holder) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              wv[i] = __hip_atomic_load(src + kMaxPeers * kRows * R + i, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (holder) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
           }
@@ -609,7 +631,7 @@ int stream_exchange_passes(int block_m) { return (block_m + kRows - 1) / kRows; 
 
 int64_t stream_exchange_bytes(int64_t units, int block_m, int r) {
   const int64_t slots = units * stream_exchange_passes(block_m);
-  return 4 * xch_part_words(slots) + slots * kMaxPeers * kRows * r * 8;
+  return 4 * xch_part_words(slots) + slots * 2 * kMaxPeers * kRows * r * 8;
 }
 
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
