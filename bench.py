@@ -395,8 +395,14 @@ def main(argv=None):
     ap.add_argument("--no-dual-stream", action="store_true",
                     help="skip the dual-stream overlap line")
     ap.add_argument("--no-k-split", action="store_true",
-                    help="skip the K-split (fused_moe_lora_ws) line")
+                    help="time fused_moe_lora (no workspace) as the step, not fused_moe_lora_ws")
+    ap.add_argument("--no-plain-line", action="store_true",
+                    help="skip the line that times the step without the K split")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone: no comparison lines (profiler runs)")
     args = ap.parse_args(argv)
+    if args.step_only:
+        args.no_plain_line = args.no_two_kernel = args.no_dual_stream = True
 
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path has no "
@@ -431,7 +437,17 @@ def main(argv=None):
                   file=sys.stderr)
             return 2
     naive_fn = lambda ds: run_naive(ds, s, naive_bm, variant)  # noqa: E731
-    step_fn = naive_fn if args.path == "naive" else (lambda ds: step(ds, s, variant))
+    # the sorted path's step: align + fused_moe_lora_ws when the fused kernel
+    # uses a workspace (the decode stream kernel's K split), else align +
+    # fused_moe_lora; one zero-filled workspace serves every copy (the calls
+    # run one after another)
+    nbx = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                             s.block_m, s.x_per_pair, variant)
+    k_split = args.path == "sorted" and nbx > 0 and not args.no_k_split
+    xws = torch.zeros(nbx, dtype=torch.uint8, device=dev) if k_split else None
+    fused_fn = ((lambda ds: run_fused_ws(ds, s, variant, xws)) if k_split  # noqa: E731
+                else (lambda ds: run_fused(ds, s, variant)))
+    step_fn = naive_fn if args.path == "naive" else (lambda ds: (run_align(ds, s), fused_fn(ds)))
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -448,7 +464,7 @@ def main(argv=None):
         align_avg = None
         kbytes = work["naive_bytes"]
     else:
-        fused_avg = time_kernel_events(sets, s, variant, "fused", args.steps)
+        fused_avg = time_kernel_events(sets, s, variant, fused_fn, args.steps)
         align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
         kbytes = work["fused_bytes"]
 
@@ -475,7 +491,9 @@ def main(argv=None):
                    "topk": s.topk, "L": s.L, "active_slots": s.active, "r": s.r,
                    "block_m": s.block_m, "mul_routed_weight": s.mul, "add_inputs": s.add,
                    "x_per_pair": s.x_per_pair,
-                   "step": ("moe_lora_align + fused_moe_lora" if args.path == "sorted" else
+                   "step": (("moe_lora_align + fused_moe_lora_ws (K split over a block's "
+                             "workgroups)" if k_split else "moe_lora_align + fused_moe_lora")
+                            if args.path == "sorted" else
                             f"fused_moe_lora_naive (no align step), block_m={naive_bm}"),
                    "timing": "one HIP graph of K steps",
                    "cache": ("warm" if args.warm else
@@ -491,7 +509,7 @@ def main(argv=None):
         "align_kernel_us_avg": round(align_avg, 3) if align_avg is not None else None,
         "work": work,
     }
-    if args.path == "sorted" and naive_ok:
+    if args.path == "sorted" and naive_ok and not args.step_only:
         # the align-free path on the same inputs: no align launch, blocks
         # formed on chip (block_m of the workload, and one pair per block)
         out["align_free"] = []
@@ -509,27 +527,23 @@ def main(argv=None):
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})
-    if args.path == "sorted" and not args.no_k_split:
-        # the same step with fused_moe_lora_ws: the decode stream kernel's
-        # workgroups of a block split the shrink's K range and exchange
-        # partial rank vectors (only when that kernel runs)
-        nbx = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
-                                                 s.block_m, s.x_per_pair, variant)
-        if nbx > 0:
-            # one zero-filled workspace: the calls run one after another
-            xws = torch.zeros(nbx, dtype=torch.uint8, device=dev)
-            log("K-split path")
-            fnk = lambda ds: (run_align(ds, s), run_fused_ws(ds, s, variant, xws))  # noqa: E731
+    if k_split:
+        out["k_split_workspace_bytes"] = nbx
+        if not args.no_plain_line:
+            # the same step without the K split (fused_moe_lora: every
+            # workgroup of a block multiplies all of A)
+            log("step without the K split")
+            fnp = lambda ds: (run_align(ds, s), run_fused(ds, s, variant))  # noqa: E731
             for i in range(args.warmup):
-                fnk(sets[i % copies])
-            usk = time_steps_graph(sets, s, variant, args.steps, fn=fnk) * 1e6
-            kusk = time_kernel_events(sets, s, variant,
-                                      lambda ds: run_fused_ws(ds, s, variant, xws), args.steps)
-            gk = work["fused_bytes"] / (kusk * 1e-6) / 1e9
-            out["k_split"] = {"us_per_call": round(usk, 3), "kernel": kname,
-                              "kernel_us_avg": round(kusk, 3), "achieved_GBps": round(gk, 1),
-                              "frac": round(gk / HBM_PEAK_GBPS, 4), "workspace_bytes": nbx,
-                              "speedup_vs_plain_kernel": round(fused_avg / kusk, 3)}
+                fnp(sets[i % copies])
+            usp = time_steps_graph(sets, s, variant, args.steps, fn=fnp) * 1e6
+            kusp = time_kernel_events(sets, s, variant, "fused", args.steps)
+            gp = work["fused_bytes"] / (kusp * 1e-6) / 1e9
+            out["without_k_split"] = {"us_per_call": round(usp, 3), "kernel": kname,
+                                      "kernel_us_avg": round(kusp, 3),
+                                      "achieved_GBps": round(gp, 1),
+                                      "frac": round(gp / HBM_PEAK_GBPS, 4),
+                                      "k_split_kernel_speedup": round(kusp / fused_avg, 3)}
     if args.path == "sorted" and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
         # the two-kernel path on the same inputs (rank vectors through memory):
         # the comparator of the one-shot kernels

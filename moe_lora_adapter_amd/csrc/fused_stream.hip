@@ -62,6 +62,7 @@ constexpr int kMaxCols = 2048;              // output columns per workgroup
 constexpr int kYBytes = kRows * kMaxCols * 2;
 constexpr int kMaxIds = 128;                // largest block_m
 constexpr int kMaxPeers = 8;                // most workgroups one K split spans
+constexpr int kLocalPolls = 3;              // polls of the XCD's L2 before device-scope reads
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
 // Ring depth: slots - 1 stages in flight per workgroup.  Three slots (32 KiB
@@ -216,9 +217,9 @@ __host__ __device__ inline int64_t xch_part_words(int64_t slots) { return (2 * s
 //
 // A partial is written twice: copy 0 with ordinary stores, which land in the
 // L2 of the writer's XCD, and copy 1 with device-scope stores, coherent
-// across the XCDs' L2s.  The peers of a unit are launched on one XCD, so
-// three polls of every four read copy 0 from that shared L2 (dropping this
-// compute unit's L1 copy first) and the fourth reads copy 1 at device scope,
+// across the XCDs' L2s.  The peers of a unit are launched on one XCD, so the
+// first kLocalPolls polls read copy 0 from that shared L2 (dropping this
+// compute unit's L1 copy first); later polls read copy 1 at device scope,
 // which also finds a peer that ran on another XCD.
 // (Device-scope stores go past the L2, so copy 1 alone, read through the L2,
 // can stay stale there; read at device scope it costs a memory round trip
@@ -281,28 +282,39 @@ __device__ __forceinline__ void gather_partials(const FusedParams& p, const XchS
       uint64_t wv[4] = {0, 0, 0, 0};
       if (w < G::RT) {
         const uint64_t* src = x.parts + (q * kRows + lr) * R + 16 * w + 4 * lq;
+        const uint64_t* src_dev = src + kMaxPeers * kRows * R;
         bool ok = false;
-        for (int n = 0; n < p.peer_wait; ++n) {
+        // two loops, one load form each: a loop whose body picks between the
+        // two forms left the compiler waiting for every memory operation at
+        // each step of the stage loop around it (the ring's DMA is invisible
+        // to it, so that wait drained the ring)
+        int n = 0;
+        for (; n < kLocalPolls && n < p.peer_wait; ++n) {
+          asm volatile("buffer_inv sc0" ::: "memory");  // this compute unit's L1 only
           ok = true;
-          if ((n & 3) != 3) {
-            asm volatile("buffer_inv sc0" ::: "memory");  // this compute unit's L1 only
-            if (holder) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-          } else if (holder) {
+          if (holder) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              wv[i] = __hip_atomic_load(src + kMaxPeers * kRows * R + i, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-          }
-          if (holder) {
+              wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
           }
           if (__ballot(!ok) == 0) break;
           __builtin_amdgcn_s_sleep(8);
+        }
+        if (__ballot(!ok) != 0) {
+          for (; n < p.peer_wait; ++n) {
+            ok = true;
+            if (holder) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                wv[i] = __hip_atomic_load(src_dev + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
+            }
+            if (__ballot(!ok) == 0) break;
+            __builtin_amdgcn_s_sleep(8);
+          }
         }
         if (lane == 0) s_ok[q][w] = __ballot(!ok) == 0;
       }

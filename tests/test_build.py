@@ -49,3 +49,38 @@ def test_no_kernel_spills_registers():
             n += 1
             assert u.get("ScratchSize", 0) == 0, f"{os.path.basename(src)}: {name} spills: {u}"
     assert n >= 40, f"expected every kernel instantiation, found {n}"
+
+
+def _kernel_asm(src):
+    flags = [f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [HIPCC, *flags, "-I", os.path.join(build.ROOT, "include"), "--cuda-device-only", "-S",
+           src, "-o", "-"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return res.stdout
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="no hipcc")
+def test_stream_stage_loop_keeps_the_ring_in_flight():
+    """The decode stream kernel's stage loop waits for its ring stages with
+    explicit counts (its DMA is inline assembly the compiler does not track).
+    A full memory wait the compiler adds inside that loop -- one not at a
+    workgroup barrier -- drains the ring on every stage; one crept in once
+    through a poll loop in the K split and cost half the kernel's speed."""
+    asm = _kernel_asm(os.path.join(build.ROOT, "moe_lora_adapter_amd", "csrc", "fused_stream.hip"))
+    found = 0
+    for m in re.finditer(r"^(_ZN\S*fused_stream_kernel\S*):", asm, re.M):
+        found += 1
+        body = asm[m.start():asm.index(".Lfunc_end", m.start())].splitlines()
+        depth = 0
+        bad = []
+        for k, line in enumerate(body):
+            if line.startswith(".LBB"):
+                d = re.search(r"Depth=(\d+)", line)
+                depth = int(d.group(1)) if d else 0
+            if "vmcnt(0)" in line and depth == 2:
+                nxt = " ".join(body[k + 1:k + 3])
+                if "s_barrier" not in nxt:
+                    bad.append(k)
+        assert not bad, f"{m.group(1)}: full memory waits inside the stage loop at lines {bad}"
+    assert found >= 6, f"expected the stream kernel instantiations, found {found}"
