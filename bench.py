@@ -394,15 +394,15 @@ def main(argv=None):
                     help="skip the two-kernel comparator line")
     ap.add_argument("--no-dual-stream", action="store_true",
                     help="skip the dual-stream overlap line")
-    ap.add_argument("--no-k-split", action="store_true",
-                    help="time fused_moe_lora (no workspace) as the step, not fused_moe_lora_ws")
-    ap.add_argument("--no-plain-line", action="store_true",
-                    help="skip the line that times the step without the K split")
+    ap.add_argument("--k-split", action="store_true",
+                    help="time align + fused_moe_lora_ws (K split) as the step")
+    ap.add_argument("--no-k-split-line", action="store_true",
+                    help="skip the line that times the step with the K split")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone: no comparison lines (profiler runs)")
     args = ap.parse_args(argv)
     if args.step_only:
-        args.no_plain_line = args.no_two_kernel = args.no_dual_stream = True
+        args.no_k_split_line = args.no_two_kernel = args.no_dual_stream = True
 
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path has no "
@@ -437,14 +437,14 @@ def main(argv=None):
                   file=sys.stderr)
             return 2
     naive_fn = lambda ds: run_naive(ds, s, naive_bm, variant)  # noqa: E731
-    # the sorted path's step: align + fused_moe_lora_ws when the fused kernel
-    # uses a workspace (the decode stream kernel's K split), else align +
-    # fused_moe_lora; one zero-filled workspace serves every copy (the calls
-    # run one after another)
+    # the sorted path's step: align + fused_moe_lora, or with --k-split align +
+    # fused_moe_lora_ws when its kernel uses a workspace (the decode stream
+    # kernel's K split); one zero-filled workspace serves every copy (the
+    # calls run one after another)
     nbx = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
                                              s.block_m, s.x_per_pair, variant)
-    k_split = args.path == "sorted" and nbx > 0 and not args.no_k_split
-    xws = torch.zeros(nbx, dtype=torch.uint8, device=dev) if k_split else None
+    k_split = args.path == "sorted" and nbx > 0 and args.k_split
+    xws = torch.zeros(nbx, dtype=torch.uint8, device=dev) if nbx > 0 else None
     fused_fn = ((lambda ds: run_fused_ws(ds, s, variant, xws)) if k_split  # noqa: E731
                 else (lambda ds: run_fused(ds, s, variant)))
     step_fn = naive_fn if args.path == "naive" else (lambda ds: (run_align(ds, s), fused_fn(ds)))
@@ -527,23 +527,25 @@ def main(argv=None):
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})
-    if k_split:
-        out["k_split_workspace_bytes"] = nbx
-        if not args.no_plain_line:
-            # the same step without the K split (fused_moe_lora: every
-            # workgroup of a block multiplies all of A)
-            log("step without the K split")
-            fnp = lambda ds: (run_align(ds, s), run_fused(ds, s, variant))  # noqa: E731
-            for i in range(args.warmup):
-                fnp(sets[i % copies])
-            usp = time_steps_graph(sets, s, variant, args.steps, fn=fnp) * 1e6
-            kusp = time_kernel_events(sets, s, variant, "fused", args.steps)
-            gp = work["fused_bytes"] / (kusp * 1e-6) / 1e9
-            out["without_k_split"] = {"us_per_call": round(usp, 3), "kernel": kname,
-                                      "kernel_us_avg": round(kusp, 3),
-                                      "achieved_GBps": round(gp, 1),
-                                      "frac": round(gp / HBM_PEAK_GBPS, 4),
-                                      "k_split_kernel_speedup": round(kusp / fused_avg, 3)}
+    if args.path == "sorted" and nbx > 0 and not args.no_k_split_line:
+        # the step the other way: with the K split (fused_moe_lora_ws: the
+        # workgroups of a block share A's K range and exchange partial rank
+        # vectors) or, when that is the step, without it
+        other = not k_split
+        log("step with the K split" if other else "step without the K split")
+        ofn = ((lambda ds: run_fused_ws(ds, s, variant, xws)) if other  # noqa: E731
+               else (lambda ds: run_fused(ds, s, variant)))
+        fno = lambda ds: (run_align(ds, s), ofn(ds))  # noqa: E731
+        for i in range(args.warmup):
+            fno(sets[i % copies])
+        uso = time_steps_graph(sets, s, variant, args.steps, fn=fno) * 1e6
+        kuso = time_kernel_events(sets, s, variant, ofn, args.steps)
+        go = work["fused_bytes"] / (kuso * 1e-6) / 1e9
+        kplain, ksplit = (fused_avg, kuso) if other else (kuso, fused_avg)
+        out["with_k_split" if other else "without_k_split"] = {
+            "us_per_call": round(uso, 3), "kernel": kname, "kernel_us_avg": round(kuso, 3),
+            "achieved_GBps": round(go, 1), "frac": round(go / HBM_PEAK_GBPS, 4),
+            "workspace_bytes": nbx, "k_split_kernel_speedup": round(kplain / ksplit, 3)}
     if args.path == "sorted" and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
         # the two-kernel path on the same inputs (rank vectors through memory):
         # the comparator of the one-shot kernels

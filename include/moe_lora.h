@@ -171,6 +171,10 @@ MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
  * never reaches memory in bf16 and is identical in every workgroup.  (The
  * split-K shrink of the pages' two-kernel path -- prhub summary of vLLM PR
  * #42290, implementation steps -- applied inside the one-shot kernel.)
+ * Measured on MI355X it is no faster than fused_moe_lora at the decode
+ * shapes configured here (the exchange costs about what sharing A saves);
+ * it is kept as the comparator of that design and for callers whose blocks
+ * have many column ranges.
  *   workspace    [device] fused_moe_lora_workspace_bytes() bytes, 16-byte
  *                aligned and ZERO-FILLED before its first use.  Every call
  *                leaves its flag words zero again (in stream order; the

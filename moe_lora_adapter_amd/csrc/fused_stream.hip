@@ -384,8 +384,12 @@ __device__ __forceinline__ void wait_first_b(int later) {
 }
 
 // NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
-// align-free path) instead of being read from the align outputs.
-template <int R, bool NAIVE>
+// align-free path) instead of being read from the align outputs.  XCH: the
+// K split (an exchange area is given); its own instantiation, so the state
+// it keeps does not crowd the registers of the kernel without it (the
+// shared build spilled scalar registers into vector lanes on every stage:
+// +2 us on the 20b-like decode).
+template <int R, bool NAIVE, bool XCH>
 __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   using G = Geo<R>;
   constexpr int VP = 32 * G::KS + 8;  // bf16 pitch of the v rows
@@ -399,7 +403,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ float s_w[kRows];
   __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
   __shared__ uint2 s_dummy[kWave];            // stores of lanes with no output
-  __shared__ __align__(16) float s_part[kST * 4];  // k-step partials
+  __shared__ __align__(16) float s_part[XCH ? kST * 4 : 4];  // k-step partials (K split)
+  static_assert(kST * 4 * 4 <= kXBytes, "k-step partials fit the X buffer");
   __shared__ int s_ok[kMaxPeers][16];         // K split: peer q's words found by wavefront w
   __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
@@ -461,7 +466,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // column split with columns) each multiply stages [ka0, ka0 + nA) of the
   // nA_all A stages and meet before the expand
   const int C = (p.Ns + nsz - 1) / nsz;
-  const bool xch = p.xch != nullptr && C > 1 && C <= kMaxPeers;
+  const bool xch = XCH && C > 1 && C <= kMaxPeers;
   const int nA_all = (p.K + G::KT - 1) / G::KT;
   const int ka0 = xch ? split * nA_all / C : 0;
   const int nA = xch ? (split + 1) * nA_all / C - ka0 : nA_all;
@@ -526,7 +531,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     for (int t = 0; t < T; ++t) {
       if (t == nA) {
         // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
-        reduce_ksteps<R>(acc, s_part);
+        // (the k-step partials go through the X buffer, which only the K
+        // split's fallback still reads)
+        reduce_ksteps<R>(acc, XCH ? s_part : reinterpret_cast<float*>(xs));
         if (xch) {
           // the wavefronts holding v publish and poll; the others meanwhile
           // load the first B stages, the holders' chunks included, so no
@@ -655,8 +662,9 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const dim3 grid(unsigned(kXcds * slots));
 #define MLR_STREAM_CASE(R_)                                                                  \
   case R_:                                                                                   \
-    if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true>), grid, dim3(kST), 0, st, p); \
-    else hipLaunchKernelGGL((fused_stream_kernel<R_, false>), grid, dim3(kST), 0, st, p);       \
+    if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false>), grid, dim3(kST), 0, st, p); \
+    else if (p.xch) hipLaunchKernelGGL((fused_stream_kernel<R_, false, true>), grid, dim3(kST), 0, st, p); \
+    else hipLaunchKernelGGL((fused_stream_kernel<R_, false, false>), grid, dim3(kST), 0, st, p);       \
     break;
   switch (p.r) {
     MLR_STREAM_CASE(32)
