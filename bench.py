@@ -1,7 +1,11 @@
 """Benchmark of the MoE-LoRA hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: moe_lora_align, then
-fused_moe_lora, on seeded synthetic inputs already resident in HBM.  The
+A step is one pass of the whole path over one batch -- the align outputs and
+the fused result -- on seeded synthetic inputs already resident in HBM: one
+fused_moe_lora_with_align launch where the batch allows it (at most 64 pairs
+and 64 slots; the decode shapes), else moe_lora_align then fused_moe_lora
+(``--path`` chooses; the two-launch step is reported beside the one-launch
+one).  The
 default workload is the gpt-oss-20b-like decode w13 shape (M=16, K=2880,
 N=2x2880, E=32, topk=4, L=6 slots all active, r=64, BLOCK_M=16).
 
@@ -103,10 +107,12 @@ def algorithmic_work(case):
     # the align-free path reads the routing (topk_ids, mapping) instead of the
     # align outputs
     naive_bytes = w_bytes + x_bytes + y_bytes + s.numel * 4 + s.M * 4 + (P * 4 if s.mul else 0)
+    # fused_moe_lora_with_align: the align-free read plus the align outputs written
+    with_align_bytes = naive_bytes + align_bytes - (s.numel * 4 + s.M * 4)
     return dict(valid_pairs=P, active_groups=len(keys), fused_bytes=int(fused_bytes),
                 weight_bytes=int(w_bytes), x_bytes=int(x_bytes), y_bytes=int(y_bytes),
                 meta_bytes=int(meta), fused_flops=flops, align_bytes=int(align_bytes),
-                naive_bytes=int(naive_bytes))
+                naive_bytes=int(naive_bytes), with_align_bytes=int(with_align_bytes))
 
 
 # ----------------------------------------------------------------- device inputs
@@ -156,6 +162,15 @@ def run_naive(ds, s, block_m, variant):
     mla.fused_moe_lora_naive(ds.x, ds.a, ds.b, ds.topk_ids, ds.mapping, ds.w, ds.y,
                              mul_routed_weight=s.mul, add_inputs=s.add, block_m=block_m,
                              x_per_pair=s.x_per_pair, variant=variant)
+
+
+def run_with_align(ds, s, variant):
+    """fused_moe_lora_with_align: the align outputs and the fused result in one launch."""
+    import moe_lora_adapter_amd as mla
+    mla.fused_moe_lora_with_align(ds.topk_ids, ds.mapping, ds.x, ds.a, ds.b, ds.w, ds.y, E=s.E,
+                                  L=s.L, block_m=s.block_m, mul_routed_weight=s.mul,
+                                  add_inputs=s.add, out=ds.align, x_per_pair=s.x_per_pair,
+                                  variant=variant)
 
 
 def naive_kernel_name(s, block_m, variant):
@@ -386,8 +401,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 256 MiB device copies (rocprofv3 counter scaling)")
-    ap.add_argument("--path", default="sorted", choices=["sorted", "naive"],
-                    help="naive: time fused_moe_lora_naive (no align step) as the step")
+    ap.add_argument("--path", default="auto", choices=["auto", "with_align", "sorted", "naive"],
+                    help="the step: with_align = fused_moe_lora_with_align (align outputs "
+                         "and fused result in one launch), sorted = moe_lora_align + "
+                         "fused_moe_lora, naive = fused_moe_lora_naive (no align outputs); "
+                         "auto = with_align where it applies (<= 64 pairs and slots), else "
+                         "sorted")
     ap.add_argument("--naive-block-m", type=int, default=None,
                     help="block_m of the align-free path (default: the workload's)")
     ap.add_argument("--no-two-kernel", action="store_true",
@@ -430,12 +449,18 @@ def main(argv=None):
         sets.append(DeviceSet(case, dev, proto=sets[0]))
     variant = args.variant
     naive_ok = s.numel <= mla.NAIVE_MAX_PAIRS
+    wa_ok = s.numel <= mla.WITH_ALIGN_MAX_PAIRS and s.L <= mla.WITH_ALIGN_MAX_SLOTS
     naive_bm = args.naive_block_m or s.block_m
-    if args.path == "naive":
-        if not naive_ok:
-            print(f"bench.py: the align-free path takes at most {mla.NAIVE_MAX_PAIRS} pairs",
-                  file=sys.stderr)
-            return 2
+    path = args.path if args.path != "auto" else ("with_align" if wa_ok else "sorted")
+    if path == "naive" and not naive_ok:
+        print(f"bench.py: the align-free path takes at most {mla.NAIVE_MAX_PAIRS} pairs",
+              file=sys.stderr)
+        return 2
+    if path == "with_align" and not wa_ok:
+        print(f"bench.py: fused_moe_lora_with_align takes at most {mla.WITH_ALIGN_MAX_PAIRS} "
+              f"pairs and {mla.WITH_ALIGN_MAX_SLOTS} slots", file=sys.stderr)
+        return 2
+    full_path = path in ("with_align", "sorted")  # steps that produce the align outputs
     naive_fn = lambda ds: run_naive(ds, s, naive_bm, variant)  # noqa: E731
     # the sorted path's step: align + fused_moe_lora, or with --k-split align +
     # fused_moe_lora_ws when its kernel uses a workspace (the decode stream
@@ -443,11 +468,13 @@ def main(argv=None):
     # calls run one after another)
     nbx = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
                                              s.block_m, s.x_per_pair, variant)
-    k_split = args.path == "sorted" and nbx > 0 and args.k_split
+    k_split = path == "sorted" and nbx > 0 and args.k_split
     xws = torch.zeros(nbx, dtype=torch.uint8, device=dev) if nbx > 0 else None
     fused_fn = ((lambda ds: run_fused_ws(ds, s, variant, xws)) if k_split  # noqa: E731
                 else (lambda ds: run_fused(ds, s, variant)))
-    step_fn = naive_fn if args.path == "naive" else (lambda ds: (run_align(ds, s), fused_fn(ds)))
+    wa_fn = lambda ds: run_with_align(ds, s, variant)  # noqa: E731
+    step_fn = {"naive": naive_fn, "with_align": wa_fn}.get(
+        path, lambda ds: (run_align(ds, s), fused_fn(ds)))
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -459,10 +486,14 @@ def main(argv=None):
     log(f"timing {args.steps} steps (one graph)")
     sec_per_step = time_steps_graph(sets, s, variant, args.steps, fn=step_fn)
     log("timing kernels with events")
-    if args.path == "naive":
+    if path == "naive":
         fused_avg = time_kernel_events(sets, s, variant, naive_fn, args.steps)
         align_avg = None
         kbytes = work["naive_bytes"]
+    elif path == "with_align":
+        fused_avg = time_kernel_events(sets, s, variant, wa_fn, args.steps)
+        align_avg = None
+        kbytes = work["with_align_bytes"]
     else:
         fused_avg = time_kernel_events(sets, s, variant, fused_fn, args.steps)
         align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
@@ -470,10 +501,11 @@ def main(argv=None):
 
     gbps = kbytes / (fused_avg * 1e-6) / 1e9
     tflops = work["fused_flops"] / (fused_avg * 1e-6) / 1e12
-    kname = (_kernel_name(s, variant) if args.path == "sorted" else
-             naive_kernel_name(s, naive_bm, variant))
-    traffic, _rec = load_traffic(kname, s.name if args.path == "sorted" else
-                                 f"{s.name}/naive_b{naive_bm}")
+    kname = {"sorted": _kernel_name(s, variant),
+             "with_align": naive_kernel_name(s, s.block_m, variant)}.get(
+        path, naive_kernel_name(s, naive_bm, variant))
+    traffic, _rec = load_traffic(kname, {"sorted": s.name, "with_align": f"{s.name}/with_align"}
+                                 .get(path, f"{s.name}/naive_b{naive_bm}"))
     out = {
         "metric": METRIC,
         "value": round(sec_per_step * 1e6, 3),
@@ -491,10 +523,13 @@ def main(argv=None):
                    "topk": s.topk, "L": s.L, "active_slots": s.active, "r": s.r,
                    "block_m": s.block_m, "mul_routed_weight": s.mul, "add_inputs": s.add,
                    "x_per_pair": s.x_per_pair,
-                   "step": (("moe_lora_align + fused_moe_lora_ws (K split over a block's "
-                             "workgroups)" if k_split else "moe_lora_align + fused_moe_lora")
-                            if args.path == "sorted" else
-                            f"fused_moe_lora_naive (no align step), block_m={naive_bm}"),
+                   "step": {"sorted": ("moe_lora_align + fused_moe_lora_ws (K split over a "
+                                       "block's workgroups)" if k_split else
+                                       "moe_lora_align + fused_moe_lora"),
+                            "with_align": ("fused_moe_lora_with_align (the align outputs and "
+                                           "the fused result in one launch)"),
+                            "naive": f"fused_moe_lora_naive (no align outputs), "
+                                     f"block_m={naive_bm}"}[path],
                    "timing": "one HIP graph of K steps",
                    "cache": ("warm" if args.warm else
                              f"cold: {copies} rotated input copies, "
@@ -509,7 +544,24 @@ def main(argv=None):
         "align_kernel_us_avg": round(align_avg, 3) if align_avg is not None else None,
         "work": work,
     }
-    if args.path == "sorted" and naive_ok and not args.step_only:
+    plain_avg = fused_avg if (path == "sorted" and not k_split) else None
+    if path == "with_align" and not args.step_only:
+        # the same path in two launches: moe_lora_align, then fused_moe_lora
+        log("two launches: align + fused")
+        fn2l = lambda ds: (run_align(ds, s), run_fused(ds, s, variant))  # noqa: E731
+        for i in range(args.warmup):
+            fn2l(sets[i % copies])
+        us2l = time_steps_graph(sets, s, variant, args.steps, fn=fn2l) * 1e6
+        plain_avg = time_kernel_events(sets, s, variant, "fused", args.steps)
+        al2l = time_kernel_events(sets, s, variant, "align", args.steps)
+        g2l = work["fused_bytes"] / (plain_avg * 1e-6) / 1e9
+        out["two_launches"] = {"us_per_call": round(us2l, 3), "kernel": _kernel_name(s, variant),
+                               "kernel_us_avg": round(plain_avg, 3),
+                               "align_kernel_us_avg": round(al2l, 3),
+                               "achieved_GBps": round(g2l, 1),
+                               "frac": round(g2l / HBM_PEAK_GBPS, 4),
+                               "algorithmic_bytes_per_launch": work["fused_bytes"]}
+    if full_path and naive_ok and not args.step_only:
         # the align-free path on the same inputs: no align launch, blocks
         # formed on chip (block_m of the workload, and one pair per block)
         out["align_free"] = []
@@ -527,7 +579,7 @@ def main(argv=None):
                 "kernel_us_avg": round(kus, 3), "achieved_GBps": round(g, 1),
                 "frac": round(g / HBM_PEAK_GBPS, 4),
                 "algorithmic_bytes_per_launch": work["naive_bytes"]})
-    if args.path == "sorted" and nbx > 0 and not args.no_k_split_line:
+    if full_path and nbx > 0 and not args.no_k_split_line:
         # the step the other way: with the K split (fused_moe_lora_ws: the
         # workgroups of a block share A's K range and exchange partial rank
         # vectors) or, when that is the step, without it
@@ -541,12 +593,13 @@ def main(argv=None):
         uso = time_steps_graph(sets, s, variant, args.steps, fn=fno) * 1e6
         kuso = time_kernel_events(sets, s, variant, ofn, args.steps)
         go = work["fused_bytes"] / (kuso * 1e-6) / 1e9
-        kplain, ksplit = (fused_avg, kuso) if other else (kuso, fused_avg)
+        kplain, ksplit = (plain_avg, kuso) if other else (kuso, fused_avg)
         out["with_k_split" if other else "without_k_split"] = {
             "us_per_call": round(uso, 3), "kernel": kname, "kernel_us_avg": round(kuso, 3),
             "achieved_GBps": round(go, 1), "frac": round(go / HBM_PEAK_GBPS, 4),
-            "workspace_bytes": nbx, "k_split_kernel_speedup": round(kplain / ksplit, 3)}
-    if args.path == "sorted" and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
+            "workspace_bytes": nbx,
+            "k_split_kernel_speedup": round(kplain / ksplit, 3) if kplain else None}
+    if full_path and s.r <= mla.TWO_KERNEL_MAX_RANK and not args.no_two_kernel:
         # the two-kernel path on the same inputs (rank vectors through memory):
         # the comparator of the one-shot kernels
         nb = mla.two_kernel_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
@@ -562,8 +615,8 @@ def main(argv=None):
         kus2 = time_kernel_events(sets, s, variant, lambda ds: run_two_kernel(ds, s), args.steps)
         out["two_kernel"] = {"us_per_call": round(us2, 3), "kernels_us_avg": round(kus2, 3),
                              "workspace_bytes": nb,
-                             "one_shot_speedup": round(kus2 / fused_avg, 3)}
-    if args.path == "sorted" and naive_ok and not args.no_dual_stream:
+                             "one_shot_speedup": round(kus2 / (plain_avg or fused_avg), 3)}
+    if full_path and naive_ok and not args.no_dual_stream:
         out["dual_stream"] = dual_stream_line(sets, s, case, args.steps, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")

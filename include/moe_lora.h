@@ -279,6 +279,39 @@ MOE_LORA_API int fused_moe_lora_naive(const uint16_t *x, int32_t x_per_pair,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
                    int32_t block_m, uint16_t *y, int32_t variant, void *stream);
 
+/* Most pairs and slots fused_moe_lora_with_align takes. */
+#define MOE_LORA_WITH_ALIGN_MAX_PAIRS 64
+#define MOE_LORA_WITH_ALIGN_MAX_SLOTS 64
+
+/*
+ * fused_moe_lora_with_align -- the whole path in one launch: the outputs of
+ * moe_lora_align (prhub summary of vLLM PR #42290's align kernel; vLLM PR
+ * #29257, Purpose) and the result of fused_moe_lora for the same inputs, for
+ * decode batches of at most MOE_LORA_WITH_ALIGN_MAX_PAIRS pairs and
+ * MOE_LORA_WITH_ALIGN_MAX_SLOTS slots.  The fused workgroups form their
+ * blocks on chip, as fused_moe_lora_naive does, and one extra workgroup
+ * writes the align outputs beside them (nothing reads them in this call), so
+ * the align costs no launch of its own and no wait.  The outputs are those of
+ * moe_lora_align, bit for bit; y is that of fused_moe_lora_naive with the
+ * same block_m, bit for bit.
+ *   Inputs as moe_lora_align (topk_ids .. block_m) and as fused_moe_lora
+ *   (x .. r, y, variant); outputs sorted_token_ids .. num_active_loras as
+ *   moe_lora_align (lora_ids and num_active_loras may be NULL); no
+ *   workspace.  block_m as moe_lora_align takes it.  MOE_LORA_ERR_UNSUPPORTED
+ *   beyond the pair or slot limit; other statuses as the two calls.  M == 0
+ *   writes the (empty) align outputs and touches no y.
+ */
+MOE_LORA_API int fused_moe_lora_with_align(const int32_t *topk_ids,
+                   const int32_t *token_lora_mapping, int64_t M, int32_t topk,
+                   int32_t E, int32_t L, int32_t block_m,
+                   int32_t *sorted_token_ids, int32_t *expert_ids,
+                   int32_t *num_tokens_post_padded, int32_t *lora_ids,
+                   int32_t *num_active_loras, const uint16_t *x, int32_t x_per_pair,
+                   const uint16_t *lora_a, const uint16_t *lora_b,
+                   const float *topk_weights, int32_t mul_routed_weight,
+                   int32_t add_inputs, int32_t K, int32_t Ns, int32_t S, int32_t r,
+                   uint16_t *y, int32_t variant, void *stream);
+
 /* Largest rank fused_moe_lora_two_kernel takes. */
 #define MOE_LORA_TWO_KERNEL_MAX_RANK 512
 

@@ -35,6 +35,9 @@ SIGNATURES = {
     "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
+    "fused_moe_lora_with_align": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P,
+                                                 _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
+                                                 _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "fused_moe_lora_ws": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                          _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                          _I32, _P, _I64, _I32, _P]),
@@ -56,6 +59,8 @@ SIGNATURES = {
 }
 
 NAIVE_MAX_PAIRS = 1024        # MOE_LORA_NAIVE_MAX_PAIRS
+WITH_ALIGN_MAX_PAIRS = 64     # MOE_LORA_WITH_ALIGN_MAX_PAIRS
+WITH_ALIGN_MAX_SLOTS = 64     # MOE_LORA_WITH_ALIGN_MAX_SLOTS
 TWO_KERNEL_MAX_RANK = 512     # MOE_LORA_TWO_KERNEL_MAX_RANK
 
 
@@ -279,6 +284,35 @@ def fused_moe_lora_ws(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
     if rc != OK:
         raise MoeLoraError(rc, "fused_moe_lora_ws")
     return y
+
+
+def fused_moe_lora_with_align(topk_ids, token_lora_mapping, x, lora_a, lora_b, topk_weights, y,
+                              *, E: int, L: int, block_m: int, mul_routed_weight: bool,
+                              add_inputs: bool, out: "AlignOutput | None" = None,
+                              x_per_pair: bool = False, variant: str | int = "auto",
+                              stream=None) -> "AlignOutput":
+    """moe_lora_align and fused_moe_lora in one launch (at most WITH_ALIGN_MAX_PAIRS pairs
+    and WITH_ALIGN_MAX_SLOTS slots); returns the align outputs; see moe_lora.h."""
+    import torch
+    M, topk, K, Ns, S, E2, L2, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
+    if (E2, L2) != (E, L):
+        raise ValueError("E and L must match lora_a / lora_b")
+    _check(topk_ids, "topk_ids", torch.int32, y.device)
+    _check(token_lora_mapping, "token_lora_mapping", torch.int32, y.device)
+    if tuple(topk_ids.shape) != (M, topk) or tuple(token_lora_mapping.shape) != (M,):
+        raise ValueError("topk_ids must be [M, topk] and token_lora_mapping [M]")
+    if out is None:
+        out = alloc_align_output(M, topk, E, L, block_m, y.device)
+    rc = lib().fused_moe_lora_with_align(
+        _dptr(topk_ids), _dptr(token_lora_mapping), M, topk, E, L, block_m,
+        _dptr(out.sorted_token_ids), _dptr(out.expert_ids), _dptr(out.num_tokens_post_padded),
+        _dptr(out.lora_ids), _dptr(out.num_active_loras), _dptr(x), int(bool(x_per_pair)),
+        _dptr(lora_a), _dptr(lora_b), _dptr(topk_weights), int(bool(mul_routed_weight)),
+        int(bool(add_inputs)), K, Ns, S, r, _dptr(y),
+        VARIANTS[variant] if isinstance(variant, str) else int(variant), _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "fused_moe_lora_with_align")
+    return out
 
 
 def fused_moe_lora_naive(x, lora_a, lora_b, topk_ids, token_lora_mapping, topk_weights, y, *,

@@ -16,6 +16,7 @@
 // the key bits (no atomics decide an order).
 #include <algorithm>
 
+#include "align_wave.h"
 #include "common.h"
 #include "internal.h"
 
@@ -124,63 +125,8 @@ __device__ void layout_groups(const AlignParams& a, const int* tot, int* off, in
 }
 
 // ---------------------------------------------------------------- one wavefront
-// At most 64 pairs and 64 slots (decode batches): lane = pair.  Equal keys
-// are found by voting on the key bits; a group's start in its slot is the sum
-// of the padded sizes of the same slot's groups with smaller keys (their
-// leaders are read lane by lane), a pair's place is that start plus the
-// number of lower lanes with its key.  Everything stays in registers: no LDS,
-// no barrier, one round trip to read the routing.
-constexpr int kWaveMaxPairs = kWave;
-constexpr int kWaveMaxSlots = kWave;
-
-__global__ void __launch_bounds__(kWave) align_wave_kernel(AlignParams a) {
-  const int lane = lane_id();
-  int l = -1, e = -1;
-  if (lane < a.numel) {  // both loads issued before either is used
-    l = a.mapping[lane / a.topk];
-    e = a.topk_ids[lane];
-  }
-  const bool ok = (unsigned(l) < unsigned(a.L)) & (unsigned(e) < unsigned(a.E));
-  const int key = ok ? l * a.E + e : -1;
-  const int slot = ok ? l : -1;
-  const uint64_t peers = match_key(key, __ballot(ok), a.nbits);
-  const bool lead = ok && (peers & lanes_below(lane)) == 0;
-  const int cnt = ok ? __popcll(peers) : 0;
-  const int pad = lead ? (cnt + a.B - 1) / a.B * a.B : 0;  // 0 unless this lane leads a group
-  int off = 0;
-  for (int j = 0; j < kWave; ++j) {
-    const int kj = __builtin_amdgcn_readlane(key, j);
-    const int sj = __builtin_amdgcn_readlane(slot, j);
-    const int pj = __builtin_amdgcn_readlane(pad, j);
-    off += (sj == slot && kj < key) ? pj : 0;
-  }
-  if (ok) {
-    const int goff = __shfl(off, __builtin_ctzll(peers));
-    a.sorted[l * a.cap + goff + __popcll(peers & lanes_below(lane))] = lane;
-  }
-  if (lead) {  // the group's expert ids and padding sentinels
-    int32_t* erow = a.eids + l * a.nb + off / a.B;
-    for (int b = 0; b < pad / a.B; ++b) erow[b] = e;
-    int32_t* srow = a.sorted + l * a.cap + off;
-    for (int i = cnt; i < pad; ++i) srow[i] = a.numel;
-  }
-  // lane = slot: padded total, the active list and its count
-  int tot = 0;
-  for (int j = 0; j < kWave; ++j) {
-    const int sj = __builtin_amdgcn_readlane(slot, j);
-    const int pj = __builtin_amdgcn_readlane(pad, j);
-    tot += sj == lane ? pj : 0;
-  }
-  const bool in = lane < a.L;
-  if (in) a.ntpp[lane] = tot;
-  const uint64_t act = __ballot(in && tot > 0);
-  const int nact = __popcll(act);
-  if (a.lora_ids) {  // entries [0, nact) get the active slots, [nact, L) get -1: disjoint stores
-    if (in && tot > 0) a.lora_ids[__popcll(act & lanes_below(lane))] = lane;
-    if (in && lane >= nact) a.lora_ids[lane] = -1;
-  }
-  if (a.nact && lane == 0) *a.nact = nact;
-}
+// (align_wave.h)
+__global__ void __launch_bounds__(kWave) align_wave_kernel(AlignParams a) { align_wave_body(a); }
 
 // ---------------------------------------------------------------- one workgroup
 __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
@@ -296,7 +242,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   (void)B;
   AlignPlan pl{};
-  if (numel <= kWaveMaxPairs && L <= kWaveMaxSlots) {
+  if (numel <= kAlignWaveMaxPairs && L <= kAlignWaveMaxSlots) {
     pl.wave = true;
     pl.threads = kWave;
     return pl;

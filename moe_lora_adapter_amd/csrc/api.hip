@@ -282,12 +282,20 @@ int fused_moe_lora_ws(const uint16_t* x, int32_t x_per_pair, const uint16_t* lor
                       need > 0 ? static_cast<int32_t*>(workspace) : nullptr, peer_wait, stream);
 }
 
-int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
-                         const uint16_t* lora_b, const int32_t* topk_ids,
-                         const int32_t* token_lora_mapping, const float* topk_weights,
-                         int32_t mul_routed_weight, int32_t add_inputs, int64_t M, int32_t topk,
-                         int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
-                         int32_t block_m, uint16_t* y, int32_t variant, void* stream) {
+static_assert(kAlignWaveMaxPairs == MOE_LORA_WITH_ALIGN_MAX_PAIRS &&
+                  kAlignWaveMaxSlots == MOE_LORA_WITH_ALIGN_MAX_SLOTS,
+              "the header's limits are the one-wavefront align's");
+
+// The align-free launch shared by fused_moe_lora_naive and
+// fused_moe_lora_with_align (al: the align outputs of the extra workgroup,
+// or null); sizes and pointers of the fused part are checked here.
+static int naive_launch(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                        const uint16_t* lora_b, const int32_t* topk_ids,
+                        const int32_t* token_lora_mapping, const float* topk_weights,
+                        int32_t mul_routed_weight, int32_t add_inputs, int64_t M, int32_t topk,
+                        int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                        int32_t block_m, uint16_t* y, int32_t variant, const AlignParams* al,
+                        void* stream) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap, true);
   if (rc != MOE_LORA_OK) return rc;
@@ -334,11 +342,70 @@ int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* 
   p.xcd_cus = xcd_compute_units();
   p.naive = 1;
   p.nbits = nbits_for(int64_t(L) * E);
+  if (al) {
+    p.al_sorted = al->sorted;
+    p.al_eids = al->eids;
+    p.al_ntpp = al->ntpp;
+    p.al_lora_ids = al->lora_ids;
+    p.al_nact = al->nact;
+    p.cap = al->cap;
+    p.nb = al->nb;
+  }
   const bool use_mfma =
       pick_variant(M, numel, K, Ns, N, E, L, r, block_m, x_per_pair, variant) == MOE_LORA_VARIANT_MFMA;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = use_mfma ? launch_fused_mfma(p, st) : launch_fused_valu(p, st);
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+int fused_moe_lora_naive(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
+                         const uint16_t* lora_b, const int32_t* topk_ids,
+                         const int32_t* token_lora_mapping, const float* topk_weights,
+                         int32_t mul_routed_weight, int32_t add_inputs, int64_t M, int32_t topk,
+                         int32_t K, int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
+                         int32_t block_m, uint16_t* y, int32_t variant, void* stream) {
+  return naive_launch(x, x_per_pair, lora_a, lora_b, topk_ids, token_lora_mapping, topk_weights,
+                      mul_routed_weight, add_inputs, M, topk, K, Ns, S, E, L, r, block_m, y,
+                      variant, nullptr, stream);
+}
+
+int fused_moe_lora_with_align(const int32_t* topk_ids, const int32_t* token_lora_mapping,
+                              int64_t M, int32_t topk, int32_t E, int32_t L, int32_t block_m,
+                              int32_t* sorted_token_ids, int32_t* expert_ids,
+                              int32_t* num_tokens_post_padded, int32_t* lora_ids,
+                              int32_t* num_active_loras, const uint16_t* x, int32_t x_per_pair,
+                              const uint16_t* lora_a, const uint16_t* lora_b,
+                              const float* topk_weights, int32_t mul_routed_weight,
+                              int32_t add_inputs, int32_t K, int32_t Ns, int32_t S, int32_t r,
+                              uint16_t* y, int32_t variant, void* stream) {
+  // the align step's own rules (block_m as moe_lora_align takes it), then the
+  // one-wavefront limits of the align that rides along
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  if (numel > kAlignWaveMaxPairs || L > kAlignWaveMaxSlots) return MOE_LORA_ERR_UNSUPPORTED;
+  if (!num_tokens_post_padded) return MOE_LORA_ERR_INVALID;
+  if (numel > 0 && (!sorted_token_ids || !expert_ids)) return MOE_LORA_ERR_INVALID;
+  // the fused part's checks, without a launch (the pointers too)
+  const int vrc = fused_moe_lora_variant(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
+  if (vrc < 0) return vrc;
+  if ((mul_routed_weight != 0 && mul_routed_weight != 1) || (add_inputs != 0 && add_inputs != 1))
+    return MOE_LORA_ERR_INVALID;
+  if (numel == 0)  // no fused work: the align alone writes the (empty) outputs
+    return moe_lora_align(topk_ids, token_lora_mapping, M, topk, E, L, block_m, sorted_token_ids,
+                          expert_ids, num_tokens_post_padded, lora_ids, num_active_loras, nullptr,
+                          0, stream);
+  AlignParams al{};
+  al.sorted = sorted_token_ids;
+  al.eids = expert_ids;
+  al.ntpp = num_tokens_post_padded;
+  al.lora_ids = lora_ids;
+  al.nact = num_active_loras;
+  al.cap = int32_t(cap);
+  al.nb = int32_t(cap / block_m);
+  return naive_launch(x, x_per_pair, lora_a, lora_b, topk_ids, token_lora_mapping, topk_weights,
+                      mul_routed_weight, add_inputs, M, topk, K, Ns, S, E, L, r, block_m, y,
+                      variant, &al, stream);
 }
 
 }  // extern "C"

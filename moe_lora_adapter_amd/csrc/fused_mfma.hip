@@ -40,6 +40,7 @@
 #include "blocks.h"
 #include "common.h"
 #include "dma.h"
+#include "align_wave.h"
 #include "groups.h"
 #include "internal.h"
 
@@ -475,6 +476,9 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   __shared__ int s_ids[NAIVE ? kMaxIdsM : 1];  // pair ids of the block (align-free path)
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
+  if constexpr (NAIVE) {
+    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
+  }
   // units = (block, slice); the split count gives every working workgroup a
   // slot (MLR_MFMA_OCCUPANCY per compute unit), at least MLR_MFMA_MIN_COLS
   // columns each
@@ -571,7 +575,7 @@ hipError_t launch_fused_mfma(FusedParams p, hipStream_t st) {
   // the kernel keeps within xcd_cus * MLR_MFMA_OCCUPANCY slots per XCD
   const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
   const int64_t slots = std::max<int64_t>(per_xcd, int64_t(p.xcd_cus) * MLR_MFMA_OCCUPANCY);
-  const dim3 grid(unsigned(kXcds * slots));
+  const dim3 grid(unsigned(kXcds * slots + (p.al_sorted ? 1 : 0)));  // + the align workgroup
 #define MLR_MFMA_CASE(RT_)                                                                       \
   case RT_:                                                                                      \
     if (p.naive) hipLaunchKernelGGL((fused_mfma_kernel<RT_, true>), grid, dim3(kThreadsM), 0, st, p); \

@@ -45,6 +45,7 @@
 #include "blocks.h"
 #include "common.h"
 #include "dma.h"
+#include "align_wave.h"
 #include "groups.h"
 #include "internal.h"
 
@@ -410,6 +411,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
+  if constexpr (NAIVE) {
+    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
+  }
   // units = (block, slice); split count: a compute unit per working
   // workgroup, at least MLR_STREAM_MIN_COLS and at most kMaxCols columns each
   GroupLds& gl = *reinterpret_cast<GroupLds*>(ring);  // free until the first stage is loaded
@@ -659,7 +663,7 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
   const int64_t need = (p.Ns + kMaxCols - 1) / kMaxCols;
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
-  const dim3 grid(unsigned(kXcds * slots));
+  const dim3 grid(unsigned(kXcds * slots + (p.al_sorted ? 1 : 0)));  // + the align workgroup
 #define MLR_STREAM_CASE(R_)                                                                  \
   case R_:                                                                                   \
     if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false>), grid, dim3(kST), 0, st, p); \

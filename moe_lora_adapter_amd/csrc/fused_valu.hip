@@ -30,6 +30,7 @@
 
 #include "blocks.h"
 #include "common.h"
+#include "align_wave.h"
 #include "groups.h"
 #include "internal.h"
 
@@ -336,6 +337,9 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
   __shared__ __align__(16) uint8_t s_grp[NAIVE ? sizeof(GroupLds) : 1];
   GroupLds& gl = *reinterpret_cast<GroupLds*>(s_grp);
+  if constexpr (NAIVE) {
+    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
+  }
 
   // The blocks present decide the split count: as many column splits (of at
   // least MLR_VALU_MIN_COLS columns) as give every working workgroup a compute
@@ -423,7 +427,8 @@ hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
   // grid: covers split * u8 + unit for every split count the kernel can pick:
   // u8 <= units_pad with one split, and n_split * u8 <= 8 * xcd_cus * OCC with more.
   const int64_t units_pad = (int64_t(p.units) + kXcds - 1) / kXcds * kXcds;
-  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus * MLR_VALU_OCC);
+  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus * MLR_VALU_OCC) +
+                       (p.al_sorted ? 1 : 0);  // the align workgroup, last
   const int cpr = (p.r % 8 == 0 && ((p.r / 8) & (p.r / 8 - 1)) == 0) ? p.r / 8 : 0;
 #define MLR_CASE(JW_, CPR_) \
   if (jw == JW_ && cpr == CPR_) { launch<JW_, CPR_>(p, sh, dim3(unsigned(grid)), st); return hipGetLastError(); }

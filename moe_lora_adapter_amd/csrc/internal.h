@@ -35,6 +35,10 @@ struct AlignPlan {
   int64_t ws_bytes;  // device workspace (0 for the single path)
 };
 
+// The one-wavefront align (lane = pair, lane = slot) takes at most this many.
+constexpr int kAlignWaveMaxPairs = 64;
+constexpr int kAlignWaveMaxSlots = 64;
+
 AlignPlan plan_align(int64_t numel, int E, int L, int B);
 hipError_t launch_align(const AlignPlan& plan, const AlignParams& a, hipStream_t st);
 
@@ -57,6 +61,13 @@ struct FusedParams {
   int32_t xcd_cus;     // compute units per XCD of the current device
   int32_t naive;       // 1: blocks formed on chip from topk_ids and mapping (no align outputs)
   int32_t nbits;       // align-free path: bits of a key l * E + e
+  // fused_moe_lora_with_align: the align outputs one extra workgroup (the
+  // last) writes beside the fused work; null when there is none
+  int32_t* al_sorted;
+  int32_t* al_eids;
+  int32_t* al_ntpp;
+  int32_t* al_lora_ids;
+  int32_t* al_nact;
   int32_t* xch;        // stream kernel: K-split exchange area, zero between calls (null: none)
   int32_t xch_passes;  // stream kernel: passes per block the exchange area holds
   int32_t peer_wait;   // stream kernel: polls for a peer's partial before computing it here

@@ -216,6 +216,36 @@ def test_naive_binding_checks_before_calling():
                                  mul_routed_weight=False, add_inputs=True)
 
 
+def wa_call(**kw):
+    a = dict(ids=P16, mp=P16, M=16, topk=4, E=32, L=6, B=16, sorted=P16, eids=P16, ntpp=P16,
+             lids=P16, nact=P16, x=P16, xpp=0, la=P16, lb=P16, w=None, mul=0, add=1, K=2880,
+             Ns=2880, S=2, r=64, y=P16, variant=0)
+    a.update(kw)
+    return mla.lib().fused_moe_lora_with_align(
+        a["ids"], a["mp"], a["M"], a["topk"], a["E"], a["L"], a["B"], a["sorted"], a["eids"],
+        a["ntpp"], a["lids"], a["nact"], a["x"], a["xpp"], a["la"], a["lb"], a["w"], a["mul"],
+        a["add"], a["K"], a["Ns"], a["S"], a["r"], a["y"], a["variant"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=17), mla.ERR_UNSUPPORTED),            # 68 pairs: beyond the one-wavefront align
+    (dict(L=65, E=2), mla.ERR_UNSUPPORTED),       # 65 slots
+    (dict(B=8), mla.ERR_UNSUPPORTED),             # block_m as moe_lora_align takes it
+    (dict(ntpp=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(x=None), mla.ERR_INVALID),
+    (dict(ids=None), mla.ERR_INVALID),
+    (dict(y=V(18)), mla.ERR_INVALID),
+    (dict(mul=1, w=None), mla.ERR_INVALID),
+    (dict(mul=2), mla.ERR_INVALID),
+    (dict(K=2884), mla.ERR_INVALID),
+    (dict(r=129), mla.ERR_UNSUPPORTED),
+    (dict(variant=5), mla.ERR_INVALID),
+])
+def test_with_align_rejects(kw, status):
+    assert wa_call(**kw) == status
+
+
 def ws_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
