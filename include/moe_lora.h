@@ -289,9 +289,9 @@ MOE_LORA_API int fused_moe_lora_naive(const uint16_t *x, int32_t x_per_pair,
  * #29257, Purpose) and the result of fused_moe_lora for the same inputs, for
  * decode batches of at most MOE_LORA_WITH_ALIGN_MAX_PAIRS pairs and
  * MOE_LORA_WITH_ALIGN_MAX_SLOTS slots.  The fused workgroups form their
- * blocks on chip, as fused_moe_lora_naive does, and one extra workgroup
- * writes the align outputs beside them (nothing reads them in this call), so
- * the align costs no launch of its own and no wait.  The outputs are those of
+ * blocks on chip, as fused_moe_lora_naive does, and one workgroup the
+ * fused work leaves idle writes the align outputs beside them (nothing reads
+ * them in this call), so the align costs no launch of its own and no wait.  The outputs are those of
  * moe_lora_align, bit for bit; y is that of fused_moe_lora_naive with the
  * same block_m, bit for bit.
  *   Inputs as moe_lora_align (topk_ids .. block_m) and as fused_moe_lora

@@ -2,6 +2,8 @@
 // that run it beside their own work (fused_moe_lora_with_align).
 #pragma once
 
+#include <limits.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -64,13 +66,20 @@ __device__ __forceinline__ void align_wave_body(const AlignParams& a) {
   if (a.nact && lane == 0) *a.nact = nact;
 }
 
-// The extra workgroup of a fused kernel launched by fused_moe_lora_with_align
-// (the last one) writes the align outputs with its first wavefront and does
-// nothing else; the fused workgroups form their blocks on chip and never read
-// these outputs, so the two run side by side.  Returns true in that
-// workgroup (every thread of it, before any barrier).
-__device__ __forceinline__ bool side_align(const FusedParams& p) {
-  if (p.al_sorted == nullptr || blockIdx.x != gridDim.x - 1) return false;
+// fused_moe_lora_with_align: one workgroup of the fused kernel writes the
+// align outputs with its first wavefront; the fused workgroups form their
+// blocks on chip and never read those outputs, so the two run side by side.
+// The align goes to the first workgroup the unit mapping leaves without work,
+// `idle`, which then does nothing else; when every workgroup has work (idle
+// is past the grid) workgroup 0 runs it before its own.  (A workgroup added
+// to the launch for it was dispatched after all others and, on a full XCD,
+// waited for a compute unit to free up: +2 to +5 us.)  Returns true when this
+// workgroup has no fused work left (every thread of it: the caller returns
+// before any barrier).
+__device__ __forceinline__ bool side_align(const FusedParams& p, int idle) {
+  if (p.al_sorted == nullptr) return false;
+  const bool spare = idle < int(gridDim.x);
+  if (int(blockIdx.x) != (spare ? idle : 0)) return false;
   if (threadIdx.x < kWave) {
     AlignParams a{};
     a.topk_ids = p.topk_ids;
@@ -91,7 +100,18 @@ __device__ __forceinline__ bool side_align(const FusedParams& p) {
     a.nb = p.nb;
     align_wave_body(a);
   }
-  return true;
+  return spare;
+}
+
+// The first workgroup index map_unit_xcd leaves without a unit: in XCD x the
+// indices x + 8 slot with slot >= (units of x) * n_split have none.
+__device__ __forceinline__ int first_idle_xcd(int units, int n_split) {
+  int best = INT_MAX;
+  for (int x = 0; x < kXcds; ++x) {
+    const int lo = int(int64_t(x) * units / kXcds), hi = int(int64_t(x + 1) * units / kXcds);
+    best = min(best, (hi - lo) * n_split * kXcds + x);
+  }
+  return best;
 }
 
 }  // namespace mlr

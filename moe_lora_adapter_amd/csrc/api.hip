@@ -287,7 +287,7 @@ static_assert(kAlignWaveMaxPairs == MOE_LORA_WITH_ALIGN_MAX_PAIRS &&
               "the header's limits are the one-wavefront align's");
 
 // The align-free launch shared by fused_moe_lora_naive and
-// fused_moe_lora_with_align (al: the align outputs of the extra workgroup,
+// fused_moe_lora_with_align (al: the align outputs one workgroup writes,
 // or null); sizes and pointers of the fused part are checked here.
 static int naive_launch(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
                         const uint16_t* lora_b, const int32_t* topk_ids,

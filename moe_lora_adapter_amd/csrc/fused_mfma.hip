@@ -476,9 +476,6 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   __shared__ int s_ids[NAIVE ? kMaxIdsM : 1];  // pair ids of the block (align-free path)
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
-  if constexpr (NAIVE) {
-    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
-  }
   // units = (block, slice); the split count gives every working workgroup a
   // slot (MLR_MFMA_OCCUPANCY per compute unit), at least MLR_MFMA_MIN_COLS
   // columns each
@@ -496,6 +493,9 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
   const int n_split = min(max_split, max(1, p.xcd_cus * MLR_MFMA_OCCUPANCY / max(per_xcd, 1)));
+  if constexpr (NAIVE) {  // fused_moe_lora_with_align: the align outputs
+    if (side_align(p, first_idle_xcd(units, n_split))) return;
+  }
   int unit, split;
   if (!map_unit_xcd(blockIdx.x, units, n_split, unit, split)) return;
   const int nsz = ((p.Ns + n_split - 1) / n_split + 15) / 16 * 16;
@@ -575,7 +575,7 @@ hipError_t launch_fused_mfma(FusedParams p, hipStream_t st) {
   // the kernel keeps within xcd_cus * MLR_MFMA_OCCUPANCY slots per XCD
   const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
   const int64_t slots = std::max<int64_t>(per_xcd, int64_t(p.xcd_cus) * MLR_MFMA_OCCUPANCY);
-  const dim3 grid(unsigned(kXcds * slots + (p.al_sorted ? 1 : 0)));  // + the align workgroup
+  const dim3 grid(unsigned(kXcds * slots));
 #define MLR_MFMA_CASE(RT_)                                                                       \
   case RT_:                                                                                      \
     if (p.naive) hipLaunchKernelGGL((fused_mfma_kernel<RT_, true>), grid, dim3(kThreadsM), 0, st, p); \

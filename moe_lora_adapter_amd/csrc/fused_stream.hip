@@ -411,9 +411,6 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
-  if constexpr (NAIVE) {
-    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
-  }
   // units = (block, slice); split count: a compute unit per working
   // workgroup, at least MLR_STREAM_MIN_COLS and at most kMaxCols columns each
   GroupLds& gl = *reinterpret_cast<GroupLds*>(ring);  // free until the first stage is loaded
@@ -431,6 +428,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const int need = (p.Ns + kMaxCols - 1) / kMaxCols;
   const int max_split = max(need, p.Ns / MLR_STREAM_MIN_COLS);
   const int n_split = min(max_split, max(need, p.xcd_cus / max(per_xcd, 1)));
+  if constexpr (NAIVE) {  // fused_moe_lora_with_align: the align outputs
+    if (side_align(p, first_idle_xcd(units, n_split))) return;
+  }
   int unit, split;
   if (!map_unit_xcd(blockIdx.x, units, n_split, unit, split)) return;
   const int nsz = ((p.Ns + n_split - 1) / n_split + 7) / 8 * 8;
@@ -663,7 +663,7 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t per_xcd = (int64_t(p.units) + kXcds - 1) / kXcds;
   const int64_t need = (p.Ns + kMaxCols - 1) / kMaxCols;
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
-  const dim3 grid(unsigned(kXcds * slots + (p.al_sorted ? 1 : 0)));  // + the align workgroup
+  const dim3 grid(unsigned(kXcds * slots));
 #define MLR_STREAM_CASE(R_)                                                                  \
   case R_:                                                                                   \
     if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false>), grid, dim3(kST), 0, st, p); \

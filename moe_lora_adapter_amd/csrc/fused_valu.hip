@@ -337,9 +337,6 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
   __shared__ __align__(16) uint8_t s_grp[NAIVE ? sizeof(GroupLds) : 1];
   GroupLds& gl = *reinterpret_cast<GroupLds*>(s_grp);
-  if constexpr (NAIVE) {
-    if (side_align(p)) return;  // fused_moe_lora_with_align: the align outputs
-  }
 
   // The blocks present decide the split count: as many column splits (of at
   // least MLR_VALU_MIN_COLS columns) as give every working workgroup a compute
@@ -360,6 +357,10 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   const int u8 = per_xcd * kXcds;
   const int max_split = max(1, p.Ns / MLR_VALU_MIN_COLS);
   const int n_split = min(max_split, max(1, p.xcd_cus * MLR_VALU_OCC / max(per_xcd, 1)));
+  if constexpr (NAIVE) {  // fused_moe_lora_with_align: the align outputs (the first
+    // index with no unit: unit `units` of split 0, else split n_split's first)
+    if (side_align(p, units < u8 ? units : n_split * u8)) return;
+  }
   // workgroup -> (split, unit), split-major; equal unit residue mod 8 = same XCD
   const int id = blockIdx.x;
   const int split = id / max(u8, 1), unit = id - split * u8;
@@ -427,8 +428,7 @@ hipError_t launch_fused_valu(FusedParams p, hipStream_t st) {
   // grid: covers split * u8 + unit for every split count the kernel can pick:
   // u8 <= units_pad with one split, and n_split * u8 <= 8 * xcd_cus * OCC with more.
   const int64_t units_pad = (int64_t(p.units) + kXcds - 1) / kXcds * kXcds;
-  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus * MLR_VALU_OCC) +
-                       (p.al_sorted ? 1 : 0);  // the align workgroup, last
+  const int64_t grid = std::max<int64_t>(units_pad, int64_t(kXcds) * p.xcd_cus * MLR_VALU_OCC);
   const int cpr = (p.r % 8 == 0 && ((p.r / 8) & (p.r / 8 - 1)) == 0) ? p.r / 8 : 0;
 #define MLR_CASE(JW_, CPR_) \
   if (jw == JW_ && cpr == CPR_) { launch<JW_, CPR_>(p, sh, dim3(unsigned(grid)), st); return hipGetLastError(); }

@@ -61,8 +61,8 @@ struct FusedParams {
   int32_t xcd_cus;     // compute units per XCD of the current device
   int32_t naive;       // 1: blocks formed on chip from topk_ids and mapping (no align outputs)
   int32_t nbits;       // align-free path: bits of a key l * E + e
-  // fused_moe_lora_with_align: the align outputs one extra workgroup (the
-  // last) writes beside the fused work; null when there is none
+  // fused_moe_lora_with_align: the align outputs one workgroup writes
+  // beside the fused work; null when there is none
   int32_t* al_sorted;
   int32_t* al_eids;
   int32_t* al_ntpp;
