@@ -169,3 +169,26 @@ def test_with_align_one_graph_across_active_counts(orc):
         ref = orc.fused(c.x, a_host, b_host, c.topk_ids, m, c.topk_weights, c.y_in, s.mul, s.add,
                         x_per_pair=s.x_per_pair)
         gh.assert_fused_close(gh.bf16_host_f64(y).reshape(s.numel, s.N), ref, f"graph/{n_active}")
+
+
+@pytest.mark.parametrize("variant", ["valu", "auto"])
+def test_with_align_no_spare_workgroup(orc, variant):
+    """64 pairs on 64 distinct experts over 4 slices: 256 (block, slice) units,
+    one per workgroup of a 256-workgroup grid, so no workgroup is left spare and
+    workgroup 0 runs the align before its own unit."""
+    s = synth.shape("tiny", dist="stress", seed=9950, M=16, topk=4, E=64, L=1, active=1,
+                    S=4, K=256, Ns=256, r=64, block_m=16, p_neg=0.0)
+    c = synth.draw(s)
+    c.topk_ids[:] = np.arange(s.numel, dtype=np.int32).reshape(s.M, s.topk)
+    c.token_lora_mapping[:] = 0
+    _log(f"with-align, no spare workgroup, {variant}")
+    dc = gh.DeviceCase(c)
+    out, y = _with_align(dc, variant)
+    ref_al = orc.align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m)
+    gh.assert_align_equal(gh.align_to_host(out), ref_al, s.block_m)
+    assert int(out.num_tokens_post_padded.cpu().numpy()[0]) == 64 * s.block_m
+    y_naive = dc.naive(block_m=s.block_m, variant=variant)
+    assert torch.equal(y.view(torch.int16), y_naive.view(torch.int16))
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+    gh.assert_fused_close(gh.bf16_host_f64(y).reshape(s.numel, s.N), ref, f"no spare/{variant}")
