@@ -164,6 +164,15 @@ def run_naive(ds, s, block_m, variant):
                              x_per_pair=s.x_per_pair, variant=variant)
 
 
+def resolve_path(requested, s):
+    """The step --path names; "auto": one launch (fused_moe_lora_with_align)
+    where the batch allows it, else align + fused."""
+    if requested != "auto":
+        return requested
+    wa_ok = s.numel <= 64 and s.L <= 64  # MOE_LORA_WITH_ALIGN_MAX_PAIRS / _SLOTS
+    return "with_align" if wa_ok else "sorted"
+
+
 def run_with_align(ds, s, variant):
     """fused_moe_lora_with_align: the align outputs and the fused result in one launch."""
     import moe_lora_adapter_amd as mla
@@ -451,7 +460,7 @@ def main(argv=None):
     naive_ok = s.numel <= mla.NAIVE_MAX_PAIRS
     wa_ok = s.numel <= mla.WITH_ALIGN_MAX_PAIRS and s.L <= mla.WITH_ALIGN_MAX_SLOTS
     naive_bm = args.naive_block_m or s.block_m
-    path = args.path if args.path != "auto" else ("with_align" if wa_ok else "sorted")
+    path = resolve_path(args.path, s)
     if path == "naive" and not naive_ok:
         print(f"bench.py: the align-free path takes at most {mla.NAIVE_MAX_PAIRS} pairs",
               file=sys.stderr)

@@ -69,3 +69,18 @@ def test_cpu_baseline_leg_reports_the_oracle():
     assert out["kind"] == "oracle" and out["unit"] == "us/call"
     assert out["value"] > 0 and out["cores"] >= 1
     assert out["value"] == pytest.approx(out["align_us"] + out["fused_us"], abs=0.2)
+
+
+def test_step_path_resolution():
+    """--path auto times the whole path in one launch for decode batches (at
+    most 64 pairs and slots) and as align + fused otherwise; the limits are the
+    library's."""
+    import moe_lora_adapter_amd as mla
+    assert (mla.WITH_ALIGN_MAX_PAIRS, mla.WITH_ALIGN_MAX_SLOTS) == (64, 64)
+    for name, want in [("oss20b_decode_w13_a6", "with_align"), ("oss120b_decode_w13", "with_align"),
+                       ("tiny", "with_align"), ("qwen3_prefill", "sorted"),
+                       ("oss120b_prefill_w13", "sorted"), ("dense_qkv", "sorted")]:
+        assert bench.resolve_path("auto", synth.shape(name)) == want, name
+    assert bench.resolve_path("auto", synth.shape("tiny", M=17, topk=4)) == "sorted"  # 68 pairs
+    assert bench.resolve_path("auto", synth.shape("tiny", L=65, E=2, active=2)) == "sorted"
+    assert bench.resolve_path("sorted", synth.shape("tiny")) == "sorted"
