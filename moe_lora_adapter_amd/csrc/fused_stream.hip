@@ -479,6 +479,12 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a + wsel * R * p.K, uint32_t(R * p.K * 2));
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
+  // The first pass's first A stage loads while the pass is set up: it needs
+  // only the expert and the ring (whose grouping tables are done with).  The
+  // pass then issues X, Y and the later stages, so the first wait still finds
+  // exactly one stage issued after the one it waits for.
+  if (TA > 0) issue_stage<R>(p, ar, br, 0, nA, ka0, ncols, ring_lds);
+
   for (int g0 = 0; g0 < p.B; g0 += kRows) {
     const XchSlot xs_slot = xch ? xch_slot<R>(p, unit * p.xch_passes + g0 / kRows) : XchSlot{};
     if (xch && tid == 0)
@@ -501,7 +507,10 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = s_vl[i] = 0;
     // valid rows are a prefix of the block (sentinels only pad a group's end)
     const int nr = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kRows && s_row[tid] >= 0));
-    if (nr == 0) break;
+    if (nr == 0) {  // (a block's first pass always has a row: only later passes end here)
+      stage_barrier<0>();
+      break;
+    }
 
     // X rows (row stride K / 8 chunks) and the split's Y values (row stride
     // ncols / 8 chunks) into LDS: 64 chunks per instruction, only
@@ -520,7 +529,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
                                ? uint32_t(int64_t(pid) * p.N + 8 * c) * 2u : kOob;
       dma16(yr, ys_lds + q0 * 16, off);
     }
-    for (int t = 0; t < kSlots - 1 && t < TA; ++t)
+    for (int t = g0 == 0 ? 1 : 0; t < kSlots - 1 && t < TA; ++t)
       issue_stage<R>(p, ar, br, t, nA, ka0, ncols, ring_lds + t * kStage);
 
     // wavefront w: A rank tile rt and k-step ka of every A stage
