@@ -43,6 +43,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -63,21 +64,41 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-# The sources each fused kernel is built from (its own file, the shared
-# device headers and the host code that sizes its launch); counters recorded
-# for a kernel stay valid while these are unchanged.
+# The sources each fused kernel is built from: its own file, the file that
+# sizes and issues its launch, the host entry points, and every header these
+# include (followed through the headers' own includes).  Counters recorded for
+# a kernel stay valid while these are unchanged.
 KERNEL_SOURCES = {
-    "fused_stream_kernel": ["fused_stream.hip", "fused_valu.hip", "groups.h"],
-    "fused_valu_kernel": ["fused_valu.hip", "groups.h"],
+    "fused_stream_kernel": ["fused_stream.hip", "fused_valu.hip"],
+    "fused_valu_kernel": ["fused_valu.hip"],
     "fused_mfma_kernel": ["fused_mfma.hip"],
 }
-SHARED_SOURCES = ["api.hip", "blocks.h", "common.h", "dma.h", "internal.h"]
+SHARED_SOURCES = ["api.hip"]
+_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def kernel_source_files(kernel: str) -> list:
+    """KERNEL_SOURCES[kernel] + SHARED_SOURCES and their included files,
+    as paths relative to the package's csrc directory."""
+    csrc = os.path.join(ROOT, "moe_lora_adapter_amd", "csrc")
+    todo = list(KERNEL_SOURCES[kernel] + SHARED_SOURCES)
+    seen = set()
+    while todo:
+        f = os.path.normpath(todo.pop())
+        if f in seen:
+            continue
+        seen.add(f)
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        base = os.path.dirname(f)
+        todo += [os.path.join(base, inc) for inc in _INCLUDE.findall(text)]
+    return sorted(seen)
 
 
 def kernel_sources_sha(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_lora_adapter_amd", "csrc")
-    for f in sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES):
+    for f in kernel_source_files(kernel):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

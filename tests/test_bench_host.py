@@ -2,6 +2,7 @@
 computed from, the one-GPU rule, the traffic records, the CPU baseline leg."""
 import json
 import os
+import re
 
 import numpy as np
 import pytest
@@ -50,7 +51,7 @@ def test_more_than_one_gpu_is_refused(capsys):
 
 def test_traffic_record_goes_stale_with_the_kernel_sources(tmp_path, monkeypatch):
     for kernel in bench.KERNEL_SOURCES:
-        for f in bench.KERNEL_SOURCES[kernel] + bench.SHARED_SOURCES:
+        for f in bench.kernel_source_files(kernel):
             assert os.path.exists(os.path.join(bench.ROOT, "moe_lora_adapter_amd", "csrc", f)), f
     rec = {"fused_stream_kernel/w": {"src_sha": bench.kernel_sources_sha("fused_stream_kernel"),
                                      "traffic_bytes_per_launch": 123},
@@ -61,6 +62,21 @@ def test_traffic_record_goes_stale_with_the_kernel_sources(tmp_path, monkeypatch
     assert bench.load_traffic("fused_stream_kernel", "w")[0] == 123
     assert bench.load_traffic("fused_mfma_kernel", "w")[0] is None      # sources changed since
     assert bench.load_traffic("fused_valu_kernel", "w")[0] is None      # never recorded
+
+
+def test_traffic_record_covers_every_included_source():
+    """A kernel's record key covers the headers its file includes, directly or
+    through another header: the device code of every file that reaches it."""
+    csrc = os.path.join(bench.ROOT, "moe_lora_adapter_amd", "csrc")
+    for kernel, own in bench.KERNEL_SOURCES.items():
+        files = bench.kernel_source_files(kernel)
+        for f in own:
+            with open(os.path.join(csrc, f)) as fh:
+                for inc in re.findall(r'^#include "([^"]+)"', fh.read(), re.M):
+                    assert os.path.normpath(inc) in files, (kernel, inc)
+    assert "align_wave.h" in bench.kernel_source_files("fused_stream_kernel")
+    assert "groups.h" in bench.kernel_source_files("fused_mfma_kernel")
+    assert "common.h" in bench.kernel_source_files("fused_valu_kernel")  # through every header
 
 
 def test_cpu_baseline_leg_reports_the_oracle():
