@@ -296,6 +296,12 @@ EDGE = [
     # K beyond what the decode stream kernel stages in LDS (4 rows x K):
     # the register-batch vector kernel takes it
     dict(K=4104, Ns=136, r=64, block_m=16, M=24, E=2, topk=2, L=2, active=2),
+    # the stream kernel at its limits: the largest K it stages (4096), rank
+    # 128, and enough units that the split count is the fewest that keep a
+    # workgroup's columns within its Y buffer (4096 columns: two of 2048)
+    dict(K=4096, Ns=4096, S=2, r=128, block_m=16, M=160, E=16, topk=4, L=2, active=2),
+    # the stream kernel's largest blocks: 128 rows in 32 passes of 4
+    dict(K=1024, Ns=1024, r=64, block_m=128, M=200, E=2, topk=1, L=1, active=1, p_neg=0.0),
 ]
 
 
