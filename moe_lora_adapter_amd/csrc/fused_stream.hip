@@ -408,6 +408,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials fit the X buffer");
   __shared__ int s_ok[kMaxPeers][16];         // K split: peer q's words found by wavefront w
   __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
+  __shared__ int s_grp1[3];                   // one-wavefront grouping: blocks, slot, expert
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
@@ -417,8 +418,21 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   PairGroup<kST> pg;
   BlockScan sc;
   int total;
+  // Up to 64 pairs the grouping is one wavefront's work (a pair per lane):
+  // wavefront 0 does it alone while the others wait, rather than all 16
+  // repeating it four to a SIMD.
+  const bool one_wave = NAIVE && p.numel <= kWave;
   if constexpr (NAIVE) {
-    total = group_pairs(p, gl, pg);
+    if (one_wave) {
+      if (wave_id() == 0) {
+        const int t = group_pairs(p, gl, pg);  // no barrier on this path
+        if (lane_id() == 0) s_grp1[0] = t;
+      }
+      __syncthreads();
+      total = __builtin_amdgcn_readfirstlane(s_grp1[0]);
+    } else {
+      total = group_pairs(p, gl, pg);
+    }
   } else {
     sc = scan_blocks(p);
     total = sc.total;
@@ -443,7 +457,20 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const int32_t* srow = nullptr;
   int id0 = p.numel;
   if constexpr (NAIVE) {
-    group_block(p, gl, pg, g, s_ids, l, e);
+    if (one_wave) {
+      if (wave_id() == 0) {
+        group_block_wave(p, pg, g, s_ids, l, e);
+        if (lane_id() == 0) {
+          s_grp1[1] = l;
+          s_grp1[2] = e;
+        }
+      }
+      __syncthreads();
+      l = __builtin_amdgcn_readfirstlane(s_grp1[1]);
+      e = __builtin_amdgcn_readfirstlane(s_grp1[2]);
+    } else {
+      group_block(p, gl, pg, g, s_ids, l, e);
+    }
   } else {
     int b;
     find_block(p, sc, g, l, b);

@@ -140,6 +140,26 @@ __device__ inline int group_pairs(const FusedParams& p, GroupLds& g, PairGroup<T
   return __builtin_amdgcn_readfirstlane(total);
 }
 
+// Phase 2 for at most 64 pairs, run by the one wavefront that ran phase 1:
+// block gi -> slot l, expert e and its pair ids in ids[0..B), ascending,
+// padded with numel.  No barrier: the caller publishes ids.
+template <int T>
+__device__ inline void group_block_wave(const FusedParams& p, const PairGroup<T>& pg, int gi,
+                                        int* ids, int& l, int& e) {
+  const int lane = lane_id();
+  const uint64_t hit = __ballot(gi >= pg.excl[0] && gi < pg.excl[0] + pg.nblk[0]);
+  const int src = hit ? __builtin_ctzll(hit) : 0;
+  const int key = __builtin_amdgcn_readfirstlane(__shfl(pg.key[0], src));
+  const int b = __builtin_amdgcn_readfirstlane(gi - __shfl(pg.excl[0], src));
+  const bool match = pg.key[0] == key;
+  const uint64_t m = __ballot(match);
+  for (int i = lane; i < p.B; i += kWave) ids[i] = p.numel;
+  const int rank = __popcll(m & lanes_below(lane)) - b * p.B;
+  if (match && rank >= 0 && rank < p.B) ids[rank] = lane;
+  l = key / p.E;
+  e = key - l * p.E;
+}
+
 // Phase 2 (every thread): block gi (< the total of phase 1) -> slot l, expert
 // e and its pair ids in ids[0..B), ascending, padded with numel.  Contains
 // barriers.
