@@ -408,7 +408,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials fit the X buffer");
   __shared__ int s_ok[kMaxPeers][16];         // K split: peer q's words found by wavefront w
   __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
-  __shared__ int s_grp1[3];                   // one-wavefront grouping: blocks, slot, expert
+  __shared__ int s_grp1[4];                   // one-wavefront grouping: blocks, slot, expert,
+                                              // valid rows of the first pass
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
@@ -460,9 +461,28 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     if (one_wave) {
       if (wave_id() == 0) {
         group_block_wave(p, pg, g, s_ids, l, e);
-        if (lane_id() == 0) {
+        // the first pass's rows too, so that one barrier publishes both
+        const int lane = lane_id();
+        int pid = p.numel, xrow = -1;
+        float wv = 1.f;
+        if (lane < kRows && lane < p.B) {
+          const int id = s_ids[lane];
+          if (id < p.numel) {
+            pid = id;
+            xrow = p.x_per_pair ? id : id / p.topk;
+            if (p.mul) wv = p.w[id];
+          }
+        }
+        if (lane < kRows) {
+          s_pair[lane] = pid;
+          s_row[lane] = xrow;
+          s_w[lane] = wv;
+        }
+        const int nr0 = __popcll(__ballot(lane < kRows && xrow >= 0));
+        if (lane == 0) {
           s_grp1[1] = l;
           s_grp1[2] = e;
+          s_grp1[3] = nr0;
         }
       }
       __syncthreads();
@@ -516,7 +536,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     const XchSlot xs_slot = xch ? xch_slot<R>(p, unit * p.xch_passes + g0 / kRows) : XchSlot{};
     if (xch && tid == 0)
       s_tag = __hip_atomic_load(xs_slot.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    if (tid < kRows) {
+    const bool rows_set = one_wave && g0 == 0;  // set with the block, before its barrier
+    if (!rows_set && tid < kRows) {
       int pid = p.numel, xrow = -1;
       float wv = 1.f;
       if (g0 + tid < p.B) {
@@ -533,7 +554,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     }
     for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = s_vl[i] = 0;
     // valid rows are a prefix of the block (sentinels only pad a group's end)
-    const int nr = __builtin_amdgcn_readfirstlane(__syncthreads_count(tid < kRows && s_row[tid] >= 0));
+    const int nr = rows_set ? __builtin_amdgcn_readfirstlane(s_grp1[3])
+                            : __builtin_amdgcn_readfirstlane(
+                                  __syncthreads_count(tid < kRows && s_row[tid] >= 0));
     if (nr == 0) {  // (a block's first pass always has a row: only later passes end here)
       stage_barrier<0>();
       break;
