@@ -421,8 +421,11 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   int total;
   // Up to 64 pairs the grouping is one wavefront's work (a pair per lane):
   // wavefront 0 does it alone while the others wait, rather than all 16
-  // repeating it four to a SIMD.
+  // repeating it four to a SIMD.  The same holds for the block lookup of up
+  // to 64 slots; wavefront 0 then also sets the first pass's rows.
   const bool one_wave = NAIVE && p.numel <= kWave;
+  // (Not with the K split: its pass barrier also publishes the pass's tag.)
+  const bool rows_first = NAIVE ? one_wave : !XCH && p.L <= kWave;
   if constexpr (NAIVE) {
     if (one_wave) {
       if (wave_id() == 0) {
@@ -457,28 +460,31 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   int l, e;
   const int32_t* srow = nullptr;
   int id0 = p.numel;
+  // The block's pair ids of the first pass -> the pass's rows, written to LDS
+  // (lanes < kRows of the calling wavefront); returns the valid rows.
+  auto first_rows = [&](int id) {
+    const int lane = lane_id();
+    int pid = p.numel, xrow = -1;
+    float wv = 1.f;
+    if (lane < kRows && lane < p.B && id < p.numel) {
+      pid = id;
+      xrow = p.x_per_pair ? id : id / p.topk;
+      if (p.mul) wv = p.w[id];
+    }
+    if (lane < kRows) {
+      s_pair[lane] = pid;
+      s_row[lane] = xrow;
+      s_w[lane] = wv;
+    }
+    return __popcll(__ballot(lane < kRows && xrow >= 0));
+  };
   if constexpr (NAIVE) {
-    if (one_wave) {
+    if (rows_first) {
       if (wave_id() == 0) {
         group_block_wave(p, pg, g, s_ids, l, e);
         // the first pass's rows too, so that one barrier publishes both
         const int lane = lane_id();
-        int pid = p.numel, xrow = -1;
-        float wv = 1.f;
-        if (lane < kRows && lane < p.B) {
-          const int id = s_ids[lane];
-          if (id < p.numel) {
-            pid = id;
-            xrow = p.x_per_pair ? id : id / p.topk;
-            if (p.mul) wv = p.w[id];
-          }
-        }
-        if (lane < kRows) {
-          s_pair[lane] = pid;
-          s_row[lane] = xrow;
-          s_w[lane] = wv;
-        }
-        const int nr0 = __popcll(__ballot(lane < kRows && xrow >= 0));
+        const int nr0 = first_rows(lane < kRows && lane < p.B ? s_ids[lane] : p.numel);
         if (lane == 0) {
           s_grp1[1] = l;
           s_grp1[2] = e;
@@ -491,6 +497,26 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     } else {
       group_block(p, gl, pg, g, s_ids, l, e);
     }
+  } else if (rows_first) {
+    // wavefront 0 looks the block up, reads its expert and first pair ids and
+    // sets the first pass's rows; one barrier publishes them
+    if (wave_id() == 0) {
+      int b;
+      find_block(p, sc, g, l, b);
+      srow = p.sorted + l * p.cap + b * p.B;
+      const int lane = lane_id();
+      const int id = (lane < kRows && lane < p.B) ? srow[lane] : p.numel;
+      e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+      const int nr0 = first_rows(id);
+      if (lane == 0) {
+        s_grp1[1] = l;
+        s_grp1[2] = e;
+        s_grp1[3] = nr0;
+      }
+    }
+    __syncthreads();
+    l = __builtin_amdgcn_readfirstlane(s_grp1[1]);
+    e = __builtin_amdgcn_readfirstlane(s_grp1[2]);
   } else {
     int b;
     find_block(p, sc, g, l, b);
@@ -536,7 +562,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     const XchSlot xs_slot = xch ? xch_slot<R>(p, unit * p.xch_passes + g0 / kRows) : XchSlot{};
     if (xch && tid == 0)
       s_tag = __hip_atomic_load(xs_slot.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    const bool rows_set = one_wave && g0 == 0;  // set with the block, before its barrier
+    const bool rows_set = rows_first && g0 == 0;  // set with the block, before its barrier
     if (!rows_set && tid < kRows) {
       int pid = p.numel, xrow = -1;
       float wv = 1.f;
