@@ -103,15 +103,12 @@ __device__ __forceinline__ bool side_align(const FusedParams& p, int idle) {
   return spare;
 }
 
-// The first workgroup index map_unit_xcd leaves without a unit: in XCD x the
-// indices x + 8 slot with slot >= (units of x) * n_split have none.
+// The first workgroup index map_unit_xcd leaves without a unit.  XCD x
+// holds units [x units / 8, (x + 1) units / 8), so XCD 0 holds the fewest,
+// units / 8, and its first index past them, 8 (units / 8) n_split, is below
+// the first idle index x + 8 (its count) n_split of every other XCD x.
 __device__ __forceinline__ int first_idle_xcd(int units, int n_split) {
-  int best = INT_MAX;
-  for (int x = 0; x < kXcds; ++x) {
-    const int lo = int(int64_t(x) * units / kXcds), hi = int(int64_t(x + 1) * units / kXcds);
-    best = min(best, (hi - lo) * n_split * kXcds + x);
-  }
-  return best;
+  return units / kXcds * n_split * kXcds;
 }
 
 }  // namespace mlr
