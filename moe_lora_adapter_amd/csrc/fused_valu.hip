@@ -336,6 +336,7 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   __shared__ float s_part[kMaxRG * 256];
   __shared__ float s_d[CPR > 0 ? RG * kRowsPerBatch : 1];
   __shared__ __align__(16) uint8_t s_grp[NAIVE ? sizeof(GroupLds) : 1];
+  __shared__ int s_one[4];  // one-wavefront lookup: blocks, slot, expert, valid rows
   GroupLds& gl = *reinterpret_cast<GroupLds*>(s_grp);
 
   // The blocks present decide the split count: as many column splits (of at
@@ -346,8 +347,22 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   PairGroup<kThreads> pg;
   BlockScan sc;
   int total;
+  // Up to 64 pairs (align-free) or 64 slots (sorted) the grouping and the
+  // block lookup are one wavefront's work: wavefront 0 does them, and sets
+  // the block's rows, while the others wait, rather than all 16 repeating
+  // them four to a SIMD.
+  const bool one_wave = NAIVE ? p.numel <= kWave : p.L <= kWave;
   if constexpr (NAIVE) {
-    total = group_pairs(p, gl, pg);
+    if (one_wave) {
+      if (wave_id() == 0) {
+        const int t = group_pairs(p, gl, pg);  // no barrier on this path
+        if (lane_id() == 0) s_one[0] = t;
+      }
+      __syncthreads();
+      total = __builtin_amdgcn_readfirstlane(s_one[0]);
+    } else {
+      total = group_pairs(p, gl, pg);
+    }
   } else {
     sc = scan_blocks(p);
     total = sc.total;
@@ -370,27 +385,57 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   if (n0 >= p.Ns) return;
   const int n1 = min(p.Ns, n0 + nsz);
   const int g = unit / p.S, s = unit - g * p.S;
-  int l, e, b = 0;
-  if constexpr (NAIVE) {
-    group_block(p, gl, pg, g, s_pair, l, e);  // pair ids straight into s_pair
+  int l, e, nv;
+  if (one_wave) {
+    if (wave_id() == 0) {
+      int b = 0;
+      if constexpr (NAIVE) {
+        group_block_wave(p, pg, g, s_pair, l, e);  // pair ids straight into s_pair
+      } else {
+        find_block(p, sc, g, l, b);
+        e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+      }
+      // the block's rows (lane 0 takes part in every step, so it counts all)
+      int cnt = 0;
+      for (int i = lane_id(); i < p.B; i += kWave) {
+        const int pid = NAIVE ? s_pair[i] : p.sorted[l * p.cap + b * p.B + i];
+        const bool valid = pid < p.numel;
+        s_pair[i] = pid;
+        s_row[i] = valid ? (p.x_per_pair ? pid : pid / p.topk) : 0;
+        cnt += __popcll(__ballot(valid));
+      }
+      if (lane_id() == 0) {
+        s_one[1] = l;
+        s_one[2] = e;
+        s_one[3] = cnt;
+      }
+    }
+    __syncthreads();
+    l = __builtin_amdgcn_readfirstlane(s_one[1]);
+    e = __builtin_amdgcn_readfirstlane(s_one[2]);
+    nv = __builtin_amdgcn_readfirstlane(s_one[3]);
   } else {
-    find_block(p, sc, g, l, b);
-    e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+    int b = 0;
+    if constexpr (NAIVE) {
+      group_block(p, gl, pg, g, s_pair, l, e);  // pair ids straight into s_pair
+    } else {
+      find_block(p, sc, g, l, b);
+      e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
+    }
+    const int tid = threadIdx.x;
+    int valid = 0;
+    if (tid < p.B) {
+      const int pid = NAIVE ? s_pair[tid] : p.sorted[l * p.cap + b * p.B + tid];
+      valid = pid < p.numel;
+      s_pair[tid] = pid;
+      s_row[tid] = valid ? (p.x_per_pair ? pid : pid / p.topk) : 0;
+    }
+    // valid rows form a prefix of the block (sentinels only pad a group's end)
+    nv = __builtin_amdgcn_readfirstlane(__syncthreads_count(valid));
   }
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
   const uint16_t* A = p.a + wsel * p.r * p.K;
   const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
-
-  const int tid = threadIdx.x;
-  int valid = 0;
-  if (tid < p.B) {
-    const int pid = NAIVE ? s_pair[tid] : p.sorted[l * p.cap + b * p.B + tid];
-    valid = pid < p.numel;
-    s_pair[tid] = pid;
-    s_row[tid] = valid ? (p.x_per_pair ? pid : pid / p.topk) : 0;
-  }
-  // valid rows form a prefix of the block (sentinels only pad a group's end)
-  const int nv = __builtin_amdgcn_readfirstlane(__syncthreads_count(valid));
 
   if (nv <= 2)
     valu_rows<2, JW, CPR>(p, A, Bm, s_row, s_pair, nv, sh, s_part, s_v, s_d, s, n0, n1);
