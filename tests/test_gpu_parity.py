@@ -302,6 +302,11 @@ EDGE = [
     dict(K=4096, Ns=4096, S=2, r=128, block_m=16, M=160, E=16, topk=4, L=2, active=2),
     # the stream kernel's largest blocks: 128 rows in 32 passes of 4
     dict(K=1024, Ns=1024, r=64, block_m=128, M=200, E=2, topk=1, L=1, active=1, p_neg=0.0),
+    # the block lookup on either side of 64 slots (one wavefront up to 64,
+    # every wavefront beyond), stream and register-batch kernels
+    dict(K=256, Ns=256, r=64, block_m=16, M=96, E=2, topk=1, L=64, active=40, p_neg=0.1),
+    dict(K=256, Ns=256, r=32, block_m=16, M=96, E=2, topk=1, L=65, active=50, p_neg=0.1),
+    dict(K=256, Ns=256, r=16, block_m=16, M=96, E=2, topk=1, L=65, active=50, p_neg=0.1),
 ]
 
 
