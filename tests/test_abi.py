@@ -369,9 +369,13 @@ def test_variant_query_resolves_auto():
     # MFMA needs r % 8 == 0, so AUTO never picks it otherwise
     assert fv(8192, 8, 2048, 768, 2, 128, 8, 100, 64) == "valu"
     # from half a row per (slot, expert) group on, small ranks take MFMA too
+    assert fv(2048, 4, 2880, 2880, 2, 128, 4, 8, 64) == "mfma"
+    assert fv(64, 4, 2880, 2880, 2, 128, 4, 8, 64) == "mfma"
+    assert fv(63, 4, 2880, 2880, 2, 128, 4, 8, 64) == "valu"
+    # rank 16 (512-thread vector kernel) from two rows per group on
     assert fv(2048, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
-    assert fv(64, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
-    assert fv(63, 4, 2880, 2880, 2, 128, 4, 16, 64) == "valu"
+    assert fv(256, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
+    assert fv(255, 4, 2880, 2880, 2, 128, 4, 16, 64) == "valu"
     # an x above 2 GiB keeps AUTO on the vector kernel
     assert fv(262145, 8, 4096, 768, 2, 128, 8, 128, 64) == "valu"
     # so does a y above 2 GiB (M * topk * S * Ns * 2 = 2^31 + 2^16 bytes)
