@@ -328,8 +328,8 @@ MOE_LORA_API int64_t fused_moe_lora_two_kernel_workspace_bytes(int64_t M, int32_
 /*
  * fused_moe_lora_two_kernel -- the same function as fused_moe_lora, computed
  * by two kernels with the rank vectors in memory: the path the one-shot
- * kernel replaces (prhub summary of vLLM PR #42290: motivation, and the
- * "two-kernel path for larger ranks" of its key source fragment; the shrink
+ * kernel replaces (prhub summary of vLLM PR #42290: motivation, and its key
+ * source fragment, where ranks above 128 are left to the two-kernel path; the shrink
  * and expand launches of the PR #32005 diff).  Takes ranks up to
  * MOE_LORA_TWO_KERNEL_MAX_RANK, past fused_moe_lora's 128.
  *

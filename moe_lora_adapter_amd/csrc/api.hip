@@ -60,10 +60,10 @@ int pick_variant(int64_t M, int64_t numel, int64_t K, int64_t Ns, int64_t N, int
   // with no padded rows, is faster; from there on the MFMA kernel is
   // (measured on MI355X: gpt-oss-20b-like w13 at 0.33 rows per group 28 vs
   // 33 us, at 1.3 rows per group 82 vs 60 us).  Rank 16 runs the 512-thread
-  // vector kernel, faster up to two rows per group (gpt-oss-120b-like w13 at
-  // 0.5 / 1 / 2 rows per group 23.2 / 45.1 / 54.2 us against MFMA
-  // 27.7 / 48.1 / 54.7; w2 at 1 row 22.5 against 27.7).
-  const bool rows = r == 16 ? numel >= 2 * L * E : 2 * numel >= L * E;
+  // vector kernel, faster up to and including two rows per group
+  // (gpt-oss-120b-like w13 at 0.5 / 1 / 2 rows per group 23.2 / 45.1 / 54.2 us
+  // against MFMA 27.7 / 48.1 / 54.7; w2 at 1 row 22.5 against 27.7).
+  const bool rows = r == 16 ? numel > 2 * L * E : 2 * numel >= L * E;
   const bool mfma = mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair) && rows;
   return mfma ? MOE_LORA_VARIANT_MFMA : MOE_LORA_VARIANT_VALU;
 }

@@ -2,9 +2,9 @@
 //
 // The pages describe the path the one-shot kernel replaces (prhub summary of
 // vLLM PR #42290, motivation: shrink and expand as two kernels with the
-// intermediate written back to HBM; the one-shot kernel's rank limit of 128
-// and "use the two-kernel path for larger ranks" in its key source
-// fragment; the PR #32005 diff shows the two launches, `_fused_moe_lora_shrink`
+// intermediate written back to HBM; key source fragment: the one-shot kernel
+// takes ranks up to 128 and leaves larger ranks to the two-kernel path; the
+// PR #32005 diff shows the two launches, `_fused_moe_lora_shrink`
 // with a `split_k` and `_fused_moe_lora_expand` with a column `offset`).  Here
 // it is the path for ranks up to 512 and the comparator of the fused kernels.
 //

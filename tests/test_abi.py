@@ -372,10 +372,10 @@ def test_variant_query_resolves_auto():
     assert fv(2048, 4, 2880, 2880, 2, 128, 4, 8, 64) == "mfma"
     assert fv(64, 4, 2880, 2880, 2, 128, 4, 8, 64) == "mfma"
     assert fv(63, 4, 2880, 2880, 2, 128, 4, 8, 64) == "valu"
-    # rank 16 (512-thread vector kernel) from two rows per group on
+    # rank 16 (512-thread vector kernel) above two rows per group
     assert fv(2048, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
-    assert fv(256, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
-    assert fv(255, 4, 2880, 2880, 2, 128, 4, 16, 64) == "valu"
+    assert fv(257, 4, 2880, 2880, 2, 128, 4, 16, 64) == "mfma"
+    assert fv(256, 4, 2880, 2880, 2, 128, 4, 16, 64) == "valu"
     # an x above 2 GiB keeps AUTO on the vector kernel
     assert fv(262145, 8, 4096, 768, 2, 128, 8, 128, 64) == "valu"
     # so does a y above 2 GiB (M * topk * S * Ns * 2 = 2^31 + 2^16 bytes)

@@ -95,24 +95,12 @@ def test_two_kernel_edge_shapes(orc, i):
 
 @pytest.mark.parametrize("dist", ["literal", "stress"])
 @pytest.mark.parametrize("name", LARGE)
-def test_two_kernel_full_size_sampled(orc, name, dist):
+def test_two_kernel_full_size(orc, name, dist):
+    """Every element of Y against the oracle at the configured full sizes."""
     s = synth.shape(name, dist=dist)
     _log(f"two-kernel full-size {name} {dist}: drawing inputs")
-    c = synth.draw(s)
-    dc = gh.DeviceCase(c)
-    v = np.nonzero(gh.valid_pairs(c))[0]
-    rng = np.random.default_rng(s.seed)
-    pairs = np.unique(np.concatenate([rng.choice(v, size=min(384, len(v)), replace=False),
-                                      [v[0], v[-1]]]))
-    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
-                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair, pairs=pairs)
     _log(f"two-kernel full-size {name} {dist}")
-    y = _two(dc).view(s.numel, s.N)
-    got = gh.bf16_host_f64(y[torch.from_numpy(pairs).to(gh.DEV)])
-    gh.assert_fused_close(got, ref, f"{name}/{dist}")
-    inval = torch.from_numpy(~gh.valid_pairs(c)).to(gh.DEV)
-    same = y[inval].view(torch.int16) == dc.y_in.view(s.numel, s.N)[inval].view(torch.int16)
-    assert bool(same.all()), "rows of unmapped pairs changed"
+    _full(orc, s, f"{name}/{dist}")
 
 
 @pytest.mark.parametrize("name,kw", [("oss20b_decode_w13_a6", {}),
