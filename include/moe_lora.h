@@ -114,6 +114,34 @@ MOE_LORA_API int moe_lora_align(const int32_t *topk_ids, const int32_t *token_lo
                    int32_t *lora_ids, int32_t *num_active_loras,
                    void *workspace, int64_t workspace_bytes, void *stream);
 
+/* Bytes of the device scratch moe_lora_align_noalloc owns on each GPU. */
+#define MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+
+/*
+ * moe_lora_align_noalloc -- moe_lora_align for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments
+ * without the workspace, the same outputs bit for bit.  The scratch the
+ * multi-workgroup path needs (per-tile key counts and per-key totals) lives
+ * in a static device array of MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it has run on until the process ends; its
+ * address is looked up once per device.  The call allocates nothing.
+ *   - Every call on one GPU shares that array: calls that may overlap on one
+ *     GPU (other streams, other threads) race and must not be issued.
+ *     Calls in stream order are fine; nothing in the array needs clearing
+ *     (its contents on entry do not matter).
+ *   - MOE_LORA_ERR_WORKSPACE (nothing launched) when the sizes need more
+ *     scratch than that (moe_lora_align_workspace_bytes() above the limit;
+ *     no size the limits of this header allow does today).
+ *   - MOE_LORA_ERR_HIP when the scratch's address cannot be found.
+ * Other arguments, statuses and outputs as moe_lora_align.
+ */
+MOE_LORA_API int moe_lora_align_noalloc(const int32_t *topk_ids,
+                   const int32_t *token_lora_mapping, int64_t M, int32_t topk,
+                   int32_t E, int32_t L, int32_t block_m, int32_t *sorted_token_ids,
+                   int32_t *expert_ids, int32_t *num_tokens_post_padded,
+                   int32_t *lora_ids, int32_t *num_active_loras, void *stream);
+
 /* Kernel choice for fused_moe_lora. */
 enum moe_lora_variant {
     MOE_LORA_VARIANT_AUTO = 0, /* chosen from the expected rows per block */

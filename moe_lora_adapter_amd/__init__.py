@@ -32,6 +32,8 @@ SIGNATURES = {
     "moe_lora_align_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32]),
     "moe_lora_align": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
                                       _P, _P, _P, _I64, _P]),
+    "moe_lora_align_noalloc": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P,
+                                              _P, _P, _P, _P]),
     "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
@@ -194,6 +196,30 @@ def moe_lora_align(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *
         workspace.numel() if workspace is not None else 0, _stream_ptr(stream))
     if rc != OK:
         raise MoeLoraError(rc, "moe_lora_align")
+    return out
+
+
+ALIGN_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024   # MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES
+
+
+def moe_lora_align_noalloc(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *,
+                           out: AlignOutput, stream=None) -> AlignOutput:
+    """moe_lora_align with the library's own per-GPU scratch instead of a workspace: the
+    call allocates nothing (out must be given).  Calls that may overlap on one GPU race;
+    see moe_lora.h."""
+    import torch
+    dev = topk_ids.device
+    _check(topk_ids, "topk_ids", torch.int32, dev)
+    _check(token_lora_mapping, "token_lora_mapping", torch.int32, dev)
+    if topk_ids.dim() != 2 or token_lora_mapping.shape != (topk_ids.shape[0],):
+        raise ValueError("topk_ids must be [M, topk] and token_lora_mapping [M]")
+    M, topk = topk_ids.shape
+    rc = lib().moe_lora_align_noalloc(
+        _dptr(topk_ids), _dptr(token_lora_mapping), M, topk, E, L, block_m,
+        _dptr(out.sorted_token_ids), _dptr(out.expert_ids), _dptr(out.num_tokens_post_padded),
+        _dptr(out.lora_ids), _dptr(out.num_active_loras), _stream_ptr(stream))
+    if rc != OK:
+        raise MoeLoraError(rc, "moe_lora_align_noalloc")
     return out
 
 

@@ -122,12 +122,16 @@ int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int32_t E, int32
   return plan_align(numel, E, L, block_m).ws_bytes;
 }
 
-int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, int64_t M,
-                   int32_t topk, int32_t E, int32_t L, int32_t block_m,
-                   int32_t* sorted_token_ids, int32_t* expert_ids,
-                   int32_t* num_tokens_post_padded, int32_t* lora_ids,
-                   int32_t* num_active_loras, void* workspace, int64_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+// The align call with its workspace (null when `ws_bytes` is 0): checks,
+// plan, launch.
+static int align_call(const int32_t* topk_ids, const int32_t* token_lora_mapping, int64_t M,
+                      int32_t topk, int32_t E, int32_t L, int32_t block_m,
+                      int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, int32_t* lora_ids,
+                      int32_t* num_active_loras, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
   if (rc != MOE_LORA_OK) return rc;
@@ -168,6 +172,71 @@ int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, i
   }
   const hipError_t err = launch_align(plan, a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+}
+
+extern "C" {
+
+int moe_lora_align(const int32_t* topk_ids, const int32_t* token_lora_mapping, int64_t M,
+                   int32_t topk, int32_t E, int32_t L, int32_t block_m,
+                   int32_t* sorted_token_ids, int32_t* expert_ids,
+                   int32_t* num_tokens_post_padded, int32_t* lora_ids,
+                   int32_t* num_active_loras, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  return align_call(topk_ids, token_lora_mapping, M, topk, E, L, block_m, sorted_token_ids,
+                    expert_ids, num_tokens_post_padded, lora_ids, num_active_loras, workspace,
+                    workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation align
+// The scratch of moe_lora_align_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) int32_t scratch[MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices] = {nullptr};
+
+// The current device's scratch address, looked up once per device (with that
+// device current).  Two threads that race on the first call store the same
+// address.  Null when the lookup fails.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  g_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_lora_align_noalloc(const int32_t* topk_ids, const int32_t* token_lora_mapping, int64_t M,
+                           int32_t topk, int32_t E, int32_t L, int32_t block_m,
+                           int32_t* sorted_token_ids, int32_t* expert_ids,
+                           int32_t* num_tokens_post_padded, int32_t* lora_ids,
+                           int32_t* num_active_loras, void* stream) {
+  // sizes first: a rejected call makes no HIP call at all
+  int64_t numel, cap;
+  const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
+  if (rc != MOE_LORA_OK) return rc;
+  const int64_t need = plan_align(numel, E, L, block_m).ws_bytes;
+  if (need > MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES) return MOE_LORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (!ws) return MOE_LORA_ERR_HIP;
+  }
+  return align_call(topk_ids, token_lora_mapping, M, topk, E, L, block_m, sorted_token_ids,
+                    expert_ids, num_tokens_post_padded, lora_ids, num_active_loras, ws,
+                    need > 0 ? MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 // The K-split exchange area the sorted-path call needs (0: its kernel has no

@@ -85,6 +85,39 @@ def test_align_rejects(kw, status):
     assert align_call(**kw) == status
 
 
+def align_noalloc_call(**kw):
+    args = dict(topk_ids=P16, mapping=P16, M=16, topk=4, E=32, L=6, B=16, sorted=P16,
+                eids=P16, ntpp=P16, lora_ids=None, nact=None)
+    args.update(kw)
+    a = args
+    return mla.lib().moe_lora_align_noalloc(a["topk_ids"], a["mapping"], a["M"], a["topk"],
+                                            a["E"], a["L"], a["B"], a["sorted"], a["eids"],
+                                            a["ntpp"], a["lora_ids"], a["nact"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk_ids=None), mla.ERR_INVALID),
+    (dict(ntpp=None), mla.ERR_INVALID),
+    (dict(sorted=None), mla.ERR_INVALID),
+    (dict(M=-1), mla.ERR_INVALID),
+    (dict(E=1025), mla.ERR_UNSUPPORTED),
+    (dict(B=48), mla.ERR_UNSUPPORTED),
+    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
+])
+def test_align_noalloc_rejects(kw, status):
+    assert align_noalloc_call(**kw) == status
+
+
+def test_align_noalloc_scratch_covers_every_accepted_size():
+    """The static scratch of the no-allocation align holds the workspace of the largest
+    problems the limits admit (the tile path's per-tile counts are capped)."""
+    assert mla.ALIGN_NOALLOC_SCRATCH_BYTES == 2 * 1024 * 1024
+    for M, topk, E, L, B in ((65536, 8, 256, 16, 64), (2 ** 22, 8, 1024, 8, 128),
+                             (2 ** 20, 1, 1, 1024, 16), (10 ** 6, 1, 1024, 8, 16),
+                             (5000, 4, 2, 1, 16)):
+        assert mla.align_workspace_bytes(M, topk, E, L, B) <= mla.ALIGN_NOALLOC_SCRATCH_BYTES
+
+
 def fused_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
