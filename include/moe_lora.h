@@ -189,28 +189,28 @@ MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
 
 /*
  * fused_moe_lora_ws -- fused_moe_lora with a workspace: the same arguments,
- * the same function and the same result bit for bit, whatever the timing.
- * With the workspace the decode stream kernel (VALU variant, r in {32, 64,
- * 128}) splits the shrink's K range among the workgroups that share a
+ * the same function and, for given sizes, the same result bit for bit
+ * whatever the timing.  With the workspace the decode stream kernel (VALU
+ * variant, r in {32, 64, 128}) splits the shrink's K range among the
+ * workgroups that share a
  * (block, slice) -- one per column range of the expand -- instead of having
- * each of them multiply all of A: each multiplies an equal share of the K
- * stages, publishes its fp32 partial rank vectors in the workspace, and all
- * of them add the partials in the same order, so the rank vector still
- * never reaches memory in bf16 and is identical in every workgroup.  (The
- * split-K shrink of the pages' two-kernel path -- prhub summary of vLLM PR
- * #42290, implementation steps -- applied inside the one-shot kernel.)
- * Measured on MI355X it is no faster than fused_moe_lora at the decode
- * shapes configured here (the exchange costs about what sharing A saves);
- * it is kept as the comparator of that design and for callers whose blocks
- * have many column ranges.
- *   workspace    [device] fused_moe_lora_workspace_bytes() bytes, 16-byte
- *                aligned and ZERO-FILLED before its first use.  Every call
- *                leaves its flag words zero again (in stream order; the
- *                partial vectors stay behind as scratch), so it is reused as
- *                it is, also inside a captured graph.  Two calls that may run
- *                at the same time must not share one.  May be NULL when the
- *                size is 0 (then this is fused_moe_lora).
- *   peer_wait    polls (about 0.7 us each) for another workgroup's partial
+ * each of them read all of A: each multiplies an equal share of K,
+ * publishes its fp32 partial rank vectors in the workspace, and all of them
+ * add the partials in the same order, so the rank vector never reaches
+ * memory in bf16 and is identical in every workgroup.  (The split-K shrink
+ * of the pages' two-kernel path -- prhub summary of vLLM PR #42290,
+ * implementation steps -- applied inside the one-shot kernel.)
+ *   workspace    [device] at least fused_moe_lora_workspace_bytes() bytes,
+ *                16-byte aligned and ZERO-FILLED before its first use.  Its
+ *                layout depends on workspace_bytes alone, not on the sizes
+ *                of a call: reused as it is (also inside a captured graph),
+ *                one workspace serves calls of any size it is large enough
+ *                for, provided it is always passed with the same
+ *                workspace_bytes (zero-fill it again before passing another
+ *                size).  Two calls that may run at the same time must not
+ *                share one.  May be NULL when the size is 0 (then this is
+ *                fused_moe_lora).
+ *   peer_wait    polls (about 0.5 us each) for another workgroup's partial
  *                before this workgroup computes that partial itself, from A
  *                in memory and with the same bits; no workgroup waits on
  *                another beyond that, so the call completes even when the

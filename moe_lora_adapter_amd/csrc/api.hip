@@ -8,6 +8,7 @@
 #include "../../include/moe_lora.h"
 #include "common.h"
 #include "internal.h"
+#include "xch.h"
 
 using namespace mlr;
 
@@ -250,7 +251,7 @@ static int64_t fused_exchange_bytes(int64_t M, int32_t topk, int32_t K, int32_t 
   if (v == MOE_LORA_VARIANT_MFMA || numel == 0 || !valu_takes_stream(M, numel, K, N, r, x_per_pair))
     return 0;
   const int64_t units = max_total_blocks(numel, int64_t(L) * E, block_m) * S;
-  return stream_exchange_bytes(units, block_m, r);
+  return xch_area_bytes(units * exchange_passes(block_m));
 }
 
 static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
@@ -259,7 +260,7 @@ static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* l
                         const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
                         int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                         int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
-                        int32_t* xch, int32_t peer_wait, void* stream) {
+                        int32_t* xch, int64_t xch_bytes, int32_t peer_wait, void* stream) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
   if (rc != MOE_LORA_OK) return rc;
@@ -309,7 +310,8 @@ static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* l
   p.units = int32_t(units);
   p.xcd_cus = xcd_compute_units();
   p.xch = xch;
-  p.xch_passes = stream_exchange_passes(block_m);
+  p.xch_nslot = xch ? int32_t(std::min<int64_t>(xch_slots_in(xch_bytes), kInt32Max)) : 0;
+  p.xch_passes = int32_t(exchange_passes(block_m));
   p.peer_wait = peer_wait < 0 ? kDefaultPeerWait : peer_wait;
 
   const bool use_mfma =
@@ -328,7 +330,7 @@ int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a
                    void* stream) {
   return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
                       num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
-                      K, Ns, S, E, L, r, block_m, y, variant, nullptr, 0, stream);
+                      K, Ns, S, E, L, r, block_m, y, variant, nullptr, 0, 0, stream);
 }
 
 int64_t fused_moe_lora_workspace_bytes(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S,
@@ -352,7 +354,8 @@ int fused_moe_lora_ws(const uint16_t* x, int32_t x_per_pair, const uint16_t* lor
   return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
                       num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
                       K, Ns, S, E, L, r, block_m, y, variant,
-                      need > 0 ? static_cast<int32_t*>(workspace) : nullptr, peer_wait, stream);
+                      need > 0 ? static_cast<int32_t*>(workspace) : nullptr, workspace_bytes,
+                      peer_wait, stream);
 }
 
 static_assert(kAlignWaveMaxPairs == MOE_LORA_WITH_ALIGN_MAX_PAIRS &&

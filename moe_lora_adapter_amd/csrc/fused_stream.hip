@@ -48,6 +48,7 @@
 #include "align_wave.h"
 #include "groups.h"
 #include "internal.h"
+#include "xch.h"
 
 namespace mlr {
 namespace {
@@ -62,8 +63,7 @@ constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
 constexpr int kMaxCols = 2048;              // output columns per workgroup
 constexpr int kYBytes = kRows * kMaxCols * 2;
 constexpr int kMaxIds = 128;                // largest block_m
-constexpr int kMaxPeers = 8;                // most workgroups one K split spans
-constexpr int kLocalPolls = 3;              // polls of the XCD's L2 before device-scope reads
+constexpr int kMaxPeers = kXchPeers;       // most workgroups one K split spans
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
 // Ring depth: slots - 1 stages in flight per workgroup.  Three slots (32 KiB
@@ -75,6 +75,13 @@ constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 #endif
 constexpr int kSlots = MLR_STREAM_SLOTS;
 static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
+
+// With the K split, B stages are issued up to this many slots minus one
+// ahead from the exchange on: the exchange's round trip (3 to 4 us under the
+// streaming load) then passes while B keeps streaming into the ring.  The
+// slot count is what LDS leaves room for beside the exchange's buffers.
+template <int R>
+constexpr int kSlotsXch() { return R <= 64 ? 5 : 4; }
 
 #ifndef MLR_STREAM_MIN_COLS
 #define MLR_STREAM_MIN_COLS 256
@@ -196,192 +203,89 @@ __device__ __forceinline__ f32x4_t a_partial_direct(const FusedParams& p, __amdg
   return acc;
 }
 
-// Exchange area of the K split, for `slots` (unit, pass) slots: generation
-// words [slots] (uint32), departures [slots] (int32), then from a 16-byte
-// boundary the partials, [slots][2][kMaxPeers][kRows][r] 64-bit words, each
-// an fp32 value in the low half and its call's tag in the high half (copy 0
-// written through the XCD's L2, copy 1 at device scope).  Zero-filled before
-// first use; after that every call leaves it usable as it is.
-__host__ __device__ inline int64_t xch_part_words(int64_t slots) { return (2 * slots + 3) / 4 * 4; }
-
-// The K split of one pass.  The peers -- the C workgroups of a unit, one per
-// column split -- each multiply an equal share of the A stages, publish their
-// partial, and form v = P_0 + P_1 + ... + P_{C-1} in peer order, so all
-// peers hold the same v.  A peer's partial values carry the tag of this call
-// in the slot (the slot's generation + 1; the last peer to leave the slot
-// advances the generation), so a waiting peer polls the values themselves:
-// stale values of an earlier call never carry the current tag, and no flag
-// or completion wait is needed between the data and its announcement.  A
-// partial not complete after `peer_wait` polls is computed here from A in
+// The K split of one pass (exchange protocol and area: xch.h).  The peers
+// -- the C workgroups of a unit, one per column split -- each multiply an
+// equal share of the A stages, publish their partial, and form
+// v = P_0 + P_1 + ... + P_{C-1} in peer order, so all peers hold the same v.
+// A partial not complete after `peer_wait` polls is computed here from A in
 // memory (the same bits), so no wait depends on another workgroup being
 // resident.
-//
-// A partial is written twice: copy 0 with ordinary stores, which land in the
-// L2 of the writer's XCD, and copy 1 with device-scope stores, coherent
-// across the XCDs' L2s.  The peers of a unit are launched on one XCD, so the
-// first kLocalPolls polls read copy 0 from that shared L2 (dropping this
-// compute unit's L1 copy first); later polls read copy 1 at device scope,
-// which also finds a peer that ran on another XCD.
-// (Device-scope stores go past the L2, so copy 1 alone, read through the L2,
-// can stay stale there; read at device scope it costs a memory round trip
-// under the streaming load, about 3 us.)  None of this decides correctness:
-// a word with this call's tag is this call's value, and a stale read only
-// costs another poll, or at worst the partial computed here.  Device-scope
-// release / acquire fences would order plain accesses instead, but each
-// writes back or invalidates a whole L2: measured on MI355X, 20 to 30 us per
-// exchange.
-struct XchSlot {
-  uint32_t* gen;
-  int* depart;
-  uint64_t* parts;  // [2][kMaxPeers][kRows][R]
-};
 
-template <int R>
-__device__ __forceinline__ XchSlot xch_slot(const FusedParams& p, int slot) {
-  const int64_t slots = int64_t(p.units) * p.xch_passes;
-  XchSlot x;
-  x.gen = reinterpret_cast<uint32_t*>(p.xch) + slot;
-  x.depart = p.xch + slots + slot;
-  x.parts = reinterpret_cast<uint64_t*>(p.xch + xch_part_words(slots)) + int64_t(slot) * 2 * kMaxPeers * kRows * R;
-  return x;
-}
-
+// The wavefronts w < RT hold, lane (lr, lq), v[row lr][16 w + 4 lq + i].
 template <int R>
 __device__ __forceinline__ void publish_partial(const XchSlot& x, const f32x4_t& acc, int split,
                                                 uint32_t tag) {
   using G = Geo<R>;
   const int w = wave_id(), lane = lane_id(), lr = lane & 15, lq = lane >> 4;
   if (w < G::RT && lr < kRows) {
-    uint64_t* dst = x.parts + (split * kRows + lr) * R + 16 * w + 4 * lq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t word = uint64_t(__float_as_uint(acc[i])) | (uint64_t(tag) << 32);
-      __hip_atomic_store(dst + i, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_store(dst + kMaxPeers * kRows * R + i, word, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int i = 0; i < 4; ++i) xch_put(x, split, lr, 16 * w + 4 * lq + i, acc[i], tag);
   }
 }
 
-// s_ok[q][w]: wavefront w < RT found all of its words of peer q's partial.
+// All peers' words polled at once by the holders, the values parked in LDS
+// (s_peer[peer][row][rank]); s_miss collects the peers whose partial did not
+// arrive, which are then computed here.  v is then summed in peer order.
 template <int R>
 __device__ __forceinline__ void gather_partials(const FusedParams& p, const XchSlot& x, f32x4_t& acc,
-                                                float* s_part, int (*s_ok)[16], const uint8_t* xs,
-                                                __amdgpu_buffer_rsrc_t a_rsrc, int split, int C,
-                                                int nA_all, uint32_t tag) {
+                                                float* s_part, float* s_peer, int* s_miss,
+                                                const uint8_t* xs, __amdgpu_buffer_rsrc_t a_rsrc,
+                                                int split, int C, int nA_all, uint32_t tag) {
   using G = Geo<R>;
   const int w = wave_id(), lane = lane_id(), lr = lane & 15, lq = lane >> 4;
   const bool holder = w < G::RT && lr < kRows;
-  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int q = 0; q < C; ++q) {
-    f32x4_t pq = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (q == split) {
-      pq = acc;
-    } else {
-      // the wavefronts holding v poll their words of peer q's partial
-      uint64_t wv[4] = {0, 0, 0, 0};
-      if (w < G::RT) {
-        const uint64_t* src = x.parts + (q * kRows + lr) * R + 16 * w + 4 * lq;
-        const uint64_t* src_dev = src + kMaxPeers * kRows * R;
-        bool ok = false;
-        // two loops, one load form each: a loop whose body picks between the
-        // two forms left the compiler waiting for every memory operation at
-        // each step of the stage loop around it (the ring's DMA is invisible
-        // to it, so that wait drained the ring)
-        int n = 0;
-        for (; n < kLocalPolls && n < p.peer_wait; ++n) {
-          asm volatile("buffer_inv sc0" ::: "memory");  // this compute unit's L1 only
-          ok = true;
-          if (holder) {
+  float* mine = s_peer + lr * R + 16 * w + 4 * lq;  // + q * kRows * R
+  if (w < G::RT) {
+    uint32_t pending = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              wv[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int q = 0; q < kMaxPeers; ++q)
+      if (holder && q < C && q != split) pending |= 1u << q;
+    for (int n = 0; n < p.peer_wait && __ballot(pending != 0) != 0; ++n) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
-          }
-          if (__ballot(!ok) == 0) break;
-          __builtin_amdgcn_s_sleep(8);
-        }
-        if (__ballot(!ok) != 0) {
-          for (; n < p.peer_wait; ++n) {
-            ok = true;
-            if (holder) {
+      for (int q = 0; q < kMaxPeers; ++q) {
+        if ((pending >> q) & 1u) {
+          uint64_t wd[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                wv[i] = __hip_atomic_load(src_dev + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i = 0; i < 4; ++i) wd[i] = xch_get(x, q, lr, 16 * w + 4 * lq + i);
+          bool ok = true;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) ok = ok && uint32_t(wv[i] >> 32) == tag;
-            }
-            if (__ballot(!ok) == 0) break;
-            __builtin_amdgcn_s_sleep(8);
+          for (int i = 0; i < 4; ++i) ok = ok && xch_tagged(wd[i], tag);
+          if (ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mine[q * kRows * R + i] = xch_value(wd[i]);
+            pending &= ~(1u << q);
           }
         }
-        if (lane == 0) s_ok[q][w] = __ballot(!ok) == 0;
       }
-      stage_barrier<63>();
-      bool all_ok = true;
-#pragma unroll
-      for (int k = 0; k < G::RT; ++k) all_ok = all_ok && s_ok[q][k] != 0;
-      if (!all_ok) {
-        stage_barrier<0>();  // X, and everything else in flight, has landed
-        pq = a_partial_direct<R>(p, a_rsrc, xs, q * nA_all / C, (q + 1) * nA_all / C);
-        reduce_ksteps<R>(pq, s_part);
-      } else if (holder) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pq[i] = __uint_as_float(uint32_t(wv[i]));
-      }
+      if (__ballot(pending != 0) != 0) __builtin_amdgcn_s_sleep(8);
     }
+    if (pending) atomicOr(s_miss, int(pending));
+    if (holder) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] += pq[i];
-  }
-  acc = v;
-}
-
-// After the pass (every wavefront has used the slot): the last peer out
-// advances the slot's generation, which retires this call's tag.
-__device__ __forceinline__ void depart_slot(const XchSlot& x, int C, uint32_t tag) {
-  if (threadIdx.x == 0) {
-    // every read of the slot by this workgroup has returned (its values were used)
-    const int old = __hip_atomic_fetch_add(x.depart, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == C - 1) {
-      __hip_atomic_store(x.gen, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(x.depart, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < 4; ++i) mine[split * kRows * R + i] = acc[i];
     }
   }
-}
-
-// B stage u of the ring issued by the wavefronts w >= RT alone (at the
-// exchange, where the wavefronts w < RT are busy with the peers): wavefront
-// w loads its own chunks and, for RT <= w < 2 RT, those of wavefront w - RT.
-template <int R>
-__device__ __forceinline__ void issue_stage_cover(const FusedParams& p, i32x4_t br, int u, int ncols,
-                                                  uint32_t lds) {
-  using G = Geo<R>;
-  static_assert(2 * G::RT <= kST / kWave, "the other wavefronts cover the holders' chunks");
-  const int w = wave_id(), lane = lane_id();
-  auto one = [&](int wc) {
-    const int q = wc * kWave + lane;
-    const int col = q / G::CPR, js = q % G::CPR;
-    const int n = u * G::NCS + col;
-    const int jc = js ^ (col & (G::SW - 1));
-    dma16(br, lds + wc * kWave * 16, n < ncols ? uint32_t(n * R + 8 * jc) * 2u : kOob);
-  };
-  one(w);
-  if (w < 2 * G::RT) one(w - G::RT);
-}
-
-// The wait for the first B stage after the exchange: with `later` stages
-// issued after it, a wavefront has later * (its instructions per stage) of
-// them outstanding -- none for w < RT, two for RT <= w < 2 RT, one above.
-template <int R>
-__device__ __forceinline__ void wait_first_b(int later) {
-  using G = Geo<R>;
-  static_assert(kSlots - 2 <= 7, "vmcnt range");
-  const int w = wave_id();
-  const int n = w < G::RT ? 0 : (w < 2 * G::RT ? 2 * later : later);
-  if (n == 0) stage_barrier<0>();
-  else wait_counts<2 * (kSlots - 2)>(n);
+  stage_barrier<63>();
+  const int miss = __builtin_amdgcn_readfirstlane(*s_miss);
+  if (miss) {
+    stage_barrier<0>();  // X, and everything else in flight, has landed
+    for (int q = 0; q < C; ++q) {  // rare: a peer's partial computed here instead
+      if (!((miss >> q) & 1)) continue;
+      f32x4_t pq = a_partial_direct<R>(p, a_rsrc, xs, q * nA_all / C, (q + 1) * nA_all / C);
+      reduce_ksteps<R>(pq, s_part);
+      if (holder) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[q * kRows * R + i] = pq[i];
+      }
+    }
+  }
+  if (holder) {
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < C; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += mine[q * kRows * R + i];
+    acc = v;
+  }
 }
 
 // NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
@@ -394,7 +298,10 @@ template <int R, bool NAIVE, bool XCH>
 __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   using G = Geo<R>;
   constexpr int VP = 32 * G::KS + 8;  // bf16 pitch of the v rows
-  __shared__ __align__(16) uint8_t ring[kSlots * kStage];
+  // ring slots: kSlots, or with the K split a deeper ring that holds the B
+  // stages loaded while the peers' partials are awaited
+  constexpr int NS = XCH ? kSlotsXch<R>() : kSlots;
+  __shared__ __align__(16) uint8_t ring[NS * kStage];
   __shared__ __align__(16) uint8_t xs[kXBytes];
   __shared__ __align__(16) uint8_t ys[kYBytes];
   __shared__ __align__(16) uint16_t s_vb[kRows * VP];  // v, bf16 high part
@@ -406,8 +313,10 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   __shared__ uint2 s_dummy[kWave];            // stores of lanes with no output
   __shared__ __align__(16) float s_part[XCH ? kST * 4 : 4];  // k-step partials (K split)
   static_assert(kST * 4 * 4 <= kXBytes, "k-step partials fit the X buffer");
-  __shared__ int s_ok[kMaxPeers][16];         // K split: peer q's words found by wavefront w
+  __shared__ int s_miss;                      // K split: peers whose partial did not arrive
+  __shared__ float s_peer[XCH ? kMaxPeers * kRows * R : 1];  // K split: the peers' partials
   __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
+  __shared__ __align__(16) uint32_t s_left[XCH ? kXchPeers : 1];  // K split: the slot's left words
   __shared__ int s_grp1[4];                   // one-wavefront grouping: blocks, slot, expert,
                                               // valid rows of the first pass
   static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
@@ -424,8 +333,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // repeating it four to a SIMD.  The same holds for the block lookup of up
   // to 64 slots; wavefront 0 then also sets the first pass's rows.
   const bool one_wave = NAIVE && p.numel <= kWave;
-  // (Not with the K split: its pass barrier also publishes the pass's tag.)
-  const bool rows_first = NAIVE ? one_wave : !XCH && p.L <= kWave;
+  const bool rows_first = NAIVE ? one_wave : p.L <= kWave;
   if constexpr (NAIVE) {
     if (one_wave) {
       if (wave_id() == 0) {
@@ -559,9 +467,16 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   if (TA > 0) issue_stage<R>(p, ar, br, 0, nA, ka0, ncols, ring_lds);
 
   for (int g0 = 0; g0 < p.B; g0 += kRows) {
-    const XchSlot xs_slot = xch ? xch_slot<R>(p, unit * p.xch_passes + g0 / kRows) : XchSlot{};
-    if (xch && tid == 0)
-      s_tag = __hip_atomic_load(xs_slot.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // K split: the pass's slot
+    const XchSlot xs_slot = xch ? xch_slot(p.xch, p.xch_nslot, unit * p.xch_passes + g0 / kRows) : XchSlot{};
+    // K split: the slot's `left` words go to LDS by a direct load issued now
+    // (two lanes of wavefront 0, after the pass's first stage): no register
+    // holds them and nothing waits for them before the exchange, which reads
+    // them; the first stage's wait covers them
+    if (xch && w == 0 && lane < 2) {
+      const i32x4_t lr4 = dma_rsrc(xs_slot.left, 4 * kXchPeers);
+      dma16(lr4, lds_address(s_left), uint32_t(16 * lane));
+    }
     const bool rows_set = rows_first && g0 == 0;  // set with the block, before its barrier
     if (!rows_set && tid < kRows) {
       int pid = p.numel, xrow = -1;
@@ -591,7 +506,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     // X rows (row stride K / 8 chunks) and the split's Y values (row stride
     // ncols / 8 chunks) into LDS: 64 chunks per instruction, only
     // instructions that start inside the data (both buffers are multiples
-    // of 64 chunks, so a last partial instruction still fits)
+    // of 64 chunks, so a last partial instruction still fits).  (Loading Y
+    // after the first stage instead, since the expand is the first to need
+    // it, measured 4 us slower on the 20b-like decode.)
     for (int q0 = w * kWave; q0 < kRows * K8; q0 += kST) {
       const int q = q0 + lane, i = q / K8, c = q % K8;
       const int xrow = i < kRows ? s_row[i] : -1;
@@ -607,6 +524,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     }
     for (int t = g0 == 0 ? 1 : 0; t < kSlots - 1 && t < TA; ++t)
       issue_stage<R>(p, ar, br, t, nA, ka0, ncols, ring_lds + t * kStage);
+    static_assert(NS >= kSlots, "the first stages go to slots 0 .. kSlots - 2");
 
     // wavefront w: A rank tile rt and k-step ka of every A stage
     const int rt = w % G::RT, ka = w / G::RT;
@@ -616,25 +534,28 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
-    const uint32_t tag = xch ? __builtin_amdgcn_readfirstlane(s_tag) : 0u;
     for (int t = 0; t < T; ++t) {
       if (t == nA) {
         // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
         // (the k-step partials go through the X buffer, which only the K
         // split's fallback still reads)
+        if (xch && tid == 0) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int q = 0; q < kXchPeers; ++q) m = s_left[q] > m ? s_left[q] : m;
+          s_tag = m + 1u;
+          s_miss = 0;
+        }
         reduce_ksteps<R>(acc, XCH ? s_part : reinterpret_cast<float*>(xs));
         if (xch) {
-          // the wavefronts holding v publish and poll; the others meanwhile
-          // load the first B stages, the holders' chunks included, so no
-          // wait for a peer's values queues behind a B load (a wavefront's
-          // memory counter retires in order)
-          if (w < G::RT) {
-            publish_partial<R>(xs_slot, acc, split, tag);
-          } else {
-            for (int q = 0; q < kSlots - 1 && nA + q < T; ++q)
-              issue_stage_cover<R>(p, br, nA + q - nA, ncols, ring_lds + ((nA + q) % kSlots) * kStage);
-          }
-          gather_partials<R>(p, xs_slot, acc, s_part, s_ok, xs, a_rsrc, split, C, nA_all, tag);
+          const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
+          // the wavefronts holding v publish; then every wavefront issues
+          // the next NS - 1 B stages, which stream while the holders wait
+          // for the peers' partials (their polls retire after those loads)
+          publish_partial<R>(xs_slot, acc, split, tag);
+          for (int u = nA; u < nA + NS - 1 && u < T; ++u)
+            issue_stage<R>(p, ar, br, u, nA, ka0, ncols, ring_lds + (u % NS) * kStage);
+          gather_partials<R>(p, xs_slot, acc, s_part, s_peer, &s_miss, xs, a_rsrc, split, C, nA_all, tag);
         }
         // lane (lr, lq) of wavefront w < RT holds v[row lr][16 w + 4 lq + i]
         if (w < G::RT && lr < kRows) {
@@ -646,16 +567,28 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
           }
         }
       }
-      // stage t (and, at t = 0, the X rows and Y values issued before it):
-      // the later stages stay in flight, so the ring never drains to empty
+      // stage t (and, at t = 0, the X rows issued before it): the later
+      // stages stay in flight, so the ring never drains to empty
       // (with the K split the A stages drain before the exchange)
       const int lim = t < nA ? TA : T;
-      if (xch && t == nA) wait_first_b<R>(min(kSlots - 2, T - 1 - t));
-      else wait_stage<kSlots - 2>(min(kSlots - 2, lim - 1 - t));
-      if (t + kSlots - 1 < lim)
-        issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ka0, ncols,
-                       ring_lds + ((t + kSlots - 1) % kSlots) * kStage);
-      const uint4* st = reinterpret_cast<const uint4*>(ring + (t % kSlots) * kStage);
+      if constexpr (!XCH) {
+        wait_stage<kSlots - 2>(min(kSlots - 2, lim - 1 - t));
+        if (t + kSlots - 1 < lim)
+          issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ka0, ncols,
+                         ring_lds + ((t + kSlots - 1) % kSlots) * kStage);
+      } else {
+        // stages issued ahead of t: kSlots - 1, or NS - 1 from the exchange on
+        const int ahead = (xch && t >= nA) ? NS - 1 : kSlots - 1;
+        wait_stage<NS - 2>(min(ahead - 1, lim - 1 - t));
+        if (xch && t == nA && tid == 0) {
+          // every read of the slot by this workgroup has returned (its values
+          // are in s_vb / s_vl): leave it
+          xch_leave(xs_slot, split, s_tag);
+        }
+        if (t + ahead < lim)
+          issue_stage<R>(p, ar, br, t + ahead, nA, ka0, ncols, ring_lds + ((t + ahead) % NS) * kStage);
+      }
+      const uint4* st = reinterpret_cast<const uint4*>(ring + (t % NS) * kStage);
       if (t < nA) {
         // ---- shrink: V^T[rank tile rt] += A[16 ranks x 32 k] . X^T
         const int j = 16 * rt + lr, c = 4 * ka + lq;
@@ -712,7 +645,6 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       }
     }
     __syncthreads();
-    if (xch) depart_slot(xs_slot, C, tag);
     // ---- epilogue: Y rows of the split, 16 bytes per thread and step
     for (int q = tid; q < nr * c8; q += kST) {
       const int i = q / c8, c = q % c8;
@@ -734,13 +666,7 @@ bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int
   return x_bytes <= kMaxBufBytes && numel * N * 2 <= kMaxBufBytes && r * K * 2 <= kMaxBufBytes;
 }
 
-// Exchange area of the K split for a launch: one slot per (unit, pass).
-int stream_exchange_passes(int block_m) { return (block_m + kRows - 1) / kRows; }
-
-int64_t stream_exchange_bytes(int64_t units, int block_m, int r) {
-  const int64_t slots = units * stream_exchange_passes(block_m);
-  return 4 * xch_part_words(slots) + slots * 2 * kMaxPeers * kRows * r * 8;
-}
+static_assert(kRows == kXchRows, "a pass of the stream kernel is one exchange slot");
 
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   // grid: 8 XCD ranges of ceil(units / 8) units times the split count, which

@@ -68,8 +68,9 @@ struct FusedParams {
   int32_t* al_ntpp;
   int32_t* al_lora_ids;
   int32_t* al_nact;
-  int32_t* xch;        // stream kernel: K-split exchange area, zero between calls (null: none)
-  int32_t xch_passes;  // stream kernel: passes per block the exchange area holds
+  int32_t* xch;        // stream kernel: K-split exchange area (xch.h; null: no K split)
+  int32_t xch_nslot;   // slots the exchange area holds (its layout depends on this alone)
+  int32_t xch_passes;  // exchange slots per unit: one per pass of kXchRows rows
   int32_t peer_wait;   // stream kernel: polls for a peer's partial before computing it here
   float* ws;           // two-kernel path: partial rank vectors, fp32 [kz, S, numel, r]
   int32_t kz;          // two-kernel path: K splits of the shrink
@@ -101,8 +102,9 @@ int xcd_compute_units();
 hipError_t launch_fused_valu(FusedParams p, hipStream_t st);
 hipError_t launch_fused_mfma(FusedParams p, hipStream_t st);
 hipError_t launch_fused_stream(FusedParams p, hipStream_t st);
-int64_t stream_exchange_bytes(int64_t units, int block_m, int r);
-int stream_exchange_passes(int block_m);
+// Slots of the K-split exchange a launch of `units` units uses (one per unit
+// and pass of four rows).
+inline int64_t exchange_passes(int64_t block_m) { return (block_m + 3) / 4; }
 bool stream_supported(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);
 // Whether the vector variant runs the stream kernel for these sizes.
 bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair);

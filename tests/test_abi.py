@@ -312,11 +312,19 @@ def test_fused_ws_rejects(kw, status):
 
 def test_fused_workspace_query():
     q = mla.fused_moe_lora_workspace_bytes
-    # decode stream kernel: slots of (unit, 4-row pass), 8 peers of 4 x r fp32 each
-    b = q(16, 4, 2880, 2880, 2, 32, 6, 64, 16, False, "valu")
-    assert b > 0 and b % 16 == 0
-    assert q(16, 4, 2880, 2880, 2, 32, 6, 128, 16, False, "valu") > b  # rank 128: larger partials
-    assert q(16, 4, 2880, 2880, 2, 32, 6, 64, 32, False, "valu") > b   # more passes per block
+    # the decode stream kernel's K split: one slot per (unit, 4-row pass) bound;
+    # a slot holds 8 peers x 4 rows x 128 ranks of 8-byte words whatever the
+    # rank, after the slots' tag words (8 peers x 4 bytes each)
+    slot = 8 * 4 * 128 * 8
+
+    def area(n):
+        return (32 * n + 15) // 16 * 16 + n * slot
+    b = q(16, 4, 2880, 2880, 2, 32, 6, 64, 16, False, "valu")       # stream kernel
+    units = (64 + 64 * 15) // 16 * 2                                  # block bound x slices
+    assert b == area(units * 4)
+    assert q(16, 4, 2880, 2880, 2, 32, 6, 128, 16, False, "valu") == b  # rank-free layout
+    assert q(16, 4, 2880, 2880, 2, 32, 6, 64, 32, False, "valu") > b    # more passes per block
+    assert q(8, 4, 2880, 2880, 2, 128, 4, 32, 16, False, "valu") == area((32 + 32 * 15) // 16 * 2 * 4)
     # kernels without the K split need none
     assert q(16, 2, 256, 128, 1, 8, 2, 8, 16) == 0                    # register-batch kernel
     assert q(16, 4, 2880, 2880, 2, 32, 6, 64, 16, False, "mfma") == 0

@@ -1,8 +1,9 @@
-"""GPU parity of the K-split decode stream kernel (fused_moe_lora_ws) through the C ABI.
+"""GPU parity of the K split of the decode kernels (fused_moe_lora_ws) through the C ABI.
 
 The workgroups that share a (block, slice) -- one per column range of the
-expand -- each multiply an equal share of A's K stages and meet through the
-workspace, adding the partial rank vectors in the same order.  Checked here:
+expand -- each multiply an equal share of A's K range and meet through the
+workspace, adding the partial rank vectors in the same order (the decode
+stream kernel, ranks 32, 64, 128).  Checked here:
 
 - against the CPU oracle with fused_moe_lora's tolerance, rows of pairs in
   no slot untouched;
@@ -11,8 +12,11 @@ workspace, adding the partial rank vectors in the same order.  Checked here:
   in memory (the path taken when a peer is late), gives the same bytes as
   the exchange: published and recomputed partials are the same bits;
 - a workspace reused after calls on other inputs gives the same bytes as a
-  fresh zero-filled one (every call leaves the flag words zero; the stale
-  partials it leaves are never read);
+  fresh zero-filled one (the area's layout depends on its size alone and
+  every stale word carries an older tag);
+- one workspace reused by calls of different sizes (M = 16, 15, 16, and
+  ranks 64, 32, 128), each result equal bit for bit to peer_wait = 0 on
+  that workspace;
 - one captured graph, replayed with the slot mapping rewritten in place
   between replays, matches eager calls bit for bit;
 - the workspace checks of the entry point.
@@ -60,7 +64,7 @@ def orc():
     return oracle.load()
 
 
-def _stream_kernel(s):
+def _ksplit_kernel(s):
     return mla.fused_kernel_name(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r, s.block_m,
                                  s.x_per_pair, "valu") == "fused_stream_kernel"
 
@@ -81,7 +85,7 @@ def _workspace(s):
 
 
 def _check_case(orc, s, what):
-    assert _stream_kernel(s), f"{what}: the stream kernel does not take this shape"
+    assert _ksplit_kernel(s), f"{what}: the stream kernel does not take this shape"
     c = synth.draw(s)
     dc = gh.DeviceCase(c)
     al = dc.align()
@@ -213,11 +217,42 @@ def test_k_split_workspace_checks():
     with pytest.raises(mla.MoeLoraError) as ei:
         _ws(dc, al, big[4:])
     assert ei.value.status == mla.ERR_WORKSPACE
-    # a shape whose kernel needs none: the workspace may be absent
-    t = synth.shape("tiny")
+    # a shape whose kernel needs none (an odd rank: register batches): the
+    # workspace may be absent
+    t = synth.shape("tiny", r=5)
     assert mla.fused_moe_lora_workspace_bytes(t.M, t.topk, t.K, t.Ns, t.S, t.E, t.L, t.r,
                                               t.block_m, t.x_per_pair, "valu") == 0
     dt = gh.DeviceCase(synth.draw(t))
     y = _ws(dt, dt.align(), None)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), dt.fused(variant="valu").view(torch.int16))
+
+
+@pytest.mark.parametrize("name,calls", [
+    ("oss20b_decode_w13_a6", (dict(M=16), dict(M=15), dict(M=16))),
+    ("oss20b_decode_w13_a3", (dict(M=16, r=64), dict(M=12, r=32), dict(M=16, r=128)))])
+def test_k_split_workspace_reused_across_sizes(orc, name, calls):
+    """One workspace, sized for the largest call, serves calls of other sizes
+    in a row: each result equals peer_wait = 0 (every partial computed in
+    place) bit for bit, and the oracle within tolerance."""
+    shapes = [synth.shape(name, dist="stress", seed=5000 + 17 * i, **kw) for i, kw in enumerate(calls)]
+    need_max = max(mla.fused_moe_lora_workspace_bytes(t.M, t.topk, t.K, t.Ns, t.S, t.E, t.L, t.r,
+                                                      t.block_m, t.x_per_pair, "valu") for t in shapes)
+    ws = torch.zeros(need_max, dtype=torch.uint8, device=gh.DEV)
+    for i, s in enumerate(shapes):
+        M = s.M
+        assert _ksplit_kernel(s)
+        need = mla.fused_moe_lora_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                                  s.block_m, s.x_per_pair, "valu")
+        assert 0 < need <= ws.numel()
+        _log(f"k-split workspace reuse {name} call {i}: M={M} r={s.r}")
+        c = synth.draw(s)
+        dc = gh.DeviceCase(c)
+        al = dc.align()
+        y = _ws(dc, al, ws)
+        y0 = _ws(dc, al, ws, peer_wait=0)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), f"{name} M={M} r={s.r}"
+        ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping,
+                        c.topk_weights, c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+        gh.assert_fused_close(gh.bf16_host_f64(y).reshape(s.numel, s.N), ref, f"{name} M={M}")
