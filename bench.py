@@ -154,7 +154,7 @@ class DeviceSet:
             for k in ("topk_ids", "mapping", "w", "x", "a", "b", "y"):
                 setattr(self, k, getattr(proto, k).clone())
         self.align = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, dev)
-        ws = mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)
+        ws = mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.ws2 = None  # two-kernel workspace, allocated when that path is timed
 

@@ -75,7 +75,7 @@ MOE_LORA_API int64_t moe_lora_align_capacity(int64_t M, int32_t topk, int32_t E,
  * the single-workgroup path is taken).  Returns a negative status for
  * invalid sizes.  Host only.
  */
-MOE_LORA_API int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int32_t E,
+MOE_LORA_API int64_t moe_lora_align_workspace_size(int64_t M, int32_t topk, int32_t E,
                                        int32_t L, int32_t block_m);
 
 /*
@@ -100,7 +100,7 @@ MOE_LORA_API int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int
  *                       ascending, then -1 (the active-slot list of vLLM PR
  *                       #32005).
  *   num_active_loras    int32 [1] or NULL how many slots are active.
- *   workspace           [device] scratch of moe_lora_align_workspace_bytes()
+ *   workspace           [device] scratch of moe_lora_align_workspace_size()
  *                       bytes (may be NULL when that is 0); contents on entry
  *                       do not matter.
  * Pairs whose slot is outside [0, L) (including -1) or whose expert is
@@ -131,7 +131,7 @@ MOE_LORA_API int moe_lora_align(const int32_t *topk_ids, const int32_t *token_lo
  *     Calls in stream order are fine; nothing in the array needs clearing
  *     (its contents on entry do not matter).
  *   - MOE_LORA_ERR_WORKSPACE (nothing launched) when the sizes need more
- *     scratch than that (moe_lora_align_workspace_bytes() above the limit;
+ *     scratch than that (moe_lora_align_workspace_size() above the limit;
  *     no size the limits of this header allow does today).
  *   - MOE_LORA_ERR_HIP when the scratch's address cannot be found.
  * Other arguments, statuses and outputs as moe_lora_align.
@@ -169,6 +169,15 @@ enum moe_lora_variant {
  *   lora_b     bf16 [S, L, E, Ns, r]
  *   sorted_token_ids, expert_ids, num_tokens_post_padded: as produced by
  *              moe_lora_align for the same M, topk, E, L, block_m.
+ * [host] max_active_loras: at most this many slots have a non-empty row (the
+ *              pages' max_loras grid bound, vLLM PR #32005 diff; pass L when
+ *              unknown).  0 returns MOE_LORA_OK with nothing launched or read
+ *              (the no-LoRA batch, the pages' no_lora_flag); otherwise the
+ *              launch covers the blocks that many slots can hold.  With more
+ *              slots active than promised, blocks past that bound are not
+ *              computed.  MOE_LORA_ERR_INVALID outside [0, L].  (The kernels
+ *              find the active slots from num_tokens_post_padded on the
+ *              device, so the lora_ids list is not an argument.)
  *   topk_weights fp32 [M, topk]; may be NULL when mul_routed_weight == 0.
  * In/out [device]:
  *   y          bf16 [M, topk, S*Ns]
@@ -181,7 +190,7 @@ enum moe_lora_variant {
 MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
                    const uint16_t *lora_a, const uint16_t *lora_b,
                    const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                   const int32_t *num_tokens_post_padded,
+                   const int32_t *num_tokens_post_padded, int32_t max_active_loras,
                    const float *topk_weights, int32_t mul_routed_weight,
                    int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
@@ -222,7 +231,7 @@ MOE_LORA_API int fused_moe_lora(const uint16_t *x, int32_t x_per_pair,
 MOE_LORA_API int fused_moe_lora_ws(const uint16_t *x, int32_t x_per_pair,
                    const uint16_t *lora_a, const uint16_t *lora_b,
                    const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                   const int32_t *num_tokens_post_padded,
+                   const int32_t *num_tokens_post_padded, int32_t max_active_loras,
                    const float *topk_weights, int32_t mul_routed_weight,
                    int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,
@@ -380,7 +389,7 @@ MOE_LORA_API int64_t fused_moe_lora_two_kernel_workspace_bytes(int64_t M, int32_
 MOE_LORA_API int fused_moe_lora_two_kernel(const uint16_t *x, int32_t x_per_pair,
                    const uint16_t *lora_a, const uint16_t *lora_b,
                    const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                   const int32_t *num_tokens_post_padded,
+                   const int32_t *num_tokens_post_padded, int32_t max_active_loras,
                    const float *topk_weights, int32_t mul_routed_weight,
                    int32_t add_inputs, int64_t M, int32_t topk, int32_t K,
                    int32_t Ns, int32_t S, int32_t E, int32_t L, int32_t r,

@@ -29,20 +29,20 @@ _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 SIGNATURES = {
     "moe_lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_lora_align_capacity": (_I64, [_I64, _I32, _I32, _I32]),
-    "moe_lora_align_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_lora_align_workspace_size": (_I64, [_I64, _I32, _I32, _I32, _I32]),
     "moe_lora_align": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
                                       _P, _P, _P, _I64, _P]),
     "moe_lora_align_noalloc": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P,
                                               _P, _P, _P, _P]),
-    "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+    "fused_moe_lora": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I64,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                       _I32, _P]),
     "fused_moe_lora_with_align": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P,
                                                  _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                                  _I32, _I32, _I32, _I32, _P, _I32, _P]),
-    "fused_moe_lora_ws": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
-                                         _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
-                                         _I32, _P, _I64, _I32, _P]),
+    "fused_moe_lora_ws": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                         _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                         _P, _I32, _P, _I64, _I32, _P]),
     "fused_moe_lora_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _I32]),
     "fused_moe_lora_variant": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -54,9 +54,9 @@ SIGNATURES = {
                                             _I32, _P]),
     "fused_moe_lora_two_kernel_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32, _I32, _I32, _I32,
                                                          _I32, _I32, _I32]),
-    "fused_moe_lora_two_kernel": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32,
-                                                 _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
-                                                 _I32, _P, _P, _I64, _P]),
+    "fused_moe_lora_two_kernel": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I32, _P, _I32,
+                                                 _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                 _I32, _I32, _P, _P, _I64, _P]),
     "moe_lora_accumulate": (ctypes.c_int, [_P, _P, _I64, _P]),
 }
 
@@ -103,10 +103,10 @@ def align_capacity(M: int, topk: int, E: int, block_m: int) -> int:
     return int(v)
 
 
-def align_workspace_bytes(M: int, topk: int, E: int, L: int, block_m: int) -> int:
-    v = lib().moe_lora_align_workspace_bytes(M, topk, E, L, block_m)
+def align_workspace_size(M: int, topk: int, E: int, L: int, block_m: int) -> int:
+    v = lib().moe_lora_align_workspace_size(M, topk, E, L, block_m)
     if v < 0:
-        raise MoeLoraError(v, "moe_lora_align_workspace_bytes")
+        raise MoeLoraError(v, "moe_lora_align_workspace_size")
     return int(v)
 
 
@@ -186,7 +186,7 @@ def moe_lora_align(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *
     M, topk = topk_ids.shape
     if out is None:
         out = alloc_align_output(M, topk, E, L, block_m, dev)
-    ws_bytes = align_workspace_bytes(M, topk, E, L, block_m)
+    ws_bytes = align_workspace_size(M, topk, E, L, block_m)
     if ws_bytes > 0 and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     rc = lib().moe_lora_align(
@@ -252,8 +252,10 @@ def _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair):
 
 def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
                    mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
-                   variant: str | int = "auto", stream=None):
-    """Y (+)= (X A^T) B^T per routed pair and slice, in place on y; see moe_lora.h."""
+                   variant: str | int = "auto", max_active_loras: int | None = None,
+                   stream=None):
+    """Y (+)= (X A^T) B^T per routed pair and slice, in place on y; see moe_lora.h.
+    max_active_loras: host-side bound on the active slots (None: L; 0: no launch)."""
     M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
     if align.sorted_token_ids.shape[0] != L:
         raise ValueError("align output was made for another L")
@@ -261,7 +263,8 @@ def fused_moe_lora(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
     rc = lib().fused_moe_lora(
         _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
         _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
-        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        _dptr(align.num_tokens_post_padded), L if max_active_loras is None else int(max_active_loras),
+        _dptr(topk_weights),
         int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
         align.block_m, _dptr(y), v, _stream_ptr(stream))
     if rc != OK:
@@ -293,7 +296,7 @@ def alloc_fused_workspace(M: int, topk: int, K: int, Ns: int, S: int, E: int, L:
 def fused_moe_lora_ws(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
                       mul_routed_weight: bool, add_inputs: bool, workspace,
                       x_per_pair: bool = False, variant: str | int = "auto",
-                      peer_wait: int = -1, stream=None):
+                      peer_wait: int = -1, max_active_loras: int | None = None, stream=None):
     """fused_moe_lora with a K-split workspace (zero-filled before first use); see moe_lora.h."""
     M, topk, K, Ns, S, E, L, r = _fused_shapes(x, lora_a, lora_b, topk_weights, y, x_per_pair)
     if align.sorted_token_ids.shape[0] != L:
@@ -303,7 +306,8 @@ def fused_moe_lora_ws(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
     rc = lib().fused_moe_lora_ws(
         _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
         _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
-        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        _dptr(align.num_tokens_post_padded), L if max_active_loras is None else int(max_active_loras),
+        _dptr(topk_weights),
         int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
         align.block_m, _dptr(y), v, _dptr(workspace), nbytes, int(peer_wait),
         _stream_ptr(stream))
@@ -372,7 +376,7 @@ def two_kernel_workspace_bytes(M: int, topk: int, K: int, Ns: int, S: int, E: in
 
 def fused_moe_lora_two_kernel(x, lora_a, lora_b, align: AlignOutput, topk_weights, y, *,
                               mul_routed_weight: bool, add_inputs: bool, x_per_pair: bool = False,
-                              workspace=None, stream=None):
+                              workspace=None, max_active_loras: int | None = None, stream=None):
     """fused_moe_lora as shrink + expand with the rank vectors in `workspace` (ranks up to
     TWO_KERNEL_MAX_RANK); see moe_lora.h."""
     import torch
@@ -386,7 +390,8 @@ def fused_moe_lora_two_kernel(x, lora_a, lora_b, align: AlignOutput, topk_weight
     rc = lib().fused_moe_lora_two_kernel(
         _dptr(x), int(bool(x_per_pair)), _dptr(lora_a), _dptr(lora_b),
         _dptr(align.sorted_token_ids), _dptr(align.expert_ids),
-        _dptr(align.num_tokens_post_padded), _dptr(topk_weights),
+        _dptr(align.num_tokens_post_padded), L if max_active_loras is None else int(max_active_loras),
+        _dptr(topk_weights),
         int(bool(mul_routed_weight)), int(bool(add_inputs)), M, topk, K, Ns, S, E, L, r,
         align.block_m, _dptr(y), _dptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_ptr(stream))

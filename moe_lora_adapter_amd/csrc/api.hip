@@ -115,7 +115,7 @@ int64_t moe_lora_align_capacity(int64_t M, int32_t topk, int32_t E, int32_t bloc
   return rc != MOE_LORA_OK ? rc : cap;
 }
 
-int64_t moe_lora_align_workspace_bytes(int64_t M, int32_t topk, int32_t E, int32_t L,
+int64_t moe_lora_align_workspace_size(int64_t M, int32_t topk, int32_t E, int32_t L,
                                        int32_t block_m) {
   int64_t numel, cap;
   const int rc = check_sizes(M, topk, E, L, block_m, &numel, &cap);
@@ -257,6 +257,7 @@ static int64_t fused_exchange_bytes(int64_t M, int32_t topk, int32_t K, int32_t 
 static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
                         const uint16_t* lora_b, const int32_t* sorted_token_ids,
                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                        int32_t max_active_loras,
                         const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
                         int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                         int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
@@ -273,13 +274,16 @@ static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* l
   if (N > kInt32Max || numel * N / N != numel) return MOE_LORA_ERR_UNSUPPORTED;
   if (variant == MOE_LORA_VARIANT_MFMA && !mfma_ok(M, numel, K, Ns, N, r, block_m, x_per_pair))
     return MOE_LORA_ERR_UNSUPPORTED;
-  if (numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
+  if (max_active_loras < 0 || max_active_loras > L) return MOE_LORA_ERR_INVALID;
+  // no pair, or no active slot: nothing is read or written, nothing launched
+  if (numel == 0 || max_active_loras == 0) return MOE_LORA_OK;
   if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
       !num_tokens_post_padded || !y || (mul_routed_weight && !topk_weights))
     return MOE_LORA_ERR_INVALID;
   if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y))
     return MOE_LORA_ERR_INVALID;
-  const int64_t gmax = max_total_blocks(numel, int64_t(L) * E, block_m);
+  // the grid covers the blocks at most max_active_loras slots can hold
+  const int64_t gmax = max_total_blocks(numel, int64_t(max_active_loras) * E, block_m);
   const int64_t units = gmax * S;
   if (units * 64 > kInt32Max) return MOE_LORA_ERR_UNSUPPORTED;
 
@@ -324,13 +328,15 @@ static int fused_sorted(const uint16_t* x, int32_t x_per_pair, const uint16_t* l
 int fused_moe_lora(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
                    const uint16_t* lora_b, const int32_t* sorted_token_ids,
                    const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                   const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                   int32_t max_active_loras, const float* topk_weights,
+                   int32_t mul_routed_weight, int32_t add_inputs,
                    int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                    int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
                    void* stream) {
   return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
-                      num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
-                      K, Ns, S, E, L, r, block_m, y, variant, nullptr, 0, 0, stream);
+                      num_tokens_post_padded, max_active_loras, topk_weights, mul_routed_weight,
+                      add_inputs, M, topk, K, Ns, S, E, L, r, block_m, y, variant, nullptr, 0, 0,
+                      stream);
 }
 
 int64_t fused_moe_lora_workspace_bytes(int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S,
@@ -342,18 +348,21 @@ int64_t fused_moe_lora_workspace_bytes(int64_t M, int32_t topk, int32_t K, int32
 int fused_moe_lora_ws(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
                       const uint16_t* lora_b, const int32_t* sorted_token_ids,
                       const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                      const float* topk_weights, int32_t mul_routed_weight, int32_t add_inputs,
+                      int32_t max_active_loras, const float* topk_weights,
+                      int32_t mul_routed_weight, int32_t add_inputs,
                       int64_t M, int32_t topk, int32_t K, int32_t Ns, int32_t S, int32_t E,
                       int32_t L, int32_t r, int32_t block_m, uint16_t* y, int32_t variant,
                       void* workspace, int64_t workspace_bytes, int32_t peer_wait, void* stream) {
   const int64_t need = fused_exchange_bytes(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, variant);
   if (need < 0) return int(need);
   if (workspace_bytes < 0) return MOE_LORA_ERR_INVALID;
-  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+  // max_active_loras == 0 launches nothing (fused_sorted), so no area is needed
+  if (need > 0 && max_active_loras != 0 &&
+      (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return MOE_LORA_ERR_WORKSPACE;
   return fused_sorted(x, x_per_pair, lora_a, lora_b, sorted_token_ids, expert_ids,
-                      num_tokens_post_padded, topk_weights, mul_routed_weight, add_inputs, M, topk,
-                      K, Ns, S, E, L, r, block_m, y, variant,
+                      num_tokens_post_padded, max_active_loras, topk_weights, mul_routed_weight,
+                      add_inputs, M, topk, K, Ns, S, E, L, r, block_m, y, variant,
                       need > 0 ? static_cast<int32_t*>(workspace) : nullptr, workspace_bytes,
                       peer_wait, stream);
 }
@@ -531,7 +540,8 @@ int64_t fused_moe_lora_two_kernel_workspace_bytes(int64_t M, int32_t topk, int32
 int fused_moe_lora_two_kernel(const uint16_t* x, int32_t x_per_pair, const uint16_t* lora_a,
                               const uint16_t* lora_b, const int32_t* sorted_token_ids,
                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                              const float* topk_weights, int32_t mul_routed_weight,
+                              int32_t max_active_loras, const float* topk_weights,
+                              int32_t mul_routed_weight,
                               int32_t add_inputs, int64_t M, int32_t topk, int32_t K, int32_t Ns,
                               int32_t S, int32_t E, int32_t L, int32_t r, int32_t block_m,
                               uint16_t* y, void* workspace, int64_t workspace_bytes,
@@ -540,9 +550,10 @@ int fused_moe_lora_two_kernel(const uint16_t* x, int32_t x_per_pair, const uint1
   const int rc = plan_two_kernel(M, topk, K, Ns, S, E, L, r, block_m, x_per_pair, &t);
   if (rc != MOE_LORA_OK) return rc;
   if ((mul_routed_weight != 0 && mul_routed_weight != 1) || (add_inputs != 0 && add_inputs != 1) ||
-      workspace_bytes < 0)
+      workspace_bytes < 0 || max_active_loras < 0 || max_active_loras > L)
     return MOE_LORA_ERR_INVALID;
-  if (t.numel == 0) return MOE_LORA_OK;  // no pair: nothing is read or written
+  // no pair, or no active slot: nothing is read or written, nothing launched
+  if (t.numel == 0 || max_active_loras == 0) return MOE_LORA_OK;
   if (!x || !lora_a || !lora_b || !sorted_token_ids || !expert_ids ||
       !num_tokens_post_padded || !y || (mul_routed_weight && !topk_weights))
     return MOE_LORA_ERR_INVALID;
@@ -575,7 +586,8 @@ int fused_moe_lora_two_kernel(const uint16_t* x, int32_t x_per_pair, const uint1
   p.N = int32_t(t.N);
   p.cap = int32_t(t.cap);
   p.nb = int32_t(t.cap / block_m);
-  p.units = int32_t(t.units);
+  // the grid covers the blocks at most max_active_loras slots can hold
+  p.units = int32_t(max_total_blocks(t.numel, int64_t(max_active_loras) * E, block_m) * S);
   p.xcd_cus = xcd_compute_units();
   p.ws = static_cast<float*>(workspace);
   p.kz = t.kz;

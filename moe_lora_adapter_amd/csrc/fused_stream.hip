@@ -451,7 +451,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // column split with columns) each multiply stages [ka0, ka0 + nA) of the
   // nA_all A stages and meet before the expand
   const int C = (p.Ns + nsz - 1) / nsz;
-  const bool xch = XCH && C > 1 && C <= kMaxPeers;
+  // (a unit past the slots the area holds -- only when more slots are active
+  // than the call's max_active_loras promised -- multiplies all of A itself)
+  const bool xch = XCH && C > 1 && C <= kMaxPeers && (unit + 1) * p.xch_passes <= p.xch_nslot;
   const int nA_all = (p.K + G::KT - 1) / G::KT;
   const int ka0 = xch ? split * nA_all / C : 0;
   const int nA = xch ? (split + 1) * nA_all / C - ka0 : nA_all;

@@ -80,14 +80,16 @@ class DeviceCase:
         s = self.s
         return mla.moe_lora_align(self.topk_ids, self.mapping, s.E, s.L, s.block_m)
 
-    def fused(self, align=None, variant="auto", y=None, add=None, mul=None, b=None, a=None):
+    def fused(self, align=None, variant="auto", y=None, add=None, mul=None, b=None, a=None,
+              max_active=None):
         s = self.s
         align = align if align is not None else self.align()
         y = self.y_in.clone() if y is None else y
         mla.fused_moe_lora(self.x, self.a if a is None else a, self.b if b is None else b, align,
                            self.w, y, mul_routed_weight=s.mul if mul is None else mul,
                            add_inputs=s.add if add is None else add,
-                           x_per_pair=s.x_per_pair, variant=variant)
+                           x_per_pair=s.x_per_pair, variant=variant,
+                           max_active_loras=max_active)
         torch.cuda.synchronize()
         return y
 

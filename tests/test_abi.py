@@ -45,9 +45,9 @@ def test_capacity_matches_oracle_and_bound():
 
 
 def test_workspace_query():
-    assert mla.align_workspace_bytes(16, 4, 32, 6, 16) == 0          # one workgroup
-    assert mla.align_workspace_bytes(65536, 8, 256, 16, 64) > 0      # tiles
-    assert mla.align_workspace_bytes(0, 4, 32, 6, 16) == 0
+    assert mla.align_workspace_size(16, 4, 32, 6, 16) == 0          # one workgroup
+    assert mla.align_workspace_size(65536, 8, 256, 16, 64) > 0      # tiles
+    assert mla.align_workspace_size(0, 4, 32, 6, 16) == 0
 
 
 def align_call(**kw):
@@ -115,18 +115,19 @@ def test_align_noalloc_scratch_covers_every_accepted_size():
     for M, topk, E, L, B in ((65536, 8, 256, 16, 64), (2 ** 22, 8, 1024, 8, 128),
                              (2 ** 20, 1, 1, 1024, 16), (10 ** 6, 1, 1024, 8, 16),
                              (5000, 4, 2, 1, 16)):
-        assert mla.align_workspace_bytes(M, topk, E, L, B) <= mla.ALIGN_NOALLOC_SCRATCH_BYTES
+        assert mla.align_workspace_size(M, topk, E, L, B) <= mla.ALIGN_NOALLOC_SCRATCH_BYTES
 
 
 def fused_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
-             variant=0)
+             variant=0, act=None)
     a.update(kw)
+    act = a["L"] if a["act"] is None else a["act"]
     return mla.lib().fused_moe_lora(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"], a["eids"],
-                                    a["ntpp"], a["w"], a["mul"], a["add"], a["M"], a["topk"],
-                                    a["K"], a["Ns"], a["S"], a["E"], a["L"], a["r"], a["B"],
-                                    a["y"], a["variant"], None)
+                                    a["ntpp"], act, a["w"], a["mul"], a["add"], a["M"],
+                                    a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"], a["r"],
+                                    a["B"], a["y"], a["variant"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -152,6 +153,11 @@ def fused_call(**kw):
     (dict(y=V(18)), mla.ERR_INVALID),
     (dict(M=0), mla.OK),
     (dict(M=0, x=None, y=None, sorted=None, eids=None), mla.OK),
+    (dict(act=-1), mla.ERR_INVALID),
+    (dict(act=7), mla.ERR_INVALID),
+    # no active slot: nothing is launched or read, not even the pointers
+    (dict(act=0), mla.OK),
+    (dict(act=0, x=None, la=None, lb=None, y=None, sorted=None, eids=None, ntpp=None), mla.OK),
 ])
 def test_fused_rejects(kw, status):
     assert fused_call(**kw) == status
@@ -282,11 +288,12 @@ def test_with_align_rejects(kw, status):
 def ws_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=64, B=16, y=P16,
-             variant=1, ws=P16, ws_bytes=1 << 40, wait=-1)
+             variant=1, ws=P16, ws_bytes=1 << 40, wait=-1, act=None)
     a.update(kw)
+    act = a["L"] if a["act"] is None else a["act"]
     return mla.lib().fused_moe_lora_ws(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"],
-                                       a["eids"], a["ntpp"], a["w"], a["mul"], a["add"], a["M"],
-                                       a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"],
+                                       a["eids"], a["ntpp"], act, a["w"], a["mul"], a["add"],
+                                       a["M"], a["topk"], a["K"], a["Ns"], a["S"], a["E"], a["L"],
                                        a["r"], a["B"], a["y"], a["variant"], a["ws"],
                                        a["ws_bytes"], a["wait"], None)
 
@@ -305,6 +312,10 @@ def ws_call(**kw):
     (dict(ws=V(24)), mla.ERR_WORKSPACE),
     (dict(M=0), mla.OK),
     (dict(M=0, x=None, y=None, sorted=None, ws=None, ws_bytes=0), mla.OK),
+    (dict(act=-1), mla.ERR_INVALID),
+    (dict(act=7), mla.ERR_INVALID),
+    (dict(act=7, ws=None), mla.ERR_WORKSPACE),
+    (dict(act=0, x=None, y=None, sorted=None, ntpp=None, ws=None, ws_bytes=0), mla.OK),
 ])
 def test_fused_ws_rejects(kw, status):
     assert ws_call(**kw) == status
@@ -337,13 +348,14 @@ def test_fused_workspace_query():
 def two_call(**kw):
     a = dict(x=P16, xpp=0, la=P16, lb=P16, sorted=P16, eids=P16, ntpp=P16, w=None, mul=0,
              add=1, M=16, topk=4, K=2880, Ns=2880, S=2, E=32, L=6, r=256, B=16, y=P16,
-             ws=P16, ws_bytes=1 << 40)
+             ws=P16, ws_bytes=1 << 40, act=None)
     a.update(kw)
+    act = a["L"] if a["act"] is None else a["act"]
     return mla.lib().fused_moe_lora_two_kernel(a["x"], a["xpp"], a["la"], a["lb"], a["sorted"],
-                                               a["eids"], a["ntpp"], a["w"], a["mul"], a["add"],
-                                               a["M"], a["topk"], a["K"], a["Ns"], a["S"],
-                                               a["E"], a["L"], a["r"], a["B"], a["y"], a["ws"],
-                                               a["ws_bytes"], None)
+                                               a["eids"], a["ntpp"], act, a["w"], a["mul"],
+                                               a["add"], a["M"], a["topk"], a["K"], a["Ns"],
+                                               a["S"], a["E"], a["L"], a["r"], a["B"], a["y"],
+                                               a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -370,6 +382,9 @@ def two_call(**kw):
     (dict(x=V(24)), mla.ERR_INVALID),
     (dict(M=0), mla.OK),
     (dict(M=0, x=None, y=None, sorted=None, ws=None), mla.OK),
+    (dict(act=-1), mla.ERR_INVALID),
+    (dict(act=7), mla.ERR_INVALID),
+    (dict(act=0, x=None, la=None, y=None, ntpp=None, ws=None), mla.OK),
 ])
 def test_two_kernel_rejects(kw, status):
     assert two_call(**kw) == status

@@ -62,7 +62,7 @@ def test_one_graph_all_active_counts(name, path):
     mapping = dc.mapping            # rewritten in place between replays
     y = dc.y_in.clone()
     al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
-    ws = torch.empty(max(16, mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)),
+    ws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)),
                      dtype=torch.uint8, device=gh.DEV)
     ws2 = torch.empty(max(16, mla.two_kernel_workspace_bytes(s.M, s.topk, s.K, s.Ns, s.S, s.E,
                                                              s.L, s.r, s.block_m, s.x_per_pair)),

@@ -19,6 +19,7 @@ stream kernel, ranks 32, 64, 128).  Checked here:
   that workspace;
 - one captured graph, replayed with the slot mapping rewritten in place
   between replays, matches eager calls bit for bit;
+- a launch bounded by max_active_loras equals the one bounded by L;
 - the workspace checks of the entry point.
 """
 import sys
@@ -69,13 +70,13 @@ def _ksplit_kernel(s):
                                  s.x_per_pair, "valu") == "fused_stream_kernel"
 
 
-def _ws(dc, align, ws, y=None, peer_wait=-1, add=None, stream=None):
+def _ws(dc, align, ws, y=None, peer_wait=-1, add=None, stream=None, max_active=None):
     s = dc.s
     y = dc.y_in.clone() if y is None else y
     mla.fused_moe_lora_ws(dc.x, dc.a, dc.b, align, dc.w, y, mul_routed_weight=s.mul,
                           add_inputs=s.add if add is None else add, workspace=ws,
                           x_per_pair=s.x_per_pair, variant="valu", peer_wait=peer_wait,
-                          stream=stream)
+                          max_active_loras=max_active, stream=stream)
     return y
 
 
@@ -126,6 +127,33 @@ def test_k_split_edge_shapes(orc, i):
     _check_case(orc, s, f"edge {i}")
 
 
+@pytest.mark.parametrize("name", ["oss20b_decode_w13_a6", "oss20b_decode_w13_a3"])
+def test_k_split_max_active_loras(orc, name):
+    """A launch bounded by the active-slot count uses fewer exchange slots of
+    the same workspace and writes the same bits as the one bounded by L."""
+    s = synth.shape(name, dist="stress")
+    c = synth.draw(s)
+    m = c.token_lora_mapping
+    keep = (c.active_slots[0], c.active_slots[-1])   # two of the filled slots only
+    c.token_lora_mapping = np.where(m >= 0, np.where(m % 2 == 0, keep[0], keep[1]),
+                                    m).astype(m.dtype)
+    dc = gh.DeviceCase(c)
+    al = dc.align()
+    ws = _workspace(s)
+    torch.cuda.synchronize()
+    nact = int(al.num_active_loras.item())
+    _log(f"k-split max_active {name} nact={nact}")
+    full = _ws(dc, al, ws)
+    bound = _ws(dc, al, ws, max_active=nact)
+    none = _ws(dc, al, ws, max_active=0)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), bound.view(torch.int16))
+    assert torch.equal(none.view(torch.int16), dc.y_in.view(torch.int16))
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+    gh.assert_fused_close(gh.bf16_host_f64(bound).reshape(s.numel, s.N), ref, name)
+
+
 def test_k_split_rank_vector_precision(orc):
     """With add_inputs = 0, Y differs from the exact delta by the output's bf16
     rounding and a small absolute term, as for fused_moe_lora."""
@@ -154,7 +182,7 @@ def test_k_split_one_graph_across_active_counts(orc):
     dc.b = torch.from_numpy(b).to(gh.DEV).to(torch.bfloat16)
     mapping = dc.mapping
     al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
-    aws = torch.empty(max(16, mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)),
+    aws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)),
                       dtype=torch.uint8, device=gh.DEV)
     ws = _workspace(s)
     y = dc.y_in.clone()

@@ -45,7 +45,7 @@ def _mfma_ok(s):
     # probe with a zero-sized call: MOE_LORA_ERR_UNSUPPORTED means not available
     rc = mla.lib().fused_moe_lora(ctypes.c_void_p(16), 0, ctypes.c_void_p(16), ctypes.c_void_p(16),
                                   ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
-                                  None, 0, 1, 0, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
+                                  s.L, None, 0, 1, 0, s.topk, s.K, s.Ns, s.S, s.E, s.L, s.r,
                                   s.block_m, ctypes.c_void_p(16), 2, None)
     return rc == 0
 
@@ -344,6 +344,35 @@ def test_fused_no_mapped_token_and_empty_batch():
                        add_inputs=True)
 
 
+@pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "oss120b_decode_w13",
+                                  "qwen3_prefill"])
+def test_fused_max_active_loras(orc, name):
+    """A batch that uses two of the L slots: the launch bounded by
+    max_active_loras = 2 writes the same bits as the one bounded by L (and
+    matches the oracle); max_active_loras = 0 launches nothing."""
+    s = synth.shape(name)
+    c = synth.draw(s)
+    m = c.token_lora_mapping
+    keep = (c.active_slots[0], c.active_slots[-1])   # two of the filled slots only
+    c.token_lora_mapping = np.where(m >= 0, np.where(m % 2 == 0, keep[0], keep[1]), m).astype(m.dtype)
+    dc = gh.DeviceCase(c)
+    al = dc.align()
+    torch.cuda.synchronize()
+    nact = int(al.num_active_loras.item())
+    assert nact <= 2
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+    for variant in _variants(s):
+        _log(f"fused max_active {name} {variant} nact={nact}")
+        full = dc.fused(align=al, variant=variant)
+        bound = dc.fused(align=al, variant=variant, max_active=nact)
+        assert torch.equal(full.view(torch.int16), bound.view(torch.int16)), variant
+        got = gh.bf16_host_f64(bound).reshape(s.numel, s.N)
+        gh.assert_fused_close(got, ref, f"{name}/{variant}/max_active={nact}")
+        none = dc.fused(align=al, variant=variant, max_active=0)
+        assert torch.equal(none.view(torch.int16), dc.y_in.view(torch.int16))
+
+
 # ------------------------------------------------------------------ graph capture
 @pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "qwen3_prefill"])
 def test_graph_replay_matches_eager(name):
@@ -355,7 +384,7 @@ def test_graph_replay_matches_eager(name):
     variants = _variants(s)
     eager = {v: dc.fused(variant=v) for v in variants}
     al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
-    ws = torch.empty(max(16, mla.align_workspace_bytes(s.M, s.topk, s.E, s.L, s.block_m)),
+    ws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)),
                      dtype=torch.uint8, device=gh.DEV)
     for v in variants:
         _log(f"graph replay {name} {v}")

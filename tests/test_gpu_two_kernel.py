@@ -34,13 +34,13 @@ def orc():
     return oracle.load()
 
 
-def _two(dc, align=None, y=None, add=None):
+def _two(dc, align=None, y=None, add=None, max_active=None):
     s = dc.s
     align = align if align is not None else dc.align()
     y = dc.y_in.clone() if y is None else y
     mla.fused_moe_lora_two_kernel(dc.x, dc.a, dc.b, align, dc.w, y, mul_routed_weight=s.mul,
                                   add_inputs=s.add if add is None else add,
-                                  x_per_pair=s.x_per_pair)
+                                  x_per_pair=s.x_per_pair, max_active_loras=max_active)
     torch.cuda.synchronize()
     return y
 
@@ -91,6 +91,28 @@ def test_two_kernel_edge_shapes(orc, i):
     s = synth.shape("tiny", dist="stress", seed=9700 + i, **TWO_EDGE[i])
     _log(f"two-kernel edge {i} {TWO_EDGE[i]}")
     _full(orc, s, f"edge {i}")
+
+
+def test_two_kernel_max_active_loras(orc):
+    """Bounded by the active-slot count: the same bits as bounded by L; 0
+    launches nothing."""
+    s = synth.shape("tiny", dist="stress", seed=9760, K=264, Ns=136, r=256, M=64, E=4,
+                    topk=2, L=6, active=6)
+    c = synth.draw(s)
+    m = c.token_lora_mapping
+    c.token_lora_mapping = np.where(m >= 0, 5 * (m % 2), m).astype(m.dtype)  # slots 0 and 5 of 6
+    dc = gh.DeviceCase(c)
+    al = dc.align()
+    torch.cuda.synchronize()
+    nact = int(al.num_active_loras.item())
+    full = _two(dc, align=al)
+    bound = _two(dc, align=al, max_active=nact)
+    assert torch.equal(full.view(torch.int16), bound.view(torch.int16))
+    none = _two(dc, align=al, max_active=0)
+    assert torch.equal(none.view(torch.int16), dc.y_in.view(torch.int16))
+    ref = orc.fused(c.x, c.lora_a, c.lora_b, c.topk_ids, c.token_lora_mapping, c.topk_weights,
+                    c.y_in, s.mul, s.add, x_per_pair=s.x_per_pair)
+    gh.assert_fused_close(gh.bf16_host_f64(bound).reshape(s.numel, s.N), ref, "max_active")
 
 
 @pytest.mark.parametrize("dist", ["literal", "stress"])

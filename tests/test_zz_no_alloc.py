@@ -52,7 +52,7 @@ def test_noalloc_align_matches_workspace_align_twice_shrinking():
              (*_case(5003, 4, 64, 4, 32, 11), 64, 4, 32)]
     for i, (topk_ids, mapping, E, L, B) in enumerate(cases):
         M, topk = topk_ids.shape
-        assert mla.align_workspace_bytes(M, topk, E, L, B) > 0, "the case must use the scratch"
+        assert mla.align_workspace_size(M, topk, E, L, B) > 0, "the case must use the scratch"
         _log(f"no-alloc align call {i}: M={M} topk={topk} E={E} L={L} B={B}")
         got = _noalloc(topk_ids, mapping, E, L, B)
         ref_ws = gh.align_to_host(gh.run_align(topk_ids, mapping, E, L, B))
