@@ -97,6 +97,12 @@ def _catalog() -> dict:
             f"oss20b_decode_w13_a{a}", M=16, K=2880, Ns=2880, S=2, E=32, topk=4,
             L=6, r=64, block_m=16, active=a, p_neg=0.0, mul=False, add=True,
             seed=2000 + a)
+        # the same layer's down projection: X is the activation of the w13
+        # output, one row per pair, K = the w13 slice width
+        c[f"oss20b_decode_w2_a{a}"] = Shape(
+            f"oss20b_decode_w2_a{a}", M=16, K=2880, Ns=2880, S=1, E=32, topk=4,
+            L=6, r=64, block_m=16, active=a, p_neg=0.0, x_per_pair=True, mul=True,
+            add=True, seed=2010 + a)
     for i, (M, bm, tag) in enumerate(((8, 16, "decode"), (2048, 64, "prefill"))):
         c[f"oss120b_{tag}_w13"] = Shape(
             f"oss120b_{tag}_w13", M=M, K=2880, Ns=2880, S=2, E=128, topk=4, L=4,
@@ -177,6 +183,39 @@ def _normal_bf16(rng, size, scale):
     if scale != 1.0:
         a *= np.float32(scale)
     return f32_to_bf16_bits(a)
+
+
+def w2_partner(name: str) -> str:
+    """The down-projection (w2) workload of a w13 workload's layer."""
+    if "_w13" not in name or name.replace("_w13", "_w2") not in CATALOG:
+        raise KeyError(f"{name} has no w2 partner")
+    return name.replace("_w13", "_w2")
+
+
+def draw_layer(name13: str, **overrides) -> tuple:
+    """Both projections of one MoE layer: the w13 case and its w2 partner,
+    the latter with the w13 case's routing (slots, mapping, top-k ids and
+    weights) so that one align serves both.  The w2 case's X is drawn but a
+    layer feeds w2 the activation of the w13 output instead."""
+    s13 = shape(name13, **overrides)
+    s2 = shape(w2_partner(name13), **overrides)
+    if (s2.M, s2.topk, s2.E, s2.L, s2.block_m) != (s13.M, s13.topk, s13.E, s13.L, s13.block_m):
+        raise ValueError("w13 and w2 workloads of one layer must share the routing sizes")
+    if s2.active != s13.active:
+        raise ValueError("w13 and w2 workloads of one layer must have the same active count")
+    c13, c2 = draw(s13), draw(s2)
+    # the w2 adapters drawn into c2's own active slots move to c13's
+    src, dst = c2.active_slots, c13.active_slots
+    for name in ("lora_a", "lora_b"):
+        arr = getattr(c2, name)
+        moved = np.zeros_like(arr)
+        moved[:, dst] = arr[:, src]
+        setattr(c2, name, moved)
+    c2.active_slots = dst.copy()
+    c2.token_lora_mapping = c13.token_lora_mapping.copy()
+    c2.topk_ids = c13.topk_ids.copy()
+    c2.topk_weights = c13.topk_weights.copy()
+    return c13, c2
 
 
 def draw(s: Shape, with_tensors: bool = True) -> Case:

@@ -100,3 +100,22 @@ def test_step_path_resolution():
     assert bench.resolve_path("auto", synth.shape("tiny", M=17, topk=4)) == "sorted"  # 68 pairs
     assert bench.resolve_path("auto", synth.shape("tiny", L=65, E=2, active=2)) == "sorted"
     assert bench.resolve_path("sorted", synth.shape("tiny")) == "sorted"
+
+
+@pytest.mark.parametrize("name", ["oss20b_decode_w13_a6", "oss20b_decode_w13_a2",
+                                  "oss120b_decode_w13"])
+def test_draw_layer_shares_the_routing(name):
+    """The w2 case of a layer takes the w13 case's routing, and its adapters
+    sit in exactly the slots that routing uses."""
+    c13, c2 = synth.draw_layer(name)
+    s13, s2 = c13.shape, c2.shape
+    assert s2.x_per_pair and s2.K == s13.Ns and s2.name == synth.w2_partner(name)
+    for k in ("active_slots", "token_lora_mapping", "topk_ids", "topk_weights"):
+        assert np.array_equal(getattr(c13, k), getattr(c2, k)), k
+    filled = [l for l in range(s2.L) if c2.lora_a[:, l].any() or c2.lora_b[:, l].any()]
+    assert filled == sorted(c13.active_slots.tolist())
+    # the moved adapters are c2's own draw, not zeros and not w13's
+    own = synth.draw(s2)
+    assert np.array_equal(c2.lora_a[:, c13.active_slots], own.lora_a[:, own.active_slots])
+    with pytest.raises(KeyError):
+        synth.w2_partner("qwen3_prefill")

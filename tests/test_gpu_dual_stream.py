@@ -6,7 +6,14 @@ auxiliary stream; an event joins them and moe_lora_accumulate adds the delta.
 Checked against the oracle (Y_in + delta, tolerance 1e-2 (1 + |oracle|)),
 eagerly and captured in one graph; moe_lora_accumulate itself bit for bit
 against an fp32 add rounded to nearest even on the host.
+
+Also: the base MoE align (one slot, every token in it) and the LoRA align on
+two streams in one graph, both bit-exact against the oracle; and one MoE
+layer's w13 -> activation -> w2 chain with four events (moe_lora_adapter_amd.
+streams), each LoRA step against the oracle and the dual-stream run equal bit
+for bit to the serial one.
 """
+import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +97,242 @@ def test_dual_stream_matches_oracle_eager_and_in_a_graph(name):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
     check("graph")
+
+
+# ------------------------------------------------------------------ two-stream align
+def _host_i32(t):
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["oss20b_decode_w13_a6", "oss120b_prefill_w13", "qwen3_prefill",
+                                  "align_stress", "align_stress_neg"])
+def test_two_stream_align_in_one_graph(name):
+    """The base MoE align (one slot, every token mapped to it) on an auxiliary
+    stream beside the LoRA align on the main one, each with its own output and
+    workspace, captured in one graph: every replay writes both results bit for
+    bit as the oracle defines them."""
+    s = synth.shape(name)
+    c = synth.draw(s, with_tensors=False)
+    orc = oracle.load()
+    topk_ids = gh.i32_dev(c.topk_ids)
+    mapping = gh.i32_dev(c.token_lora_mapping)
+    zero_map = torch.zeros(s.M, dtype=torch.int32, device=gh.DEV)  # plain MoE: slot 0 for all
+    ref_lora = orc.align(c.topk_ids, c.token_lora_mapping, s.E, s.L, s.block_m)
+    ref_base = orc.align(c.topk_ids, np.zeros(s.M, np.int32), s.E, 1, s.block_m)
+    outs, wss = [], []
+    for L in (s.L, 1):
+        outs.append(mla.alloc_align_output(s.M, s.topk, s.E, L, s.block_m, gh.DEV))
+        nb = mla.align_workspace_size(s.M, s.topk, s.E, L, s.block_m)
+        wss.append(torch.empty(max(16, nb), dtype=torch.uint8, device=gh.DEV))
+    lora_out, base_out = outs
+    aux = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def both():
+        main = torch.cuda.current_stream()
+        fork.record(main)
+        aux.wait_event(fork)
+        with torch.cuda.stream(aux):
+            mla.moe_lora_align(topk_ids, zero_map, s.E, 1, s.block_m, out=base_out,
+                               workspace=wss[1])
+            join.record(aux)
+        mla.moe_lora_align(topk_ids, mapping, s.E, s.L, s.block_m, out=lora_out,
+                           workspace=wss[0])
+        main.wait_event(join)
+
+    def poison():
+        for o in outs:
+            for t in (o.sorted_token_ids, o.expert_ids, o.num_tokens_post_padded, o.lora_ids,
+                      o.num_active_loras):
+                t.fill_(-7)
+        torch.cuda.synchronize()
+
+    def check(what):
+        gh.assert_align_equal(gh.align_to_host(lora_out), ref_lora, s.block_m)
+        gh.assert_align_equal(gh.align_to_host(base_out), ref_base, s.block_m)
+
+    print(f"two-stream align {name}", flush=True)
+    poison()
+    both()
+    torch.cuda.synchronize()
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        both()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        both()
+    for rep in range(3):
+        poison()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"replay {rep}")
+        both()                                     # eager work between replays
+        torch.cuda.synchronize()
+        check(f"eager after replay {rep}")
+
+
+# ------------------------------------------------------------------ one MoE layer, four events
+class _Layer:
+    """One MoE layer's w13 -> activation -> w2 with the LoRA side forked off.
+
+    The base GEMMs are dense stand-ins (one shared matrix instead of one per
+    expert; the base MoE is the caller's, not this library's).  The w13 fork
+    also runs the base MoE align (one slot) beside the LoRA align."""
+
+    def __init__(self, c13, c2, seed=123):
+        from moe_lora_adapter_amd.streams import LoraStreams
+        s13, s2 = c13.shape, c2.shape
+        self.s13, self.s2 = s13, s2
+        self.d13, self.d2 = gh.DeviceCase(c13), gh.DeviceCase(c2)
+        dev = gh.DEV
+        M, topk, numel = s13.M, s13.topk, s13.numel
+        self.zero_map = torch.zeros(M, dtype=torch.int32, device=dev)
+        self.al = mla.alloc_align_output(M, topk, s13.E, s13.L, s13.block_m, dev)
+        self.al_ws = torch.empty(max(16, mla.align_workspace_size(M, topk, s13.E, s13.L,
+                                                                  s13.block_m)),
+                                 dtype=torch.uint8, device=dev)
+        self.base_al = mla.alloc_align_output(M, topk, s13.E, 1, s13.block_m, dev)
+        self.base_al_ws = torch.empty(max(16, mla.align_workspace_size(M, topk, s13.E, 1,
+                                                                       s13.block_m)),
+                                      dtype=torch.uint8, device=dev)
+        gen = torch.Generator().manual_seed(seed)
+        self.w13b = (torch.randn(s13.K, s13.N, generator=gen) / s13.K ** 0.5).to(torch.bfloat16).to(dev)
+        self.w2b = (torch.randn(s2.K, s2.N, generator=gen) / s2.K ** 0.5).to(torch.bfloat16).to(dev)
+        self.base1 = torch.empty(M, s13.N, dtype=torch.bfloat16, device=dev)
+        self.y1 = torch.empty(M, topk, s13.N, dtype=torch.bfloat16, device=dev)
+        self.delta1 = torch.empty_like(self.y1)
+        self.h = torch.empty(numel, s2.K, dtype=torch.bfloat16, device=dev)
+        self.base2 = torch.empty(numel, s2.N, dtype=torch.bfloat16, device=dev)
+        self.y2 = torch.empty(M, topk, s2.N, dtype=torch.bfloat16, device=dev)
+        self.delta2 = torch.empty_like(self.y2)
+        self.streams = LoraStreams()
+
+    def base13(self):
+        s = self.s13
+        mla.moe_lora_align(self.d13.topk_ids, self.zero_map, s.E, 1, s.block_m,
+                           out=self.base_al, workspace=self.base_al_ws)
+        torch.matmul(self.d13.x, self.w13b, out=self.base1)
+        self.y1.copy_(self.base1[:, None, :].expand(s.M, s.topk, s.N))
+
+    def lora13(self):
+        s, d = self.s13, self.d13
+        self.delta1.zero_()
+        mla.moe_lora_align(d.topk_ids, d.mapping, s.E, s.L, s.block_m, out=self.al,
+                           workspace=self.al_ws)
+        mla.fused_moe_lora(d.x, d.a, d.b, self.al, d.w, self.delta1, mul_routed_weight=s.mul,
+                           add_inputs=False)
+
+    def act(self):
+        s = self.s13
+        y = self.y1.view(s.numel, s.N)
+        if s.S == 2:       # gate and up slices (a stand-in SwiGLU)
+            torch.mul(torch.nn.functional.silu(y[:, :s.Ns]), y[:, s.Ns:], out=self.h)
+        else:
+            self.h.copy_(torch.nn.functional.silu(y))
+
+    def base2_fn(self):
+        torch.matmul(self.h, self.w2b, out=self.base2)
+        self.y2.view(self.s2.numel, self.s2.N).copy_(self.base2)
+
+    def lora2(self):
+        s, d = self.s2, self.d2
+        self.delta2.zero_()
+        mla.fused_moe_lora(self.h, d.a, d.b, self.al, d.w, self.delta2, mul_routed_weight=s.mul,
+                           add_inputs=False, x_per_pair=True)
+
+    def dual(self):
+        from moe_lora_adapter_amd.streams import W13, W2
+        self.streams.fork_join(W13, self.base13, self.lora13, self.y1, self.delta1)
+        self.act()
+        self.streams.fork_join(W2, self.base2_fn, self.lora2, self.y2, self.delta2)
+
+    def serial(self):
+        self.base13()
+        self.lora13()
+        mla.moe_lora_accumulate(self.y1, self.delta1)
+        self.act()
+        self.base2_fn()
+        self.lora2()
+        mla.moe_lora_accumulate(self.y2, self.delta2)
+
+    def results(self):
+        return [t.clone() for t in (self.y1, self.h, self.y2)]
+
+    def poison(self):
+        for t in (self.y1, self.delta1, self.h, self.y2, self.delta2, self.base1, self.base2):
+            t.fill_(5.0)
+        for o in (self.al, self.base_al):
+            o.sorted_token_ids.fill_(-7)
+            o.num_tokens_post_padded.fill_(-7)
+        torch.cuda.synchronize()
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _same(a, b):
+    return all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("name", ["oss20b_decode_w13_a6", "oss120b_decode_w13",
+                                  "oss120b_prefill_w13"])
+def test_layer_chain_four_events(name):
+    """w13 (LoRA ‖ base, join) -> activation -> w2 (LoRA with per-pair X ‖ base,
+    join), the LoRA side on an auxiliary stream: each LoRA step against the
+    oracle on the inputs it actually saw, both aligns bit-exact, and the
+    dual-stream run equal bit for bit to the serial one, eagerly and on every
+    replay of one captured graph."""
+    c13, c2 = synth.draw_layer(name, dist="stress")
+    s13, s2 = c13.shape, c2.shape
+    lay = _Layer(c13, c2)
+    orc = oracle.load()
+    print(f"layer chain {name}", flush=True)
+    lay.poison()
+    lay.serial()
+    torch.cuda.synchronize()
+    serial = lay.results()
+
+    # the LoRA align and the base MoE align
+    gh.assert_align_equal(gh.align_to_host(lay.al),
+                          orc.align(c13.topk_ids, c13.token_lora_mapping, s13.E, s13.L,
+                                    s13.block_m), s13.block_m)
+    gh.assert_align_equal(gh.align_to_host(lay.base_al),
+                          orc.align(c13.topk_ids, np.zeros(s13.M, np.int32), s13.E, 1,
+                                    s13.block_m), s13.block_m)
+    # w13: Y1 = base + LoRA delta
+    y1_in = np.broadcast_to(_bits(lay.base1)[:, None, :], (s13.M, s13.topk, s13.N)).copy()
+    ref1 = orc.fused(c13.x, c13.lora_a, c13.lora_b, c13.topk_ids, c13.token_lora_mapping,
+                     c13.topk_weights, y1_in, s13.mul, True)
+    gh.assert_fused_close(gh.bf16_host_f64(serial[0]).reshape(s13.numel, s13.N), ref1, "w13")
+    # w2: Y2 = base + LoRA delta of the activation (one X row per pair)
+    y2_in = _bits(lay.base2).reshape(s2.M, s2.topk, s2.N)
+    ref2 = orc.fused(_bits(serial[1]), c2.lora_a, c2.lora_b, c2.topk_ids, c2.token_lora_mapping,
+                     c2.topk_weights, y2_in, s2.mul, True, x_per_pair=True)
+    gh.assert_fused_close(gh.bf16_host_f64(serial[2]).reshape(s2.numel, s2.N), ref2, "w2")
+
+    lay.poison()
+    lay.dual()
+    torch.cuda.synchronize()
+    assert _same(lay.results(), serial), "dual-stream eager run differs from the serial one"
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lay.dual()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        lay.dual()
+    for rep in range(3):
+        lay.poison()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(lay.results(), serial), f"replay {rep}"
+        lay.serial()                               # eager work between replays
+        torch.cuda.synchronize()
