@@ -25,10 +25,18 @@ Timing:
     vectors through memory) on the same inputs, graph-timed with the align
     step and event-timed for its two kernels; one_shot_speedup is the latter
     over the fused kernel's time.
-  * dual_stream (batches of at most 1024 pairs): the LoRA side (align, fused
-    with add_inputs = 0 into a zero buffer, moe_lora_accumulate to join) on an
-    auxiliary stream beside a stand-in base GEMM that streams the same base
-    expert weights a decode step reads; each alone, serial and overlapped.
+  * layer_chain (decode workloads with a w2 partner): one MoE layer, w13 ->
+    activation -> w2, the LoRA side of each projection (align, fused with
+    add_inputs = 0 into a zero buffer, moe_lora_accumulate to join) on an
+    auxiliary stream with four events beside stand-in base GEMMs that stream
+    the base expert weights a decode step reads (and the base MoE align);
+    each side alone, serial and overlapped.  dual_stream: the same for one
+    projection, for the other decode workloads.
+  * align_stress: the align step alone at M = 65536, topk = 8, E = 256, L = 16.
+  * prefill: the Qwen3-MoE-like prefill (C4) -- fused kernel time, HBM
+    roofline, MFMA rate, and rocprofv3's MFMA counters when recorded for the
+    current sources -- so one default run covers both halves of the metric.
+  * value's spread: p10 / p50 / p90 over 9 replays of the same graph.
   * align_free (batches of at most 1024 pairs): fused_moe_lora_naive on the
     same inputs -- the decode path with no align launch -- at the workload's
     block_m and at block_m = 1.  ``--path naive`` times it as the step instead.
@@ -58,6 +66,7 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
 def log(msg):
@@ -221,9 +230,12 @@ def step(ds, s, variant):
 
 
 # ----------------------------------------------------------------- measurements
-def time_steps_graph(sets, s, variant, steps, fn=None):
+def time_steps_graph(sets, s, variant, steps, fn=None, replays=None, n_replays=9):
     """Capture `steps` steps (rotating over the copies) in one graph; replay.
-    `fn(ds)` replaces the align + fused step when given."""
+    `fn(ds)` replaces the align + fused step when given.  Returns the seconds
+    per step of the first timed replay; with a list in `replays`, the graph is
+    replayed `n_replays` times in all and every replay's seconds per step are
+    appended to it (the first included)."""
     import torch
     fn = fn or (lambda ds: step(ds, s, variant))
     g = torch.cuda.CUDAGraph()
@@ -242,7 +254,16 @@ def time_steps_graph(sets, s, variant, steps, fn=None):
     t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    first = (time.perf_counter() - t0) / steps
+    if replays is not None:
+        # more replays of the same graph, each bracketed the same way
+        replays.append(first)
+        for _ in range(n_replays - 1):
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            replays.append((time.perf_counter() - t0) / steps)
+    return first
 
 
 def time_kernel_events(sets, s, variant, which, launches):
@@ -267,6 +288,246 @@ def time_kernel_events(sets, s, variant, which, launches):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / launches
+
+
+def time_kernel_windows(sets, s, variant, which, launches, windows=5):
+    """time_kernel_events over several windows: (mean, p10, p90) of the
+    per-window averages, in us."""
+    w = [time_kernel_events(sets, s, variant, which, launches) for _ in range(windows)]
+    return float(np.mean(w)), float(np.percentile(w, 10)), float(np.percentile(w, 90))
+
+
+def spread(us_list):
+    a = np.asarray(us_list, dtype=np.float64)
+    return {"n": int(a.size), "p10": round(float(np.percentile(a, 10)), 3),
+            "p50": round(float(np.percentile(a, 50)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def load_counters(kernel, workload):
+    """MFMA counters of a kernel and workload (profiles/counters.json), or None
+    when the kernel's sources changed since they were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_sha") != kernel_sources_sha(kernel):
+        return None
+    return rec
+
+
+def prefill_line(args, dev, variant):
+    """The prefill half of the metric: the Qwen3-MoE-like prefill (M = 8192,
+    topk = 8, E = 128, L = 8 with 3 active, r = 128, K = 2048, N = 2 x 768,
+    BLOCK_M = 64), cold inputs, the fused kernel event-timed, its HBM
+    roofline and its MFMA rate (algorithmic and, when recorded for these
+    sources, rocprofv3's MfmaUtil / MfmaFlopsBF16)."""
+    import torch
+    from moe_lora_adapter_amd import synth
+    s = synth.shape("qwen3_prefill")
+    log(f"prefill line: drawing {s.name}")
+    case = synth.draw(s)
+    work = algorithmic_work(case)
+    touched = work["fused_bytes"] + work["align_bytes"]
+    copies = 1 if args.warm else max(1, min(8, math.ceil(args.cold_bytes / touched)))
+    sets = [DeviceSet(case, dev)]
+    for _ in range(copies - 1):
+        sets.append(DeviceSet(case, dev, proto=sets[0]))
+    steps = max(10, min(args.steps, 100))
+    for i in range(min(args.warmup, 5)):
+        step(sets[i % copies], s, variant)
+    torch.cuda.synchronize()
+    reps = []
+    time_steps_graph(sets, s, variant, steps, replays=reps, n_replays=5)
+    kus, k10, k90 = time_kernel_windows(sets, s, variant, "fused", steps)
+    kname = _kernel_name(s, variant)
+    gbps = work["fused_bytes"] / (kus * 1e-6) / 1e9
+    tflops = work["fused_flops"] / (kus * 1e-6) / 1e12
+    traffic, _ = load_traffic(kname, s.name)
+    ctr = load_counters(kname, s.name)
+    res = {"workload": s.name, "steps": steps, "step": "moe_lora_align + fused_moe_lora",
+           "us_per_call": round(float(np.median(reps)) * 1e6, 3),
+           "us_per_call_replays": spread([r * 1e6 for r in reps]),
+           "cache": f"cold: {copies} rotated input copies" if not args.warm else "warm",
+           "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                        "algorithmic_bytes_per_launch": work["fused_bytes"],
+                        "kernel_us_avg": round(kus, 3), "kernel_us_p10": round(k10, 3),
+                        "kernel_us_p90": round(k90, 3)},
+           "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                    "counters": None if ctr is None else
+                    {k: ctr[k] for k in ("mfma_util_pct", "mfma_flops_bf16_per_dispatch",
+                                         "mfma_issued_tflops", "kernel_trace_avg_us")
+                     if k in ctr}},
+           "work": {k: work[k] for k in ("valid_pairs", "active_groups", "fused_bytes",
+                                         "fused_flops")}}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def align_stress_line(args, dev):
+    """The align step alone on its stress case (M = 65536, topk = 8, E = 256,
+    L = 16, BLOCK_M = 64): graph-timed calls and event-timed windows."""
+    import torch
+    import moe_lora_adapter_amd as mla
+    from moe_lora_adapter_amd import synth
+    s = synth.shape("align_stress")
+    case = synth.draw(s, with_tensors=False)
+    work = algorithmic_work(case)
+    steps = max(10, min(args.steps, 200))
+
+    class _Set:
+        pass
+    sets = []
+    for _ in range(4):   # a few copies of the routing, rotated
+        d = _Set()
+        d.topk_ids = torch.from_numpy(case.topk_ids).to(dev)
+        d.mapping = torch.from_numpy(case.token_lora_mapping).to(dev)
+        d.align = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, dev)
+        d.ws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)),
+                           dtype=torch.uint8, device=dev)
+        sets.append(d)
+    fn = lambda ds: run_align(ds, s)  # noqa: E731
+    for i in range(5):
+        fn(sets[i % 4])
+    torch.cuda.synchronize()
+    reps = []
+    time_steps_graph(sets, s, None, steps, fn=fn, replays=reps, n_replays=5)
+    kus, k10, k90 = time_kernel_windows(sets, s, None, "align", steps)
+    gbps = work["align_bytes"] / (kus * 1e-6) / 1e9
+    return {"workload": s.name, "M": s.M, "topk": s.topk, "E": s.E, "L": s.L,
+            "block_m": s.block_m, "steps": steps,
+            "us_per_call": round(float(np.median(reps)) * 1e6, 3),
+            "us_per_call_replays": spread([r * 1e6 for r in reps]),
+            "kernels_us_avg": round(kus, 3), "kernels_us_p10": round(k10, 3),
+            "kernels_us_p90": round(k90, 3),
+            "algorithmic_bytes": work["align_bytes"], "achieved_GBps": round(gbps, 1)}
+
+
+def layer_chain_line(sets, s, case, steps, dev, copies):
+    """One MoE layer, w13 -> activation -> w2, with the LoRA side of each
+    projection on an auxiliary stream (moe_lora_adapter_amd.streams: four
+    events) beside stand-in base GEMMs that stream the base weights of the
+    experts the batch routes to (one bf16 GEMM per projection over
+    [K, N x distinct experts]; the w13 side also runs the base MoE align, one
+    slot, beside the LoRA align).  Graph-timed per layer: base alone, LoRA
+    alone, both serial on one stream, and dual-stream."""
+    import torch
+    import moe_lora_adapter_amd as mla
+    from moe_lora_adapter_amd import synth
+    from moe_lora_adapter_amd.streams import LoraStreams, W13, W2
+    c13, c2 = synth.draw_layer(s.name)
+    if not (np.array_equal(c13.topk_ids, case.topk_ids)
+            and np.array_equal(c13.token_lora_mapping, case.token_lora_mapping)):
+        raise RuntimeError("layer draw does not reproduce the workload's routing")
+    s2 = c2.shape
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    for k, d in enumerate(sets):     # the w2 adapters, one copy per rotated set
+        d.a2 = t16(c2.lora_a) if k == 0 else sets[0].a2.clone()
+        d.b2 = t16(c2.lora_b) if k == 0 else sets[0].b2.clone()
+    w2 = torch.from_numpy(c2.topk_weights).to(dev)
+    ex = case.topk_ids.reshape(-1)
+    n_exp = max(1, len(np.unique(ex[(ex >= 0) & (ex < s.E)])))
+    w13cat = torch.empty((s.K, s.N * n_exp), dtype=torch.bfloat16, device=dev).normal_(0, s.K ** -0.5)
+    w2cat = torch.empty((s2.K, s2.N * n_exp), dtype=torch.bfloat16, device=dev).normal_(0, s2.K ** -0.5)
+    base1 = torch.empty((s.M, s.N * n_exp), dtype=torch.bfloat16, device=dev)
+    base2 = torch.empty((s.numel, s2.N * n_exp), dtype=torch.bfloat16, device=dev)
+    zero_map = torch.zeros(s.M, dtype=torch.int32, device=dev)
+    base_al = mla.alloc_align_output(s.M, s.topk, s.E, 1, s.block_m, dev)
+    base_ws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, 1, s.block_m)),
+                          dtype=torch.uint8, device=dev)
+    d1 = torch.zeros_like(sets[0].y)
+    h = torch.empty((s.numel, s2.K), dtype=torch.bfloat16, device=dev)
+    y2 = torch.zeros((s.M, s.topk, s2.N), dtype=torch.bfloat16, device=dev)
+    d2 = torch.zeros_like(y2)
+    st = LoraStreams()
+
+    def base13(d):
+        mla.moe_lora_align(d.topk_ids, zero_map, s.E, 1, s.block_m, out=base_al,
+                           workspace=base_ws)
+        torch.matmul(d.x, w13cat, out=base1)
+
+    def lora13(d):
+        d1.zero_()
+        run_align(d, s)
+        mla.fused_moe_lora(d.x, d.a, d.b, d.align, d.w, d1, mul_routed_weight=s.mul,
+                           add_inputs=False)
+
+    def act(d):   # a stand-in SwiGLU over the gate and up slices
+        y = d.y.view(s.numel, s.N)
+        torch.mul(torch.nn.functional.silu(y[:, :s.Ns]), y[:, s.Ns:], out=h)
+
+    def base2_fn(d):
+        torch.matmul(h, w2cat, out=base2)
+
+    def lora2(d):
+        d2.zero_()
+        mla.fused_moe_lora(h, d.a2, d.b2, d.align, w2, d2, mul_routed_weight=s2.mul,
+                           add_inputs=False, x_per_pair=True)
+
+    def serial(d):
+        base13(d)
+        lora13(d)
+        mla.moe_lora_accumulate(d.y, d1)
+        act(d)
+        base2_fn(d)
+        lora2(d)
+        mla.moe_lora_accumulate(y2, d2)
+
+    def dual(d):
+        st.fork_join(W13, lambda: base13(d), lambda: lora13(d), d.y, d1)
+        act(d)
+        st.fork_join(W2, lambda: base2_fn(d), lambda: lora2(d), y2, d2)
+
+    def base_only(d):
+        base13(d)
+        act(d)
+        base2_fn(d)
+
+    def lora_only(d):
+        lora13(d)
+        mla.moe_lora_accumulate(d.y, d1)
+        act(d)
+        lora2(d)
+        mla.moe_lora_accumulate(y2, d2)
+
+    def timed(fn):
+        return time_steps_graph(sets, s, None, steps, fn=fn) * 1e6
+
+    log("layer chain line")
+    res = {"w2_workload": s2.name,
+           "base_stand_in": (f"w13: bf16 GEMM [{s.M} x {s.K}] x [{s.K} x {s.N * n_exp}], "
+                             f"w2: [{s.numel} x {s2.K}] x [{s2.K} x {s2.N * n_exp}] "
+                             f"({n_exp} distinct experts' base weights, "
+                             f"{(w13cat.numel() + w2cat.numel()) * 2 / 1e9:.2f} GB), "
+                             "plus the base MoE align"),
+           "events": 4,
+           "base_us": round(timed(base_only), 3),
+           "lora_us": round(timed(lora_only), 3),
+           "serial_us": round(timed(serial), 3),
+           "dual_stream_us": round(timed(dual), 3)}
+    res["overlap_saving_us"] = round(res["serial_us"] - res["dual_stream_us"], 3)
+    for d in sets:
+        del d.a2, d.b2
+    del w13cat, w2cat, base1, base2
+    torch.cuda.empty_cache()
+    return res
 
 
 def dual_stream_line(sets, s, case, steps, dev):
@@ -391,7 +652,7 @@ def cpu_baseline(case, budget_s):
         desc = (f"align over all pairs + fused over {n_sample} of {n_full} valid pairs "
                 f"(evenly spaced), scaled to all pairs")
     return {"value": round((t_align + t_fused) * 1e6, 1), "unit": "us/call", "cores": threads,
-            "kind": "oracle", "sample": desc,
+            "cpu_model": cpu_model(), "kind": "oracle", "sample": desc,
             "align_us": round(t_align * 1e6, 1), "fused_us": round(t_fused * 1e6, 1)}
 
 
@@ -447,11 +708,16 @@ def main(argv=None):
                     help="time align + fused_moe_lora_ws (K split) as the step")
     ap.add_argument("--no-k-split-line", action="store_true",
                     help="skip the line that times the step with the K split")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill sub-object (Qwen3-MoE-like prefill)")
+    ap.add_argument("--no-align-stress", action="store_true",
+                    help="skip the align stress sub-object")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone: no comparison lines (profiler runs)")
     args = ap.parse_args(argv)
     if args.step_only:
         args.no_k_split_line = args.no_two_kernel = args.no_dual_stream = True
+        args.no_prefill = args.no_align_stress = True
 
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path has no "
@@ -514,18 +780,19 @@ def main(argv=None):
         copy_calibration(dev)
 
     log(f"timing {args.steps} steps (one graph)")
-    sec_per_step = time_steps_graph(sets, s, variant, args.steps, fn=step_fn)
+    replays = []
+    sec_per_step = time_steps_graph(sets, s, variant, args.steps, fn=step_fn, replays=replays)
     log("timing kernels with events")
     if path == "naive":
-        fused_avg = time_kernel_events(sets, s, variant, naive_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, naive_fn, args.steps)
         align_avg = None
         kbytes = work["naive_bytes"]
     elif path == "with_align":
-        fused_avg = time_kernel_events(sets, s, variant, wa_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, wa_fn, args.steps)
         align_avg = None
         kbytes = work["with_align_bytes"]
     else:
-        fused_avg = time_kernel_events(sets, s, variant, fused_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, fused_fn, args.steps)
         align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
         kbytes = work["fused_bytes"]
 
@@ -560,7 +827,7 @@ def main(argv=None):
                                            "the fused result in one launch)"),
                             "naive": f"fused_moe_lora_naive (no align outputs), "
                                      f"block_m={naive_bm}"}[path],
-                   "timing": "one HIP graph of K steps",
+                   "timing": "one HIP graph of K steps; value from its first timed replay",
                    "cache": ("warm" if args.warm else
                              f"cold: {copies} rotated input copies, "
                              f"{copies * touched / 2 ** 30:.2f} GiB touched")},
@@ -568,7 +835,12 @@ def main(argv=None):
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": kbytes,
-                     "kernel_us_avg": round(fused_avg, 3)},
+                     "kernel_us_avg": round(fused_avg, 3),
+                     "kernel_us_p10": round(f10, 3), "kernel_us_p90": round(f90, 3),
+                     "kernel_timing": "HIP events on the kernel's stream, 5 windows of K "
+                                      "back-to-back launches; avg over windows, p10/p90 of "
+                                      "the window averages"},
+        "us_per_call_replays": spread([r * 1e6 for r in replays]),
         "fused_tflops": round(tflops, 3),
         "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
         "align_kernel_us_avg": round(align_avg, 3) if align_avg is not None else None,
@@ -647,10 +919,26 @@ def main(argv=None):
                              "workspace_bytes": nb,
                              "one_shot_speedup": round(kus2 / (plain_avg or fused_avg), 3)}
     if full_path and naive_ok and not args.no_dual_stream:
-        out["dual_stream"] = dual_stream_line(sets, s, case, args.steps, dev)
+        from moe_lora_adapter_amd import synth as _synth
+        try:
+            _synth.w2_partner(s.name)
+            has_w2 = True
+        except KeyError:
+            has_w2 = False
+        if has_w2:
+            out["layer_chain"] = layer_chain_line(sets, s, case, args.steps, dev, copies)
+        else:
+            out["dual_stream"] = dual_stream_line(sets, s, case, args.steps, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle, ~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    if not args.no_align_stress:
+        log("align stress line")
+        out["align_stress"] = align_stress_line(args, dev)
+    if not args.no_prefill and s.name != "qwen3_prefill":
+        del sets
+        torch.cuda.empty_cache()
+        out["prefill"] = prefill_line(args, dev, variant)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -115,7 +115,7 @@ MOE_LORA_API int moe_lora_align(const int32_t *topk_ids, const int32_t *token_lo
                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Bytes of the device scratch moe_lora_align_noalloc owns on each GPU. */
-#define MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+#define MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
 
 /*
  * moe_lora_align_noalloc -- moe_lora_align for callers that cannot allocate

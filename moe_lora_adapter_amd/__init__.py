@@ -199,7 +199,7 @@ def moe_lora_align(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *
     return out
 
 
-ALIGN_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024   # MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES
+ALIGN_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024   # MOE_LORA_ALIGN_NOALLOC_SCRATCH_BYTES
 
 
 def moe_lora_align_noalloc(topk_ids, token_lora_mapping, E: int, L: int, block_m: int, *,

@@ -24,6 +24,12 @@ namespace mlr {
 
 constexpr int kLdsInts = 16384;  // 64 KiB of LDS per workgroup
 
+// Most per-wave count rows of the tile scatter (its wavefronts per
+// workgroup); can be overridden when building to re-tune.
+#ifndef MLR_ALIGN_MAX_ROWS
+#define MLR_ALIGN_MAX_ROWS 16
+#endif
+
 __device__ __forceinline__ int pair_key(const AlignParams& a, int p) {
   const int m = p / a.topk;
   const int l = a.mapping[m];
@@ -160,84 +166,290 @@ __global__ void __launch_bounds__(1024) align_single_kernel(AlignParams a) {
 }
 
 // ---------------------------------------------------------------- tiles
-__global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
-  extern __shared__ int smem[];
-  int* cnt = smem;  // [W][LE]
-  const int tid = threadIdx.x, w = wave_id(), t = blockIdx.x;
-  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
-  __syncthreads();
-  const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
-  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE, nullptr);
-  __syncthreads();
-  for (int key = tid; key < a.LE; key += blockDim.x) {
-    int sum = 0;
-    for (int q = 0; q < a.W; ++q) sum += cnt[q * a.LE + key];
-    a.tile_cnt[t * a.LE + key] = sum;
+// A tile is `seg` consecutive pairs (the last one shorter); tile t is handled
+// by workgroup t of the count and of the scatter kernel.  Every lane loads the
+// keys of kKeyBatch of its pairs before it uses any, so a wavefront waits for
+// memory once per 64 * kKeyBatch pairs instead of once per 64.
+constexpr int kKeyBatch = 16;
+constexpr int kKeyChunk = kKeyBatch * kWave;
+
+// Keys of pairs base + 64 i + lane (i < kKeyBatch); -1 for a pair at or past
+// s1 (s1 > base) or one outside every group.  The loads are unconditional
+// (addresses clamped into [base, s1)) so that all of them are in flight
+// together.
+__device__ __forceinline__ void load_keys(const AlignParams& a, int64_t base, int s1,
+                                          int (&key)[kKeyBatch]) {
+  const int lane = lane_id();
+  int e[kKeyBatch], l[kKeyBatch];
+#pragma unroll
+  for (int i = 0; i < kKeyBatch; ++i) {
+    const int p = int(min<int64_t>(base + i * kWave + lane, s1 - 1));
+    e[i] = a.topk_ids[p];
+    l[i] = a.mapping[p / a.topk];
+  }
+#pragma unroll
+  for (int i = 0; i < kKeyBatch; ++i) {
+    const bool in = base + i * kWave + lane < s1 && unsigned(l[i]) < unsigned(a.L) &&
+                    unsigned(e[i]) < unsigned(a.E);
+    key[i] = in ? l[i] * a.E + e[i] : -1;
   }
 }
 
-// One workgroup: per key, the exclusive prefix of the tile counts over tiles
-// (written back in place) and the total (key_tot), then the layout of all
-// groups; the expert ids and padding sentinels are left to the tile
-// scatter, spread over its workgroups (one workgroup issuing every group's
-// stores was the slow part here).  The counts of kPrefixBatch tiles are
-// loaded before any is summed.
-constexpr int kPrefixBatch = 32;
-__global__ void __launch_bounds__(1024) align_meta_kernel(AlignParams a) {
-  extern __shared__ int smem[];
-  int* off = smem;            // [LE]
-  int* sb = off + a.LE;       // [L + 1]
-  int* wtot = sb + a.L + 1;   // [17]
-  for (int key = threadIdx.x; key < a.LE; key += blockDim.x) {
-    int run = 0;
-    for (int t0 = 0; t0 < a.ntiles; t0 += kPrefixBatch) {
-      int v[kPrefixBatch];
+// One wavefront's pairs of one 64-pair step, keys known: positions from
+// row[key] (the next free position of each key), the lowest lane of each
+// equal-key set advancing it.
+__device__ __forceinline__ void place_step(const AlignParams& a, int* row, int key, int p) {
+  const int lane = lane_id();
+  const uint64_t valid = __ballot(key >= 0);
+  if (valid == 0) return;
+  const uint64_t peers = match_key(key, valid, a.nbits);
+  if (key >= 0) {
+    const uint64_t below = peers & lanes_below(lane);
+    const int pos = row[key] + __popcll(below);
+    const int l = key / a.E;
+    a.sorted[l * a.cap + pos] = p;
+    if (below == 0) row[key] = pos + __popcll(peers);
+  }
+}
+
+// Per tile: the pair count of every key (one LDS histogram shared by the
+// workgroup) to tile_cnt[t][key].
+__global__ void __launch_bounds__(1024) align_tile_count_kernel(AlignParams a) {
+  extern __shared__ int hist[];  // [LE]
+  const int tid = threadIdx.x, t = blockIdx.x;
+  const int nw = blockDim.x / kWave, w = wave_id();
+  for (int i = tid; i < a.LE; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int64_t t0 = int64_t(t) * a.seg;
+  const int t1 = int(min<int64_t>(a.numel, t0 + a.seg));
+  for (int64_t base = t0 + w * kKeyChunk; base < t1; base += nw * kKeyChunk) {
+    int key[kKeyBatch];
+    load_keys(a, base, t1, key);
 #pragma unroll
-      for (int i = 0; i < kPrefixBatch; ++i)
-        v[i] = t0 + i < a.ntiles ? a.tile_cnt[(t0 + i) * a.LE + key] : 0;
+    for (int i = 0; i < kKeyBatch; ++i)
+      if (key[i] >= 0) atomicAdd(&hist[key[i]], 1);
+  }
+  __syncthreads();
+  int* out = a.tile_cnt + int64_t(t) * a.LE;
+  for (int key = tid; key < a.LE; key += blockDim.x) out[key] = hist[key];
+}
+
+// Per key, the exclusive prefix of its tile counts over tiles (in place) and
+// its total (key_tot).  A workgroup takes 64 consecutive keys (lane = key, so
+// every load reads 256 contiguous bytes of a tile's row) and its Q
+// wavefronts split the tiles into runs; each run's counts are loaded a batch
+// at a time before any is used, and the runs' sums are combined in LDS.
+__global__ void __launch_bounds__(1024) align_prefix_kernel(AlignParams a) {
+  __shared__ int part[16][kWave];
+  const int lane = lane_id(), q = wave_id(), Q = blockDim.x / kWave;
+  const int key = blockIdx.x * kWave + lane;
+  const bool live = key < a.LE;
+  const int chunk = (a.ntiles + Q - 1) / Q;
+  const int ta = min(a.ntiles, q * chunk), tb = min(a.ntiles, ta + chunk);
+  int* col = a.tile_cnt + (live ? key : 0);
+  int sum = 0;
+  for (int t = ta; t < tb; t += kKeyBatch) {
+    int v[kKeyBatch];
 #pragma unroll
-      for (int i = 0; i < kPrefixBatch; ++i) {
-        if (t0 + i < a.ntiles) a.tile_cnt[(t0 + i) * a.LE + key] = run;
+    for (int i = 0; i < kKeyBatch; ++i) v[i] = col[int64_t(min(t + i, tb - 1)) * a.LE];
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i) sum += t + i < tb ? v[i] : 0;
+  }
+  part[q][lane] = sum;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int u = 0; u < Q; ++u) {
+    const int c = part[u][lane];
+    run += u < q ? c : 0;
+    total += c;
+  }
+  if (!live) return;
+  for (int t = ta; t < tb; t += kKeyBatch) {
+    int v[kKeyBatch];
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i) v[i] = col[int64_t(min(t + i, tb - 1)) * a.LE];
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i) {
+      if (t + i < tb) {
+        col[int64_t(t + i) * a.LE] = run;
         run += v[i];
       }
     }
-    a.key_tot[key] = run;
   }
-  layout_groups(a, a.key_tot, off, sb, wtot, false);
-  for (int key = threadIdx.x; key < a.LE; key += blockDim.x) a.key_off[key] = off[key];
+  if (q == 0) a.key_tot[key] = total;
 }
 
+// Exclusive prefix sum in place of a[0..n) in LDS, each thread taking a
+// contiguous run of about n / blockDim entries (two barriers in all, against
+// three per blockDim entries for block_excl_scan).  Returns the total.
+__device__ int block_excl_scan_runs(int* a, int n, int* wtot) {
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int nw = blockDim.x / kWave;
+  const int r = (n + blockDim.x - 1) / blockDim.x;
+  const int i0 = min(n, tid * r), i1 = min(n, i0 + r);
+  int s = 0;
+  for (int i = i0; i < i1; ++i) s += a[i];
+  const int incl = wave_incl_scan(s);
+  if (lane == kWave - 1) wtot[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < nw ? wtot[lane] : 0;
+    const int ti = wave_incl_scan(t);
+    if (lane < nw) wtot[lane] = ti - t;
+    if (lane == nw - 1) wtot[16] = ti;
+  }
+  __syncthreads();
+  int run = wtot[w] + incl - s;
+  for (int i = i0; i < i1; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  const int total = wtot[16];
+  __syncthreads();
+  return total;
+}
+
+// Per tile, W = blockDim / 64 wavefronts, wave w owning pairs
+// [t seg + w segw, + segw) of the tile:
+//   1. per-wave counts (LDS rows), while the key totals are in flight;
+//   2. the layout of every group from the key totals (each workgroup computes
+//      it: padded sizes, one scan, slot starts), and each row turned into the
+//      next free position of every key for that wave (group start in the
+//      slot + pairs of the key in earlier tiles + in earlier waves of this
+//      tile);
+//   3. the placement;
+//   4. the expert ids and padding sentinels of this tile's share of the
+//      groups; workgroup 0 also writes num_tokens_post_padded and the active
+//      slot list.
 __global__ void __launch_bounds__(1024) align_tile_scatter_kernel(AlignParams a) {
   extern __shared__ int smem[];
-  int* cnt = smem;  // [W][LE]
-  const int tid = threadIdx.x, w = wave_id(), t = blockIdx.x;
-  for (int i = tid; i < a.W * a.LE; i += blockDim.x) cnt[i] = 0;
+  int* off = smem;               // [LE]: padded sizes, then group starts in the slot
+  int* sb = off + a.LE;          // [L + 1]: slot starts in the scan
+  int* wtot = sb + a.L + 1;      // [17]
+  int* cnt = wtot + 17;          // [W][LE]
+  const int tid = threadIdx.x, w = wave_id(), t = blockIdx.x, W = blockDim.x / kWave;
+  const int64_t s0 = int64_t(t) * a.seg + int64_t(w) * a.segw;
+  const int t1 = int(min<int64_t>(a.numel, (int64_t(t) + 1) * a.seg));
+  const int s1 = int(min<int64_t>(t1, s0 + a.segw));
+  int key0[kKeyBatch];           // keys of the wave's first chunk, kept for both passes
+  if (s0 < s1) load_keys(a, s0, s1, key0);
+  int tv[8];                     // the first key totals of this thread, in flight meanwhile
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tv[i] = a.key_tot[min(tid + i * int(blockDim.x), a.LE - 1)];
+  for (int i = tid; i < W * a.LE; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
-  const int s0 = (t * a.W + w) * a.seg, s1 = min(a.numel, s0 + a.seg);
-  if (s0 < s1) count_segment(a, s0, s1, cnt + w * a.LE, nullptr);
+  int* row = cnt + w * a.LE;
+  for (int64_t base = s0; base < s1; base += kKeyChunk) {
+    int key[kKeyBatch];
+    if (base == s0) {
+#pragma unroll
+      for (int i = 0; i < kKeyBatch; ++i) key[i] = key0[i];
+    } else {
+      load_keys(a, base, s1, key);
+    }
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i)
+      if (key[i] >= 0) atomicAdd(&row[key[i]], 1);
+  }
+  // padded group sizes, then their scan: group starts, slot starts
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (tid + i * int(blockDim.x) < a.LE) off[tid + i * blockDim.x] = (tv[i] + a.B - 1) / a.B * a.B;
+  for (int k0 = tid + 8 * blockDim.x; k0 < a.LE; k0 += blockDim.x * 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = a.key_tot[min(k0 + i * int(blockDim.x), a.LE - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i * int(blockDim.x) < a.LE) off[k0 + i * blockDim.x] = (v[i] + a.B - 1) / a.B * a.B;
+  }
   __syncthreads();
-  for (int key = tid; key < a.LE; key += blockDim.x) {
-    int run = a.key_off[key] + a.tile_cnt[t * a.LE + key];
-    for (int q = 0; q < a.W; ++q) {
-      const int c = cnt[q * a.LE + key];
-      cnt[q * a.LE + key] = run;
-      run += c;
+  const int total = block_excl_scan_runs(off, a.LE, wtot);
+  for (int l = tid; l <= a.L; l += blockDim.x) sb[l] = l < a.L ? off[l * a.E] : total;
+  __syncthreads();
+  const int* tc = a.tile_cnt + int64_t(t) * a.LE;
+  for (int k0 = tid; k0 < a.LE; k0 += blockDim.x * 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tc[min(k0 + i * int(blockDim.x), a.LE - 1)];
+    for (int i = 0; i < 8; ++i) {
+      const int key = k0 + i * blockDim.x;
+      if (key >= a.LE) break;
+      int c[16];                 // the W rows' counts of this key, read together
+#pragma unroll
+      for (int q = 0; q < 16; ++q) c[q] = q < W ? cnt[q * a.LE + key] : 0;
+      int run = off[key] - sb[key / a.E] + v[i];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (q < W) {
+          cnt[q * a.LE + key] = run;
+          run += c[q];
+        }
+      }
     }
   }
   __syncthreads();
-  if (s0 < s1) scatter_segment(a, s0, s1, cnt + w * a.LE, nullptr);
+  for (int64_t base = s0; base < s1; base += kKeyChunk) {
+    int key[kKeyBatch];
+    if (base == s0) {
+#pragma unroll
+      for (int i = 0; i < kKeyBatch; ++i) key[i] = key0[i];
+    } else {
+      load_keys(a, base, s1, key);
+    }
+#pragma unroll
+    for (int i = 0; i < kKeyBatch; ++i)
+      place_step(a, row, key[i], int(base + i * kWave + lane_id()));
+  }
   // expert ids and padding sentinels of this tile's share of the groups
   const int per = (a.LE + a.ntiles - 1) / a.ntiles;
   const int k0 = t * per, k1 = min(a.LE, k0 + per);
   const int lpk = a.B / 4;
   const int sub = lane_id() / lpk, sl = lane_id() % lpk;
-  const int stride = (blockDim.x / kWave) * (kWave / lpk);
+  const int stride = W * (kWave / lpk);
   for (int key = k0 + w * (kWave / lpk) + sub; key < k1; key += stride)
-    fill_group(a, key, a.key_off[key], a.key_tot[key], sl, lpk);
+    fill_group(a, key, off[key] - sb[key / a.E], a.key_tot[key], sl, lpk);
+  if (t == 0) {
+    for (int l = tid; l < a.L; l += blockDim.x) a.ntpp[l] = sb[l + 1] - sb[l];
+    if (w == 0 && (a.lora_ids || a.nact)) {
+      const int lane = lane_id();
+      int run = 0;
+      for (int c0 = 0; c0 < a.L; c0 += kWave) {
+        const int l = c0 + lane;
+        const bool act = l < a.L && sb[l + 1] > sb[l];
+        const uint64_t mk = __ballot(act);
+        if (act && a.lora_ids) a.lora_ids[run + __popcll(mk & lanes_below(lane))] = l;
+        run += __popcll(mk);
+      }
+      if (a.lora_ids)
+        for (int i = run + lane; i < a.L; i += kWave) a.lora_ids[i] = -1;
+      if (a.nact && lane == 0) *a.nact = run;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- host
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Most LDS bytes one workgroup may take on the current device (cached).
+static int lds_per_block() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kLdsInts * 4;
+  if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+  int bytes = 0;
+  if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      bytes <= 0)
+    bytes = kLdsInts * 4;
+  if (dev < kMaxDevices) cache[dev] = bytes;
+  return bytes;
+}
+
+// Tiles of at least kMinTile pairs; at most 2^20 / (L E) of them, so that the
+// per-tile counts fit a fixed workspace bound (4 MiB).
+constexpr int64_t kMinTile = 512;
 
 AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   (void)B;
@@ -265,23 +477,18 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
     return pl;
   }
   pl.single = false;
-  const int64_t W = std::min<int64_t>(16, kLdsInts / LE);
-  const int64_t max_tiles = std::max<int64_t>(1, std::min<int64_t>(1024, (int64_t(1) << 18) / LE));
-  int64_t ntiles = std::min<int64_t>(max_tiles, cdiv(numel, W * kWave));
-  ntiles = std::max<int64_t>(ntiles, 1);
-  int64_t seg = std::max<int64_t>(kWave, cdiv(cdiv(numel, ntiles * W), kWave) * kWave);
-  ntiles = std::max<int64_t>(1, cdiv(numel, W * seg));
-  pl.W = int(W);
-  pl.seg = int(seg);
-  pl.ntiles = int(ntiles);
-  pl.threads = int(W * kWave);
-  pl.lds_bytes = size_t(W * LE * 4);
-  pl.meta_lds_bytes = size_t((LE + L + 1 + 17) * 4);
-  pl.ws_bytes = (ntiles * LE + 2 * LE) * 4;
+  const int64_t max_tiles = std::max<int64_t>(1, std::min<int64_t>(1024, (int64_t(1) << 20) / LE));
+  int64_t tile = std::max<int64_t>(kMinTile, cdiv(numel, max_tiles));
+  tile = cdiv(tile, kWave) * kWave;
+  pl.seg = int(tile);
+  pl.ntiles = int(cdiv(numel, tile));
+  pl.threads = int(std::min<int64_t>(1024, tile));               // count kernel
+  pl.lds_bytes = size_t(LE * 4);
+  pl.ws_bytes = (int64_t(pl.ntiles) + 1) * LE * 4;   // tile counts, then key totals
   return pl;
 }
 
-hipError_t launch_align(const AlignPlan& pl, const AlignParams& a, hipStream_t st) {
+hipError_t launch_align(const AlignPlan& pl, AlignParams a, hipStream_t st) {
   if (pl.wave) {
     hipLaunchKernelGGL(align_wave_kernel, dim3(1), dim3(kWave), 0, st, a);
     return hipGetLastError();
@@ -290,11 +497,35 @@ hipError_t launch_align(const AlignPlan& pl, const AlignParams& a, hipStream_t s
     hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(pl.threads), pl.lds_bytes, st, a);
     return hipGetLastError();
   }
+  // prefix kernel: 64 keys per workgroup, enough wavefronts (at most 16)
+  // that each sums at most 16 tiles where the tile count allows
+  const int prefix_waves = int(std::min<int64_t>(16, cdiv(a.ntiles, kKeyBatch)));
+  // scatter kernel: as many per-wave rows as LDS holds beside the layout
+  // tables (at most 16), each wave owning an equal run of the tile (a
+  // multiple of 64 pairs)
+  const int64_t fixed_ints = int64_t(a.LE) + a.L + 1 + 17;
+  auto fit_rows = [&](int64_t lds_bytes) {
+    int w = int(std::max<int64_t>(
+        1, std::min<int64_t>(MLR_ALIGN_MAX_ROWS, (lds_bytes / 4 - fixed_ints) / a.LE)));
+    w = int(std::min<int64_t>(w, cdiv(a.seg, kWave)));
+    a.segw = int(cdiv(cdiv(a.seg, w), kWave) * kWave);
+    a.W = int(cdiv(a.seg, a.segw));
+  };
+  fit_rows(lds_per_block());
+  if ((fixed_ints + int64_t(a.W) * a.LE) * 4 > kLdsInts * 4 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(align_tile_scatter_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          int((fixed_ints + int64_t(a.W) * a.LE) * 4)) != hipSuccess) {
+    (void)hipGetLastError();   // keep within the 64 KiB every launch may take
+    fit_rows(kLdsInts * 4);
+  }
+  const size_t scatter_lds = size_t(fixed_ints + int64_t(a.W) * a.LE) * 4;
   hipLaunchKernelGGL(align_tile_count_kernel, dim3(pl.ntiles), dim3(pl.threads), pl.lds_bytes,
                      st, a);
-  hipLaunchKernelGGL(align_meta_kernel, dim3(1), dim3(1024), pl.meta_lds_bytes, st, a);
-  hipLaunchKernelGGL(align_tile_scatter_kernel, dim3(pl.ntiles), dim3(pl.threads),
-                     pl.lds_bytes, st, a);
+  hipLaunchKernelGGL(align_prefix_kernel, dim3(unsigned(cdiv(a.LE, kWave))),
+                     dim3(prefix_waves * kWave), 0, st, a);
+  hipLaunchKernelGGL(align_tile_scatter_kernel, dim3(pl.ntiles), dim3(a.W * kWave), scatter_lds,
+                     st, a);
   return hipGetLastError();
 }
 

@@ -169,7 +169,6 @@ static int align_call(const int32_t* topk_ids, const int32_t* token_lora_mapping
     int32_t* ws = static_cast<int32_t*>(workspace);
     a.tile_cnt = ws;
     a.key_tot = ws + int64_t(plan.ntiles) * a.LE;
-    a.key_off = a.key_tot + a.LE;
   }
   const hipError_t err = launch_align(plan, a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;

@@ -17,21 +17,20 @@ struct AlignParams {
   int32_t* nact;      // [1] or null
   int32_t* tile_cnt;  // [ntiles, LE]  (multi-workgroup path)
   int32_t* key_tot;   // [LE]
-  int32_t* key_off;   // [LE]
   int32_t numel, topk, E, L, LE, B, nbits;
   int32_t cap, nb;
   int32_t W;       // waves that own a pair segment, per workgroup
-  int32_t seg;     // pairs per wave segment (multiple of 64)
+  int32_t seg;     // single workgroup: pairs per wave; tiles: pairs per tile
   int32_t ntiles;  // workgroups of the tile kernels
+  int32_t segw;    // tile scatter: pairs per wave (multiple of 64)
 };
 
 struct AlignPlan {
   bool wave;         // one wavefront does everything (at most 64 pairs and 64 slots)
   bool single;       // one workgroup does everything
   int W, seg, ntiles;
-  int threads;       // block size of the single / tile kernels
-  size_t lds_bytes;  // dynamic LDS of the single / tile kernels
-  size_t meta_lds_bytes;
+  int threads;       // block size of the single / tile count kernels
+  size_t lds_bytes;  // dynamic LDS of the single / tile count kernels
   int64_t ws_bytes;  // device workspace (0 for the single path)
 };
 
@@ -40,7 +39,7 @@ constexpr int kAlignWaveMaxPairs = 64;
 constexpr int kAlignWaveMaxSlots = 64;
 
 AlignPlan plan_align(int64_t numel, int E, int L, int B);
-hipError_t launch_align(const AlignPlan& plan, const AlignParams& a, hipStream_t st);
+hipError_t launch_align(const AlignPlan& plan, AlignParams a, hipStream_t st);
 
 // ---------------------------------------------------------------- fused
 struct FusedParams {

@@ -46,7 +46,10 @@ def test_capacity_matches_oracle_and_bound():
 
 def test_workspace_query():
     assert mla.align_workspace_size(16, 4, 32, 6, 16) == 0          # one workgroup
-    assert mla.align_workspace_size(65536, 8, 256, 16, 64) > 0      # tiles
+    # tiles: the per-tile counts (tiles of >= 512 pairs, at most 2^20 / (L E)
+    # of them) and the key totals, int32
+    assert mla.align_workspace_size(65536, 8, 256, 16, 64) == (256 + 1) * 4096 * 4
+    assert mla.align_workspace_size(8192, 8, 128, 8, 64) == (128 + 1) * 1024 * 4
     assert mla.align_workspace_size(0, 4, 32, 6, 16) == 0
 
 
@@ -111,7 +114,7 @@ def test_align_noalloc_rejects(kw, status):
 def test_align_noalloc_scratch_covers_every_accepted_size():
     """The static scratch of the no-allocation align holds the workspace of the largest
     problems the limits admit (the tile path's per-tile counts are capped)."""
-    assert mla.ALIGN_NOALLOC_SCRATCH_BYTES == 2 * 1024 * 1024
+    assert mla.ALIGN_NOALLOC_SCRATCH_BYTES == 8 * 1024 * 1024
     for M, topk, E, L, B in ((65536, 8, 256, 16, 64), (2 ** 22, 8, 1024, 8, 128),
                              (2 ** 20, 1, 1, 1024, 16), (10 ** 6, 1, 1024, 8, 16),
                              (5000, 4, 2, 1, 16)):
