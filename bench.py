@@ -510,6 +510,16 @@ def layer_chain_line(sets, s, case, steps, dev, copies):
     def timed(fn):
         return time_steps_graph(sets, s, None, steps, fn=fn) * 1e6
 
+    def timed_eager(fn):
+        for i in range(len(sets)):
+            fn(sets[i])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
     log("layer chain line")
     res = {"w2_workload": s2.name,
            "base_stand_in": (f"w13: bf16 GEMM [{s.M} x {s.K}] x [{s.K} x {s.N * n_exp}], "
@@ -521,8 +531,13 @@ def layer_chain_line(sets, s, case, steps, dev, copies):
            "base_us": round(timed(base_only), 3),
            "lora_us": round(timed(lora_only), 3),
            "serial_us": round(timed(serial), 3),
-           "dual_stream_us": round(timed(dual), 3)}
+           "dual_stream_us": round(timed(dual), 3),
+           "eager_serial_us": round(timed_eager(serial), 3),
+           "eager_dual_stream_us": round(timed_eager(dual), 3),
+           "timing": "graph: one HIP graph of K layers; eager: K layers launched from the "
+                     "host, synchronize on both sides"}
     res["overlap_saving_us"] = round(res["serial_us"] - res["dual_stream_us"], 3)
+    res["eager_overlap_saving_us"] = round(res["eager_serial_us"] - res["eager_dual_stream_us"], 3)
     for d in sets:
         del d.a2, d.b2
     del w13cat, w2cat, base1, base2

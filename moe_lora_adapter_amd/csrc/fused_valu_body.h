@@ -146,26 +146,129 @@ __device__ __forceinline__ void load_y(const FusedParams& p, const int* s_pair, 
     y[i] = (p.add && i < nr) ? p.y[int64_t(s_pair[i]) * p.N + col] : uint16_t(0);
 }
 
+constexpr int kRowsPerBatch = 2 * kThreads;  // columns of one expand batch (at most)
+// one epilogue task (one row, 8 columns) per thread covers a batch
+static_assert(kMaxRG * kRowsPerBatch / 8 <= kThreads, "epilogue tasks exceed the threads");
+
+// The loads of one expand batch: this thread's B chunks and the Y piece of
+// its epilogue task.  They do not depend on v, so the first batch can be in
+// flight with A.
+template <int NB>
+struct ExpandBatch {
+  uint4 bv[NB];
+  uint4 yv;
+};
+
+template <int RG, int CPR>
+struct ExpandGeom {
+  static constexpr int NB0 = RG <= 2 ? 16 : 8;            // chunk loads in flight per thread
+  static constexpr int NBR = kRowsPerBatch * CPR / kThreads;
+  static constexpr int NB = NB0 < NBR ? NB0 : (NBR > 0 ? NBR : 1);
+};
+
+// Epilogue task of this thread in the batch starting at chunk `base`: row
+// task_i, 8 columns from 8 task_c; none when the batch has fewer than 8
+// columns or the row is past nr.
+struct ExpandTask {
+  int row0, rows, task_i, task_c;
+  bool has;
+};
+
+template <int CPR>
+__device__ __forceinline__ ExpandTask expand_task(int base, int nchunks, int NBT, int nr) {
+  ExpandTask t;
+  t.rows = min(NBT, nchunks - base) / CPR;  // columns in this batch
+  t.row0 = base / CPR;
+  const int c8n = t.rows / 8;
+  t.task_i = int(threadIdx.x) / max(c8n, 1);
+  t.task_c = int(threadIdx.x) - t.task_i * max(c8n, 1);
+  t.has = c8n > 0 && t.task_i < nr;
+  return t;
+}
+
+template <int RG, int CPR>
+__device__ __forceinline__ void expand_issue(const FusedParams& p, const uint16_t* __restrict__ tile,
+                                             const int* s_pair, int nr, int col0, int base,
+                                             int nchunks, ExpandBatch<ExpandGeom<RG, CPR>::NB>& eb) {
+  constexpr int NB = ExpandGeom<RG, CPR>::NB;
+  const int tid = threadIdx.x;
+  const ExpandTask t = expand_task<CPR>(base, nchunks, NB * kThreads, nr);
+  eb.yv = make_uint4(0, 0, 0, 0);
+  if (t.has && p.add)
+    eb.yv = *reinterpret_cast<const uint4*>(p.y + int64_t(s_pair[t.task_i]) * p.N + col0 + t.row0 +
+                                            t.task_c * 8);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int q = min(base + k * kThreads + tid, nchunks - 1);
+    eb.bv[k] = ld16(tile + int64_t(q) * 8);
+  }
+}
+
 // Expand for r == 8 * CPR: the B tile rows [n0, n1) read as one coalesced
 // stream of 16-byte chunks.  Chunk q of the tile is row q / CPR, ranks
 // 8 * (q % CPR) .. +8; since the thread count is a multiple of CPR a thread
 // always sees the same eight ranks.  The row sums land in LDS (s_d), and the
 // epilogue then reads Y and writes it back in 16-byte pieces (8 columns per
-// thread), the Y reads issued before the B chunks are consumed.
-constexpr int kRowsPerBatch = 2 * kThreads;
-// one epilogue task (one row, 8 columns) per thread covers a batch
-static_assert(kMaxRG * kRowsPerBatch / 8 <= kThreads, "epilogue tasks exceed the threads");
+// thread), the Y reads issued before the B chunks are consumed.  With FIRST,
+// `first` holds the loads of the first batch, issued by the caller
+// (expand_issue).
 
+// One batch of the expand from its loads: row sums into s_d, then the
+// epilogue (Y (+)= w d, one rounding) of this thread's task.
 template <int RG, int CPR>
-__device__ __forceinline__ void expand_stream(const FusedParams& p, const uint16_t* __restrict__ Bm,
-                                              const int* s_pair, int nr, const float* s_v, int s,
-                                              int n0, int n1, float* s_d) {
-  // chunk loads in flight per thread; one batch covers at most kRowsPerBatch rows
-  constexpr int NB0 = RG <= 2 ? 16 : 8;
-  constexpr int NBR = kRowsPerBatch * CPR / kThreads;
-  constexpr int NB = NB0 < NBR ? NB0 : (NBR > 0 ? NBR : 1);
+__device__ __forceinline__ void expand_batch(const FusedParams& p, const int* s_pair, int nr,
+                                             const float (&vr)[RG][8], const float (&wt)[RG],
+                                             int col0, int base, int nchunks, float* s_d,
+                                             const ExpandBatch<ExpandGeom<RG, CPR>::NB>& eb) {
+  constexpr int NB = ExpandGeom<RG, CPR>::NB;
   const int tid = threadIdx.x;
   const int jc = tid % CPR;
+  const ExpandTask t = expand_task<CPR>(base, nchunks, NB * kThreads, nr);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int q = base + k * kThreads + tid;
+    const uint4 b4 = eb.bv[k];
+    const float b[8] = {bf16_lo(b4.x), bf16_hi(b4.x), bf16_lo(b4.y), bf16_hi(b4.y),
+                        bf16_lo(b4.z), bf16_hi(b4.z), bf16_lo(b4.w), bf16_hi(b4.w)};
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      float d = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) d += vr[i][u] * b[u];
+#pragma unroll
+      for (int o = CPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
+      if (jc == 0 && q < nchunks) s_d[i * kRowsPerBatch + q / CPR - t.row0] = d;
+    }
+  }
+  __syncthreads();
+  if (t.has) {
+    uint16_t* yp = p.y + int64_t(s_pair[t.task_i]) * p.N + col0 + t.row0 + t.task_c * 8;
+    const float* dd = s_d + t.task_i * kRowsPerBatch + t.task_c * 8;
+    const float w = wt[t.task_i];
+    const uint32_t in[4] = {eb.yv.x, eb.yv.y, eb.yv.z, eb.yv.w};
+    uint32_t outw[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float lo = dd[2 * h] * w, hi = dd[2 * h + 1] * w;
+      if (p.add) {
+        lo += bf16_lo(in[h]);
+        hi += bf16_hi(in[h]);
+      }
+      outw[h] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    }
+    *reinterpret_cast<uint4*>(yp) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+  __syncthreads();
+}
+
+template <int RG, int CPR, bool FIRST>
+__device__ __forceinline__ void expand_stream(const FusedParams& p, const uint16_t* __restrict__ Bm,
+                                              const int* s_pair, int nr, const float* s_v, int s,
+                                              int n0, int n1, float* s_d,
+                                              const ExpandBatch<ExpandGeom<RG, CPR>::NB>& first) {
+  constexpr int NB = ExpandGeom<RG, CPR>::NB;
+  const int jc = int(threadIdx.x) % CPR;
   float vr[RG][8];
 #pragma unroll
   for (int i = 0; i < RG; ++i)
@@ -176,61 +279,16 @@ __device__ __forceinline__ void expand_stream(const FusedParams& p, const uint16
   const uint16_t* tile = Bm + int64_t(n0) * p.r;
   const int nchunks = (n1 - n0) * CPR;
   const int col0 = s * p.Ns + n0;
+  int base = 0;
+  if constexpr (FIRST) {
+    expand_batch<RG, CPR>(p, s_pair, nr, vr, wt, col0, 0, nchunks, s_d, first);
+    base = NB * kThreads;
+  }
 #pragma unroll 1
-  for (int base = 0; base < nchunks; base += NB * kThreads) {
-    const int rows = min(NB * kThreads, nchunks - base) / CPR;  // columns in this batch
-    const int row0 = base / CPR;
-    // epilogue task of this thread: row i, 8 columns starting at 8 * c8
-    const int c8n = rows / 8;
-    const int task_i = tid / max(c8n, 1), task_c = tid - task_i * max(c8n, 1);
-    const bool has_task = c8n > 0 && task_i < nr;
-    uint4 yv = make_uint4(0, 0, 0, 0);
-    uint16_t* yp = nullptr;
-    if (has_task) {
-      yp = p.y + int64_t(s_pair[task_i]) * p.N + col0 + row0 + task_c * 8;
-      if (p.add) yv = *reinterpret_cast<const uint4*>(yp);
-    }
-    uint4 bv[NB];
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int q = min(base + k * kThreads + tid, nchunks - 1);
-      bv[k] = ld16(tile + int64_t(q) * 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int q = base + k * kThreads + tid;
-      const uint4 b4 = bv[k];
-      const float b[8] = {bf16_lo(b4.x), bf16_hi(b4.x), bf16_lo(b4.y), bf16_hi(b4.y),
-                          bf16_lo(b4.z), bf16_hi(b4.z), bf16_lo(b4.w), bf16_hi(b4.w)};
-#pragma unroll
-      for (int i = 0; i < RG; ++i) {
-        float d = 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) d += vr[i][t] * b[t];
-#pragma unroll
-        for (int o = CPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
-        if (jc == 0 && q < nchunks) s_d[i * kRowsPerBatch + q / CPR - row0] = d;
-      }
-    }
-    __syncthreads();
-    if (has_task) {
-      const float* dd = s_d + task_i * kRowsPerBatch + task_c * 8;
-      const float w = wt[task_i];
-      const uint32_t in[4] = {yv.x, yv.y, yv.z, yv.w};
-      uint32_t outw[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float lo = dd[2 * h] * w, hi = dd[2 * h + 1] * w;
-        if (p.add) {
-          lo += bf16_lo(in[h]);
-          hi += bf16_hi(in[h]);
-        }
-        outw[h] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-      }
-      *reinterpret_cast<uint4*>(yp) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-    }
-    __syncthreads();
+  for (; base < nchunks; base += NB * kThreads) {
+    ExpandBatch<NB> eb;
+    expand_issue<RG, CPR>(p, tile, s_pair, nr, col0, base, nchunks, eb);
+    expand_batch<RG, CPR>(p, s_pair, nr, vr, wt, col0, base, nchunks, s_d, eb);
   }
 }
 
@@ -267,11 +325,20 @@ __device__ __forceinline__ void valu_rows(const FusedParams& p, const uint16_t* 
                                           int s, int n0, int n1) {
   for (int g0 = 0; g0 < nv; g0 += RG) {
     const int nr = min(RG, nv - g0);
-    shrink_group<RG, JW>(p, A, s_row + g0, nr, sh, s_part, s_v);
-    if constexpr (CPR > 0)
-      expand_stream<RG, CPR>(p, Bm, s_pair + g0, nr, s_v, s, n0, n1, s_d);
-    else
+    if constexpr (CPR > 0) {
+      // with 512 threads the expand's first B and Y loads go out with A's
+      // (with 1024 the registers they would hold through the shrink spill)
+      constexpr bool kEarly = kThreads <= 512;
+      ExpandBatch<ExpandGeom<RG, CPR>::NB> first;
+      if constexpr (kEarly)
+        expand_issue<RG, CPR>(p, Bm + int64_t(n0) * p.r, s_pair + g0, nr, s * p.Ns + n0, 0,
+                              (n1 - n0) * CPR, first);
+      shrink_group<RG, JW>(p, A, s_row + g0, nr, sh, s_part, s_v);
+      expand_stream<RG, CPR, kEarly>(p, Bm, s_pair + g0, nr, s_v, s, n0, n1, s_d, first);
+    } else {
+      shrink_group<RG, JW>(p, A, s_row + g0, nr, sh, s_part, s_v);
       expand_columns<RG>(p, Bm, s_pair + g0, nr, s_v, s, n0, n1);
+    }
     __syncthreads();
   }
 }
