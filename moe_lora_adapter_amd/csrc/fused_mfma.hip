@@ -465,6 +465,42 @@ __device__ __forceinline__ void run_pass(const FusedParams& p, const PassCtx& c)
   stage_barrier<0>();  // V (slot 0) and the row tables are reused by the next pass
 }
 
+// How the work of a (block, slice) unit is spread when the units leave
+// compute units idle: n_split column ranges and n_rs row parts (16-row
+// multiples) per unit, each a workgroup of its own.  A column split re-reads
+// the unit's X rows and A; a row part re-reads A and B.  Among the splittings
+// that keep every workgroup in one round (xcd_cus * MLR_MFMA_OCCUPANCY slots
+// per XCD), the one that moves the fewest bytes per workgroup wins -- for
+// the dense projections (few blocks of full rows, small rank, large K) that
+// is row parts, where column splits would stream the same X rows many times.
+// With every slot taken there is one workgroup per unit.
+__device__ __forceinline__ void pick_splits(const FusedParams& p, int total, int per_xcd, int& n_rs,
+                                            int& n_split) {
+  const int cap = p.xcd_cus * MLR_MFMA_OCCUPANCY;
+  const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
+  const int room = max(1, cap / max(per_xcd, 1));
+  n_rs = 1;
+  n_split = min(max_split, room);
+  if (room < 2) return;
+  // rows a block holds on average (valid rows form each block's prefix)
+  const float rows = float(min(p.B, (p.numel + total - 1) / max(total, 1)));
+  const float K = float(p.K), r = float(p.r), Ns = float(p.Ns);
+  auto cost = [&](int rs, int cs) {
+    const float pr = rows / rs, pc = Ns / cs;
+    return pr * K * 2.f + r * K * 2.f + pc * r * 2.f + pr * pc * 2.f * (p.add ? 2.f : 1.f);
+  };
+  float best = cost(1, n_split);
+  for (int rs = 2; rs <= 8 && 16 * rs <= p.B && rows >= 16.f * rs && rs <= room; rs *= 2) {
+    const int cs = min(max_split, room / rs);
+    const float c = cost(rs, cs);
+    if (c < best) {
+      best = c;
+      n_rs = rs;
+      n_split = cs;
+    }
+  }
+}
+
 // NAIVE: the blocks are formed on chip from topk_ids and the mapping (the
 // align-free path) instead of being read from the align outputs.
 template <int RT, bool NAIVE>
@@ -491,13 +527,15 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   }
   const int units = total * p.S;
   const int per_xcd = (units + kXcds - 1) / kXcds;
-  const int max_split = max(1, p.Ns / MLR_MFMA_MIN_COLS);
-  const int n_split = min(max_split, max(1, p.xcd_cus * MLR_MFMA_OCCUPANCY / max(per_xcd, 1)));
+  int n_rs, n_split;
+  pick_splits(p, total, per_xcd, n_rs, n_split);
   if constexpr (NAIVE) {  // fused_moe_lora_with_align: the align outputs
-    if (side_align(p, first_idle_xcd(units, n_split))) return;
+    if (side_align(p, first_idle_xcd(units * n_rs, n_split))) return;
   }
-  int unit, split;
-  if (!map_unit_xcd(blockIdx.x, units, n_split, unit, split)) return;
+  int sub, split;
+  if (!map_unit_xcd(blockIdx.x, units * n_rs, n_split, sub, split)) return;
+  const int unit = sub / n_rs, rpart = sub - unit * n_rs;
+  const int prows = p.B / n_rs;  // rows of the block this workgroup takes
   const int nsz = ((p.Ns + n_split - 1) / n_split + 15) / 16 * 16;
   const int n0 = split * nsz;
   if (n0 >= p.Ns) return;
@@ -528,11 +566,12 @@ __global__ void __launch_bounds__(kThreadsM) __attribute__((amdgpu_waves_per_eu(
   c.n1 = n1;
 
   const int tid = threadIdx.x;
-  for (int r0 = 0; r0 < p.B; r0 += kPassRows) {
+  const int rend = (rpart + 1) * prows;
+  for (int r0 = rpart * prows; r0 < rend; r0 += kPassRows) {
     if (tid < kPassRows) {
       int pid = p.numel, xr = -1;
       float wv = 1.f;
-      if (r0 + tid < p.B) {
+      if (r0 + tid < rend) {
         pid = NAIVE ? s_ids[r0 + tid] : p.sorted[l * p.cap + b * p.B + r0 + tid];
         if (pid < p.numel) {
           xr = p.x_per_pair ? pid : pid / p.topk;
