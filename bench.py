@@ -381,13 +381,14 @@ def prefill_line(args, dev, variant):
     return res
 
 
-def align_stress_line(args, dev):
+def align_stress_line(args, dev, workload="align_stress"):
     """The align step alone on its stress case (M = 65536, topk = 8, E = 256,
-    L = 16, BLOCK_M = 64): graph-timed calls and event-timed windows."""
+    L = 16, BLOCK_M = 64; or another align-only workload): graph-timed calls
+    and event-timed windows."""
     import torch
     import moe_lora_adapter_amd as mla
     from moe_lora_adapter_amd import synth
-    s = synth.shape("align_stress")
+    s = synth.shape(workload)
     case = synth.draw(s, with_tensors=False)
     work = algorithmic_work(case)
     steps = max(10, min(args.steps, 200))
@@ -749,6 +750,22 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     mla.lib()
     s = synth.shape(args.workload)
+    if s.align_only:
+        # an align-only workload: the align step is the whole step
+        log(f"workload {s.name}: align only")
+        if args.calibrate_copy:
+            copy_calibration(dev)
+        res = align_stress_line(args, dev, s.name)
+        out = {"metric": "moe_lora_align us/call", "value": res["us_per_call"], "unit": "us/call",
+               "n_gpus": 1, "steps": res["steps"], "warmup": args.warmup,
+               "ms_per_step": round(res["us_per_call"] / 1e3, 6), "higher_is_better": False,
+               "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+               "data": "synthetic (seeded routing and adapter mapping, no dataset)",
+               "config": {"workload": s.name, "M": s.M, "topk": s.topk, "E": s.E, "L": s.L,
+                          "block_m": s.block_m, "step": "moe_lora_align"},
+               "align": res}
+        print(json.dumps(out), flush=True)
+        return 0
     log(f"workload {s.name}: drawing inputs")
     case = synth.draw(s)
     work = algorithmic_work(case)
