@@ -119,3 +119,18 @@ def test_draw_layer_shares_the_routing(name):
     assert np.array_equal(c2.lora_a[:, c13.active_slots], own.lora_a[:, own.active_slots])
     with pytest.raises(KeyError):
         synth.w2_partner("qwen3_prefill")
+
+
+def test_active_count_buckets():
+    from moe_lora_adapter_amd import graphs
+    assert graphs.active_count_buckets(1) == [0, 1]
+    assert graphs.active_count_buckets(4) == [0, 1, 2, 4]
+    assert graphs.active_count_buckets(6) == [0, 1, 2, 4, 6]
+    assert graphs.active_count_buckets(8) == [0, 1, 2, 4, 8]
+    # key count for L = 4 and two batch sizes: 4 buckets x 2
+    assert 2 * len(graphs.active_count_buckets(4)) == 8
+    assert [graphs.bucket_for(n, 6) for n in range(7)] == [0, 1, 2, 4, 4, 6, 6]
+    with pytest.raises(ValueError):
+        graphs.bucket_for(7, 6)
+    with pytest.raises(ValueError):
+        graphs.active_count_buckets(0)

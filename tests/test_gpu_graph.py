@@ -117,3 +117,63 @@ def test_one_graph_all_active_counts(name, path):
                         s.add, x_per_pair=s.x_per_pair)
         gh.assert_fused_close(gh.bf16_host_f64(y).reshape(s.numel, s.N), ref,
                               f"{name}/{path}/{n_active}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "oss20b_decode_w13_a6", "qwen3_prefill"])
+def test_graph_per_active_count_bucket(name):
+    """The per-bucket scheme: one graph per bound on the active slots
+    (max_active_loras = bucket), the host choosing the bucket from the batch's
+    adapters; each replay equals the eager launch bounded by L, bit for bit."""
+    from moe_lora_adapter_amd import graphs
+    s = synth.shape(name, dist="stress")
+    rng = np.random.default_rng(4343)
+    c = synth.draw(s)
+    dc = gh.DeviceCase(c)
+    dc.a, dc.b = _full_adapters(s, rng)
+    mapping = dc.mapping
+    y = dc.y_in.clone()
+    al = mla.alloc_align_output(s.M, s.topk, s.E, s.L, s.block_m, gh.DEV)
+    ws = torch.empty(max(16, mla.align_workspace_size(s.M, s.topk, s.E, s.L, s.block_m)),
+                     dtype=torch.uint8, device=gh.DEV)
+
+    def call(bound):
+        mla.moe_lora_align(dc.topk_ids, mapping, s.E, s.L, s.block_m, out=al, workspace=ws)
+        mla.fused_moe_lora(dc.x, dc.a, dc.b, al, dc.w, y, mul_routed_weight=s.mul,
+                           add_inputs=s.add, x_per_pair=s.x_per_pair, max_active_loras=bound)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(s.L)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    per_bucket = {}
+    for bk in graphs.active_count_buckets(s.L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(bk)
+        per_bucket[bk] = g
+    orc = oracle.load()
+    a_host = dc.a.view(torch.int16).cpu().numpy().view(np.uint16)
+    b_host = dc.b.view(torch.int16).cpu().numpy().view(np.uint16)
+    for n_active, m in _mappings(s, rng):
+        bk = graphs.bucket_for(len(np.unique(m[m >= 0])), s.L)
+        _log(f"bucket graphs {name}: {n_active} active -> bucket {bk}")
+        mapping.copy_(torch.from_numpy(m))
+        y.copy_(dc.y_in)
+        torch.cuda.synchronize()
+        call(s.L)
+        torch.cuda.synchronize()
+        eager = y.clone()
+        for rep in range(2):
+            y.copy_(dc.y_in)
+            al.num_tokens_post_padded.fill_(-7)
+            torch.cuda.synchronize()
+            per_bucket[bk].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), \
+                f"{n_active} active, bucket {bk}, replay {rep}"
+        ref = orc.fused(c.x, a_host, b_host, c.topk_ids, m, c.topk_weights, c.y_in, s.mul,
+                        s.add, x_per_pair=s.x_per_pair)
+        gh.assert_fused_close(gh.bf16_host_f64(y).reshape(s.numel, s.N), ref,
+                              f"{name}/bucket {bk}/{n_active}")
