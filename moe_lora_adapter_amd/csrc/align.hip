@@ -449,7 +449,10 @@ static int lds_per_block() {
 
 // Tiles of at least kMinTile pairs; at most 2^20 / (L E) of them, so that the
 // per-tile counts fit a fixed workspace bound (4 MiB).
-constexpr int64_t kMinTile = 512;
+#ifndef MLR_ALIGN_MIN_TILE
+#define MLR_ALIGN_MIN_TILE 512
+#endif
+constexpr int64_t kMinTile = MLR_ALIGN_MIN_TILE;
 
 AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   (void)B;
