@@ -64,6 +64,12 @@ if ROOT not in sys.path:
 METRIC = ("fused MoE-LoRA µs/call + achieved HBM TB/s (decode) / MFMA % (prefill)")
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# attainable dense bf16 MFMA rates measured on MI355X with loops of eight
+# independent products per wavefront on every SIMD: v_mfma_f32_32x32x16_bf16
+# reaches 2310 TFLOP/s, v_mfma_f32_16x16x32_bf16 (the instruction the fused
+# kernels use) 1260 TFLOP/s
+BF16_MEASURED_TFLOPS_32X32X16 = 2310.0
+BF16_MEASURED_TFLOPS_16X16X32 = 1260.0
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
@@ -290,10 +296,12 @@ def time_kernel_events(sets, s, variant, which, launches):
     return e0.elapsed_time(e1) * 1e3 / launches
 
 
-def time_kernel_windows(sets, s, variant, which, launches, windows=5):
+def time_kernel_windows(sets, s, variant, which, launches, windows=5, out=None):
     """time_kernel_events over several windows: (mean, p10, p90) of the
-    per-window averages, in us."""
+    per-window averages, in us; with a dict in `out`, also its p50 there."""
     w = [time_kernel_events(sets, s, variant, which, launches) for _ in range(windows)]
+    if out is not None:
+        out["p50"] = float(np.percentile(w, 50))
     return float(np.mean(w)), float(np.percentile(w, 10)), float(np.percentile(w, 90))
 
 
@@ -352,7 +360,8 @@ def prefill_line(args, dev, variant):
     torch.cuda.synchronize()
     reps = []
     time_steps_graph(sets, s, variant, steps, replays=reps, n_replays=5)
-    kus, k10, k90 = time_kernel_windows(sets, s, variant, "fused", steps)
+    med = {}
+    kus, k10, k90 = time_kernel_windows(sets, s, variant, "fused", steps, out=med)
     kname = _kernel_name(s, variant)
     gbps = work["fused_bytes"] / (kus * 1e-6) / 1e9
     tflops = work["fused_flops"] / (kus * 1e-6) / 1e12
@@ -367,9 +376,12 @@ def prefill_line(args, dev, variant):
                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                         "algorithmic_bytes_per_launch": work["fused_bytes"],
                         "kernel_us_avg": round(kus, 3), "kernel_us_p10": round(k10, 3),
-                        "kernel_us_p90": round(k90, 3)},
+                        "kernel_us_p50": round(med["p50"], 3), "kernel_us_p90": round(k90, 3)},
            "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                    "measured_peak_tflops": {"32x32x16": BF16_MEASURED_TFLOPS_32X32X16,
+                                             "16x16x32": BF16_MEASURED_TFLOPS_16X16X32},
+                    "frac_of_measured_16x16x32": round(tflops / BF16_MEASURED_TFLOPS_16X16X32, 4),
                     "counters": None if ctr is None else
                     {k: ctr[k] for k in ("mfma_util_pct", "mfma_flops_bf16_per_dispatch",
                                          "mfma_issued_tflops", "kernel_trace_avg_us")
@@ -815,16 +827,17 @@ def main(argv=None):
     replays = []
     sec_per_step = time_steps_graph(sets, s, variant, args.steps, fn=step_fn, replays=replays)
     log("timing kernels with events")
+    med = {}
     if path == "naive":
-        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, naive_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, naive_fn, args.steps, out=med)
         align_avg = None
         kbytes = work["naive_bytes"]
     elif path == "with_align":
-        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, wa_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, wa_fn, args.steps, out=med)
         align_avg = None
         kbytes = work["with_align_bytes"]
     else:
-        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, fused_fn, args.steps)
+        fused_avg, f10, f90 = time_kernel_windows(sets, s, variant, fused_fn, args.steps, out=med)
         align_avg = time_kernel_events(sets, s, variant, "align", args.steps)
         kbytes = work["fused_bytes"]
 
@@ -868,10 +881,11 @@ def main(argv=None):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": kbytes,
                      "kernel_us_avg": round(fused_avg, 3),
-                     "kernel_us_p10": round(f10, 3), "kernel_us_p90": round(f90, 3),
+                     "kernel_us_p10": round(f10, 3), "kernel_us_p50": round(med["p50"], 3),
+                     "kernel_us_p90": round(f90, 3),
                      "kernel_timing": "HIP events on the kernel's stream, 5 windows of K "
-                                      "back-to-back launches; avg over windows, p10/p90 of "
-                                      "the window averages"},
+                                      "back-to-back launches; avg over windows, p10/p50/p90 "
+                                      "of the window averages"},
         "us_per_call_replays": spread([r * 1e6 for r in replays]),
         "fused_tflops": round(tflops, 3),
         "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
