@@ -354,8 +354,8 @@ def prefill_line(args, dev, variant):
     sets = [DeviceSet(case, dev)]
     for _ in range(copies - 1):
         sets.append(DeviceSet(case, dev, proto=sets[0]))
-    steps = max(10, min(args.steps, 100))
-    for i in range(min(args.warmup, 5)):
+    steps = max(10, args.steps)
+    for i in range(max(args.warmup, 3)):
         step(sets[i % copies], s, variant)
     torch.cuda.synchronize()
     reps = []
