@@ -134,3 +134,32 @@ def test_active_count_buckets():
         graphs.bucket_for(7, 6)
     with pytest.raises(ValueError):
         graphs.active_count_buckets(0)
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", dict(dist="stress")),
+                                     ("oss20b_decode_w13_a6", dict(K=256, Ns=256)),
+                                     ("align_stress", {}),
+                                     ("qwen3_prefill", dict(M=64, K=64, Ns=64, r=8))])
+def test_generator_is_deterministic(name, kw):
+    """The same seed draws the same bytes; another seed draws other routing.
+    The drawn routing has the recipe's structure: the mapping names only the
+    drawn active slots (or -1), every token's top-k experts are distinct and in
+    range, and the routing weights of a token sum to one."""
+    s = synth.shape(name, **kw)
+    c1, c2 = synth.draw(s), synth.draw(s)
+    for k in ("active_slots", "token_lora_mapping", "topk_ids", "topk_weights",
+              "x", "lora_a", "lora_b", "y_in"):
+        a, b = getattr(c1, k), getattr(c2, k)
+        assert (a is None) == (b is None), k
+        if a is not None:
+            assert a.dtype == b.dtype and a.tobytes() == b.tobytes(), k
+    other = synth.draw(s.replace(seed=s.seed + 1), with_tensors=False)
+    assert not np.array_equal(other.topk_ids, c1.topk_ids)
+    assert len(c1.active_slots) == s.active == len(set(c1.active_slots.tolist()))
+    used = set(c1.token_lora_mapping.tolist()) - {-1}
+    assert used <= set(c1.active_slots.tolist())
+    ids = c1.topk_ids
+    assert ids.shape == (s.M, s.topk) and ids.min() >= 0 and ids.max() < s.E
+    if s.topk <= s.E:
+        assert all(len(set(row)) == s.topk for row in ids.tolist())
+    np.testing.assert_allclose(c1.topk_weights.sum(axis=1), 1.0, rtol=1e-5)
