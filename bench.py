@@ -14,9 +14,10 @@ Timing:
     bracketed by synchronize on both sides.  Every input buffer is rotated
     over enough copies that the touched bytes exceed 4x the 256 MB
     Infinity Cache, so weights are read from HBM (``--warm`` disables this).
-  * roofline: the fused kernel's own duration from HIP events on its stream
-    around K back-to-back launches (queued behind a short GPU sleep so they
-    run back to back), against the algorithmic bytes
+  * roofline: the fused kernel's own duration from HIP events on the replay
+    stream around replays of one graph of K launches of that kernel alone
+    (the eager figure beside it: K back-to-back launches queued behind a
+    short GPU sleep), against the algorithmic bytes
     it must move (weights of the active (slice, slot, expert) groups once,
     the X rows it reads, the Y rows it reads and writes, routed weights and
     block metadata).
@@ -296,12 +297,54 @@ def time_kernel_events(sets, s, variant, which, launches):
     return e0.elapsed_time(e1) * 1e3 / launches
 
 
+def time_kernel_graph(sets, s, variant, which, launches, windows=5):
+    """Per-window average duration of one kernel launched as a graph replay
+    runs it: `launches` launches of it (rotating over the copies) captured in
+    one HIP graph, each of `windows` replays bracketed by a pair of HIP events
+    on the stream the replay runs on.  Returns the list of window averages
+    in us.  (Eager launches carry their kernel arguments in host memory,
+    which a kernel's first read then waits for; graph-launched kernels do
+    not.)"""
+    import torch
+    fn = which if callable(which) else (
+        (lambda ds: run_fused(ds, s, variant)) if which == "fused" else (lambda ds: run_align(ds, s)))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(sets[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(windows):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / launches)
+    del g
+    return out
+
+
 def time_kernel_windows(sets, s, variant, which, launches, windows=5, out=None):
-    """time_kernel_events over several windows: (mean, p10, p90) of the
-    per-window averages, in us; with a dict in `out`, also its p50 there."""
-    w = [time_kernel_events(sets, s, variant, which, launches) for _ in range(windows)]
+    """A kernel's duration over several windows of graph-replayed launches
+    (time_kernel_graph): (mean, p10, p90) of the per-window averages, in us;
+    with a dict in `out`, also their p50 and the same statistics of eager
+    launches (time_kernel_events) there."""
+    w = time_kernel_graph(sets, s, variant, which, launches, windows)
     if out is not None:
         out["p50"] = float(np.percentile(w, 50))
+        ew = [time_kernel_events(sets, s, variant, which, launches) for _ in range(windows)]
+        out["eager_avg"] = float(np.mean(ew))
+        out["eager_p50"] = float(np.percentile(ew, 50))
     return float(np.mean(w)), float(np.percentile(w, 10)), float(np.percentile(w, 90))
 
 
@@ -376,7 +419,8 @@ def prefill_line(args, dev, variant):
                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                         "algorithmic_bytes_per_launch": work["fused_bytes"],
                         "kernel_us_avg": round(kus, 3), "kernel_us_p10": round(k10, 3),
-                        "kernel_us_p50": round(med["p50"], 3), "kernel_us_p90": round(k90, 3)},
+                        "kernel_us_p50": round(med["p50"], 3), "kernel_us_p90": round(k90, 3),
+                        "kernel_us_eager_avg": round(med["eager_avg"], 3)},
            "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                     "measured_peak_tflops": {"32x32x16": BF16_MEASURED_TFLOPS_32X32X16,
@@ -883,9 +927,11 @@ def main(argv=None):
                      "kernel_us_avg": round(fused_avg, 3),
                      "kernel_us_p10": round(f10, 3), "kernel_us_p50": round(med["p50"], 3),
                      "kernel_us_p90": round(f90, 3),
-                     "kernel_timing": "HIP events on the kernel's stream, 5 windows of K "
-                                      "back-to-back launches; avg over windows, p10/p50/p90 "
-                                      "of the window averages"},
+                     "kernel_us_eager_avg": round(med["eager_avg"], 3),
+                     "kernel_timing": "HIP events on the replay stream around 5 replays of "
+                                      "one graph of K launches of the kernel alone; avg over "
+                                      "the replays, p10/p50/p90 of the replay averages "
+                                      "(kernel_us_eager_avg: the same launches eager)"},
         "us_per_call_replays": spread([r * 1e6 for r in replays]),
         "fused_tflops": round(tflops, 3),
         "mfma_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 5),
