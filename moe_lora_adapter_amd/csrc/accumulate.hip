@@ -31,7 +31,7 @@ __global__ void __launch_bounds__(kTA) accumulate_kernel(uint16_t* __restrict__ 
     for (int i = 0; i < 4; ++i) {
       const float lo = bf16_lo(ys[i]) + bf16_lo(ds[i]);
       const float hi = bf16_hi(ys[i]) + bf16_hi(ds[i]);
-      o[i] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+      o[i] = pack_bf16x2(lo, hi);
     }
     reinterpret_cast<uint4*>(y)[c] = make_uint4(o[0], o[1], o[2], o[3]);
   }

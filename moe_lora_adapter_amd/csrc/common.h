@@ -91,13 +91,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// (a select, not a branch: the compiler turned the early return for NaN into
-// a divergent branch around every conversion of an epilogue)
+// f32 -> bf16, rounded to nearest even, subnormals kept, NaN stays NaN: one
+// v_cvt_pk_bf16_f32 (gfx950), which rounds exactly as adding 0x7fff plus the
+// kept lowest bit to the f32 pattern and truncating does, for every finite
+// input.  The pair form converts two values with one instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t qnan = (u >> 16) | 0x40u;
-  return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Raw buffer access: a wave-uniform descriptor (base, byte range) in scalar

@@ -344,7 +344,7 @@ __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx
     uint32_t ow[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      ow[e] = uint32_t(f32_to_bf16(o[2 * e])) | (uint32_t(f32_to_bf16(o[2 * e + 1])) << 16);
+      ow[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
     buf_st16(make_uint4(ow[0], ow[1], ow[2], ow[3]), c.yr, ychunk_off(c, yc, i, nb), 0);
   }
 }

@@ -536,39 +536,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
     const float wrow = lr < kRows ? s_w[lr] : 0.f;
 
-    for (int t = 0; t < T; ++t) {
-      if (t == nA) {
-        // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
-        // (the k-step partials go through the X buffer, which only the K
-        // split's fallback still reads)
-        if (xch && tid == 0) {
-          uint32_t m = 0;
-#pragma unroll
-          for (int q = 0; q < kXchPeers; ++q) m = s_left[q] > m ? s_left[q] : m;
-          s_tag = m + 1u;
-          s_miss = 0;
-        }
-        reduce_ksteps<R>(acc, XCH ? s_part : reinterpret_cast<float*>(xs));
-        if (xch) {
-          const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
-          // the wavefronts holding v publish; then every wavefront issues
-          // the next NS - 1 B stages, which stream while the holders wait
-          // for the peers' partials (their polls retire after those loads)
-          publish_partial<R>(xs_slot, acc, split, tag);
-          for (int u = nA; u < nA + NS - 1 && u < T; ++u)
-            issue_stage<R>(p, ar, br, u, nA, ka0, ncols, ring_lds + (u % NS) * kStage);
-          gather_partials<R>(p, xs_slot, acc, s_part, s_peer, &s_miss, xs, a_rsrc, split, C, nA_all, tag);
-        }
-        // lane (lr, lq) of wavefront w < RT holds v[row lr][16 w + 4 lq + i]
-        if (w < G::RT && lr < kRows) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint16_t hi = f32_to_bf16(acc[i]);
-            s_vb[lr * VP + 16 * w + 4 * lq + i] = hi;
-            s_vl[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i] - bf16_to_f32(hi));
-          }
-        }
-      }
+    // stage t's wait and the next stage's issue (the ring's step)
+    auto ring_step = [&](int t) {
       // stage t (and, at t = 0, the X rows issued before it): the later
       // stages stay in flight, so the ring never drains to empty
       // (with the K split the A stages drain before the exchange)
@@ -590,60 +559,100 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
         if (t + ahead < lim)
           issue_stage<R>(p, ar, br, t + ahead, nA, ka0, ncols, ring_lds + ((t + ahead) % NS) * kStage);
       }
+    };
+    // ---- shrink, the A stages: V^T[rank tile rt] += A[16 ranks x 32 k] . X^T
+    for (int t = 0; t < nA; ++t) {
+      ring_step(t);
       const uint4* st = reinterpret_cast<const uint4*>(ring + (t % NS) * kStage);
-      if (t < nA) {
-        // ---- shrink: V^T[rank tile rt] += A[16 ranks x 32 k] . X^T
-        const int j = 16 * rt + lr, c = 4 * ka + lq;
-        const uint4 a = st[j * G::CPRK + (c ^ (j & 7))];
-        const int xc = (ka0 + t) * (G::KT / 8) + c;
-        const uint4 x = (lr < kRows && xc < K8)
-                            ? reinterpret_cast<const uint4*>(xs)[lr * K8 + xc] : zero4;
-        acc = mfma16(a, x, acc);
-      } else {
-        // ---- expand: D^T[16 cols x 16 rows] = B[16 cols x 32 ranks] . V^T
-        const int u = t - nA;
-        if (u == 0) {
-          // operand column lr: V_hi of row lr (lr < kRows), V_lo of row
-          // lr - kRows (kRows <= lr < 2 kRows), else zero
+      const int j = 16 * rt + lr, c = 4 * ka + lq;
+      const uint4 a = st[j * G::CPRK + (c ^ (j & 7))];
+      const int xc = (ka0 + t) * (G::KT / 8) + c;
+      // one 16-byte read at a clamped index, then the select (a read
+      // guarded by the condition became four masked 4-byte reads)
+      const uint4 xv = reinterpret_cast<const uint4*>(xs)[min(lr, kRows - 1) * K8 + min(xc, K8 - 1)];
+      const uint4 x = (lr < kRows && xc < K8) ? xv : zero4;
+      acc = mfma16(a, x, acc);
+    }
+    {
+      // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
+      // (the k-step partials go through the X buffer, which only the K
+      // split's fallback still reads)
+      if (xch && tid == 0) {
+        uint32_t m = 0;
 #pragma unroll
-          for (int ks = 0; ks < G::KS; ++ks) {
-            const int row = lr < kRows ? lr : (lr < 2 * kRows ? lr - kRows : 0);
-            const uint16_t* src = lr < kRows ? s_vb : s_vl;
-            vop[ks] = lr < 2 * kRows ? *reinterpret_cast<const uint4*>(src + row * VP + 32 * ks + 8 * lq)
-                                     : zero4;
-          }
+        for (int q = 0; q < kXchPeers; ++q) m = s_left[q] > m ? s_left[q] : m;
+        s_tag = m + 1u;
+        s_miss = 0;
+      }
+      reduce_ksteps<R>(acc, XCH ? s_part : reinterpret_cast<float*>(xs));
+      if (xch) {
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
+        // the wavefronts holding v publish; then every wavefront issues
+        // the next NS - 1 B stages, which stream while the holders wait
+        // for the peers' partials (their polls retire after those loads)
+        publish_partial<R>(xs_slot, acc, split, tag);
+        for (int u = nA; u < nA + NS - 1 && u < T; ++u)
+          issue_stage<R>(p, ar, br, u, nA, ka0, ncols, ring_lds + (u % NS) * kStage);
+        gather_partials<R>(p, xs_slot, acc, s_part, s_peer, &s_miss, xs, a_rsrc, split, C, nA_all, tag);
+      }
+      // lane (lr, lq) of wavefront w < RT holds v[row lr][16 w + 4 lq + i]
+      if (w < G::RT && lr < kRows) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t hi = f32_to_bf16(acc[i]);
+          s_vb[lr * VP + 16 * w + 4 * lq + i] = hi;
+          s_vl[lr * VP + 16 * w + 4 * lq + i] = f32_to_bf16(acc[i] - bf16_to_f32(hi));
         }
-        for (int ct = w; ct < G::CT; ct += kST / kWave) {
-          const int col = 16 * ct + lr;
-          // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage.
-          // Its Y values are read before the products so the read's latency
-          // hides behind them (lanes with nothing to write read row 0,
-          // column 0 and drop it).
-          const int n = u * G::NCS + 16 * ct + 4 * lq;
-          const bool live = lr < nr && n < ncols;
-          uint2* yp = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(ys) +
-                                               (live ? lr * ncols + n : 0));
-          const uint2 yv = *yp;
-          f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // ---- expand, the B stages: D^T[16 cols x 16 rows] = B[16 cols x 32 ranks] . V^T
+    // (a loop of its own, so that the expand's operands do not share
+    // registers with the shrink's and move between them at every stage)
+    for (int t = nA; t < T; ++t) {
+      ring_step(t);
+      const uint4* st = reinterpret_cast<const uint4*>(ring + (t % NS) * kStage);
+      const int u = t - nA;
+      if (u == 0) {
+        // operand column lr: V_hi of row lr (lr < kRows), V_lo of row
+        // lr - kRows (kRows <= lr < 2 kRows), else zero
 #pragma unroll
-          for (int ks = 0; ks < G::KS; ++ks) {
-            const int jc = 4 * ks + lq;
-            const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
-            dt = mfma16(bb, vop[ks], dt);
-          }
-          // lane (lr, lq) adds the V_lo product of its row, held kRows lanes up
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dt[i] += lane_plus_rows(dt[i]);
-          // every lane forms and stores its result -- lanes with nothing to
-          // write into a dummy LDS slot -- so no branch exists that the Y read
-          // and the arithmetic could be sunk into (below the products)
-          const float ya = p.add ? 1.f : 0.f;
-          const float o[4] = {dt[0] * wrow + ya * bf16_lo(yv.x), dt[1] * wrow + ya * bf16_hi(yv.x),
-                              dt[2] * wrow + ya * bf16_lo(yv.y), dt[3] * wrow + ya * bf16_hi(yv.y)};
-          const uint2 out = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
-                                       uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
-          *(live ? yp : &s_dummy[lane]) = out;
+        for (int ks = 0; ks < G::KS; ++ks) {
+          const int row = lr < kRows ? lr : (lr < 2 * kRows ? lr - kRows : 0);
+          const uint16_t* src = lr < kRows ? s_vb : s_vl;
+          const uint4 vv = *reinterpret_cast<const uint4*>(src + row * VP + 32 * ks + 8 * lq);
+          vop[ks] = lr < 2 * kRows ? vv : zero4;
         }
+      }
+      for (int ct = w; ct < G::CT; ct += kST / kWave) {
+        const int col = 16 * ct + lr;
+        // lane (lr, lq): row lr, columns 16 ct + 4 lq .. + 3 of this stage.
+        // Its Y values are read before the products so the read's latency
+        // hides behind them (lanes with nothing to write read row 0,
+        // column 0 and drop it).
+        const int n = u * G::NCS + 16 * ct + 4 * lq;
+        const bool live = lr < nr && n < ncols;
+        uint2* yp = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(ys) +
+                                             (live ? lr * ncols + n : 0));
+        const uint2 yv = *yp;
+        f32x4_t dt = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+          const int jc = 4 * ks + lq;
+          const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
+          dt = mfma16(bb, vop[ks], dt);
+        }
+        // lane (lr, lq) adds the V_lo product of its row, held kRows lanes up
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dt[i] += lane_plus_rows(dt[i]);
+        // every lane forms and stores its result -- lanes with nothing to
+        // write into a dummy LDS slot -- so no branch exists that the Y read
+        // and the arithmetic could be sunk into (below the products)
+        const float ya = p.add ? 1.f : 0.f;
+        const float o[4] = {dt[0] * wrow + ya * bf16_lo(yv.x), dt[1] * wrow + ya * bf16_hi(yv.x),
+                            dt[2] * wrow + ya * bf16_lo(yv.y), dt[3] * wrow + ya * bf16_hi(yv.y)};
+        const uint2 out = make_uint2(pack_bf16x2(o[0], o[1]),
+                                     pack_bf16x2(o[2], o[3]));
+        *(live ? yp : &s_dummy[lane]) = out;
       }
     }
     __syncthreads();

@@ -255,7 +255,7 @@ __device__ __forceinline__ void expand_batch(const FusedParams& p, const int* s_
         lo += bf16_lo(in[h]);
         hi += bf16_hi(in[h]);
       }
-      outw[h] = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+      outw[h] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<uint4*>(yp) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
   }

@@ -345,8 +345,8 @@ lora_expand_kernel(FusedParams p) {
               o[3] += bf16_hi(yv[i][m].y);
             }
             *reinterpret_cast<uint2*>(p.y + yrow[m] + n) =
-                make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
-                           uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+                make_uint2(pack_bf16x2(o[0], o[1]),
+                           pack_bf16x2(o[2], o[3]));
           }
         }
       }

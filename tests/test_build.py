@@ -72,13 +72,25 @@ def test_stream_stage_loop_keeps_the_ring_in_flight():
     for m in re.finditer(r"^(_ZN\S*fused_stream_kernel\S*):", asm, re.M):
         found += 1
         body = asm[m.start():asm.index(".Lfunc_end", m.start())].splitlines()
-        depth = 0
+        # each line's innermost loop (the header its block names) and its depth
+        loop_of, depth, cur, d = [], [], None, 0
+        for line in body:
+            if re.match(r"^(\.LBB\S+|; %bb\.\d+):", line):
+                h = re.search(r"Loop Header: Depth", line)
+                inl = re.search(r"in Loop: Header=(\S+)", line)
+                cur = line.split(":")[0].lstrip(".") if h else (inl.group(1) if inl else None)
+                dm = re.search(r"Depth=(\d+)", line)
+                d = int(dm.group(1)) if dm else 0
+            loop_of.append(cur)
+            depth.append(d)
+        # stage loops: the loops inside a pass (depth 2) whose own blocks issue
+        # ring loads (direct to LDS); the pass loop itself sets a pass up
+        stage_loops = {loop_of[k] for k, line in enumerate(body)
+                       if depth[k] == 2 and "buffer_load_dwordx4" in line and " lds" in line}
+        assert stage_loops, f"{m.group(1)}: no stage loop found"
         bad = []
         for k, line in enumerate(body):
-            if line.startswith(".LBB"):
-                d = re.search(r"Depth=(\d+)", line)
-                depth = int(d.group(1)) if d else 0
-            if "vmcnt(0)" in line and depth == 2:
+            if loop_of[k] in stage_loops and "vmcnt(0)" in line:
                 nxt = " ".join(body[k + 1:k + 3])
                 if "s_barrier" not in nxt:
                     bad.append(k)
