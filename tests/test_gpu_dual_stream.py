@@ -40,6 +40,46 @@ def test_accumulate_bit_exact(n):
     assert torch.equal(yd.cpu().view(torch.int16), ref.view(torch.int16))
 
 
+def test_accumulate_rounding_edges():
+    """The one rounding of every kernel's output, through moe_lora_accumulate:
+    sums that fall exactly halfway between two bf16 values (ties to even, both
+    directions, both signs), subnormal sums, sums past the largest bf16 (to
+    infinity), cancellation to zero, against an fp32 add rounded to nearest
+    even on the host."""
+    bf = torch.bfloat16
+    ulp_at_1 = 2.0 ** -7
+    tiny = 2.0 ** -133                     # a bf16 subnormal
+    big = float(torch.finfo(bf).max)
+    pairs = [
+        (1.0, ulp_at_1 / 2),               # tie: 1 (even) stays
+        (1.0 + ulp_at_1, ulp_at_1 / 2),    # tie: odd rounds up to even
+        (-1.0, -ulp_at_1 / 2),
+        (-(1.0 + ulp_at_1), -ulp_at_1 / 2),
+        (1.0, ulp_at_1 / 4),               # below the tie: down
+        (1.0, 3 * ulp_at_1 / 4),           # above the tie: up
+        (tiny, tiny),                      # subnormal + subnormal
+        (3 * tiny, -tiny),
+        (2.0 ** -126, -2.0 ** -127),       # normal - subnormal -> subnormal
+        (big, big),                        # overflow -> inf
+        (-big, -big),
+        (2.5, -2.5),                       # exact cancellation
+        (0.0, -0.0),
+    ]
+    y = torch.tensor([a for a, _ in pairs], dtype=torch.float32).to(bf)
+    d = torch.tensor([b for _, b in pairs], dtype=torch.float32).to(bf)
+    # the inputs are exact in bf16
+    assert torch.equal(y.float(), torch.tensor([a for a, _ in pairs], dtype=torch.float32))
+    assert torch.equal(d.float(), torch.tensor([b for _, b in pairs], dtype=torch.float32))
+    ref = (y.float() + d.float()).to(bf)
+    yd, dd = y.to(gh.DEV), d.to(gh.DEV)
+    mla.moe_lora_accumulate(yd, dd)
+    torch.cuda.synchronize()
+    got = yd.cpu()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), (got, ref)
+    assert got[0].item() == 1.0 and got[1].item() == 1.0 + 2 * ulp_at_1
+    assert got[9].item() == float("inf") and got[10].item() == float("-inf")
+
+
 def _dual(dc, al, y, delta, aux, ev):
     """Base output (here: Y_in) on the current stream, the LoRA delta on `aux`, then the join."""
     s = dc.s
