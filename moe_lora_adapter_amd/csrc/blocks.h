@@ -14,7 +14,7 @@ __device__ __forceinline__ int count_blocks(const FusedParams& p) {
   for (int c0 = 0; c0 < p.L; c0 += kWave) {
     const int sl = c0 + lane_id();
     const int nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
-    run += __shfl(wave_incl_scan(nbk), kWave - 1);
+    run += lane_value(wave_incl_scan(nbk), kWave - 1);
   }
   return run;
 }
@@ -35,7 +35,7 @@ __device__ __forceinline__ BlockScan scan_blocks(const FusedParams& p) {
     const int sl = lane_id();
     sc.nbk = sl < p.L ? p.ntpp[sl] / p.B : 0;
     sc.incl = wave_incl_scan(sc.nbk);
-    sc.total = __shfl(sc.incl, kWave - 1);
+    sc.total = lane_value(sc.incl, kWave - 1);
   } else {
     sc.nbk = sc.incl = 0;
     sc.total = count_blocks(p);
@@ -56,10 +56,10 @@ __device__ __forceinline__ void find_block(const FusedParams& p, int g, int& l, 
     if (hit) {
       const int first = __builtin_ctzll(hit);
       l = c0 + first;
-      b = g - (__shfl(incl, first) - __shfl(nbk, first));
+      b = g - (lane_value(incl, first) - lane_value(nbk, first));
       return;
     }
-    run = __shfl(incl, kWave - 1);
+    run = lane_value(incl, kWave - 1);
   }
   l = b = 0;
 }
@@ -85,7 +85,7 @@ __device__ __forceinline__ void find_block(const FusedParams& p, const BlockScan
     const uint64_t hit = __ballot(sc.incl > g);
     const int first = hit ? __builtin_ctzll(hit) : 0;
     l = first;
-    b = g - (__shfl(sc.incl, first) - __shfl(sc.nbk, first));
+    b = g - (lane_value(sc.incl, first) - lane_value(sc.nbk, first));
   } else {
     find_block(p, g, l, b);
   }

@@ -19,22 +19,72 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return (uint64_t(1) << lane) - 1;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
+// DPP move of a lane value (VALU, no trip through the LDS crossbar): the
+// result of a lane whose source lies outside the pattern, or whose row is
+// not in row_mask, is 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// The partner of this lane in a butterfly at distance O (a power of two
+// below 64): lane ^ O, except that O = 4 pairs lane i with i ^ 7 inside
+// each group of 8 (DPP's half-row mirror).  Both differ from the lane in
+// bit log2(O) and agree on the bits above it, so a sum or reduce-scatter
+// over the levels O = 32, 16, ..., 1 pairs the same halves either way.
+// O = 32 and 16 are gfx950's lane-swap instructions, 8 a row rotation, 4, 2
+// and 1 DPP within a row.
+template <int O>
+__device__ __forceinline__ uint32_t butterfly_partner(uint32_t v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "distance");
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane_id() & 32) ? r[0] : r[1];
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else if constexpr (O == 8) {
+    return uint32_t(dpp_move<0x128>(int(v)));  // row_ror:8
+  } else if constexpr (O == 4) {
+    return uint32_t(dpp_move<0x141>(int(v)));  // row_half_mirror
+  } else if constexpr (O == 2) {
+    return uint32_t(dpp_move<0x4e>(int(v)));   // quad_perm [2,3,0,1]
+  } else {
+    return uint32_t(dpp_move<0xb1>(int(v)));   // quad_perm [1,0,3,2]
   }
+}
+
+__device__ __forceinline__ float butterfly_partner(float v, int o) {
+  const uint32_t u = __float_as_uint(v);
+  // o is a constant wherever this is called from an unrolled loop
+  switch (o) {
+    case 32: return __uint_as_float(butterfly_partner<32>(u));
+    case 16: return __uint_as_float(butterfly_partner<16>(u));
+    case 8: return __uint_as_float(butterfly_partner<8>(u));
+    case 4: return __uint_as_float(butterfly_partner<4>(u));
+    case 2: return __uint_as_float(butterfly_partner<2>(u));
+    default: return __uint_as_float(butterfly_partner<1>(u));
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts by 1, 2, 4
+// and 8 inside each row of 16 lanes, then the last lane of row 0 added to row
+// 1 and of row 2 to row 3, then the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_move<0x111>(v);       // row_shr:1
+  v += dpp_move<0x112>(v);       // row_shr:2
+  v += dpp_move<0x114>(v);       // row_shr:4
+  v += dpp_move<0x118>(v);       // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// The value of lane `src` (wave-uniform) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
 }
+
 
 // Mask of the lanes (among `active`) whose key equals this lane's key, found
 // by voting on each key bit in turn.  Keys are below 2^nbits.

@@ -32,12 +32,13 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int& which) {
       const uint32_t lo = __float_as_uint(v[q]), hi = __float_as_uint(v[q + half]);
       const float send = __uint_as_float((lo & m) | (hi & ~m));
       const float keep = __uint_as_float((hi & m) | (lo & ~m));
-      v[q] = keep + __shfl_xor(send, o);
+      v[q] = keep + butterfly_partner(send, o);
     }
     if (up) which += half;
   }
   float t = v[0];
-  for (; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+#pragma unroll
+  for (; o >= 1; o >>= 1) t += butterfly_partner(t, o);
   return t;
 }
 
@@ -237,7 +238,7 @@ __device__ __forceinline__ void expand_batch(const FusedParams& p, const int* s_
 #pragma unroll
       for (int u = 0; u < 8; ++u) d += vr[i][u] * b[u];
 #pragma unroll
-      for (int o = CPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
+      for (int o = CPR / 2; o >= 1; o >>= 1) d += butterfly_partner(d, o);
       if (jc == 0 && q < nchunks) s_d[i * kRowsPerBatch + q / CPR - t.row0] = d;
     }
   }

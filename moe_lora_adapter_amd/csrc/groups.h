@@ -91,7 +91,7 @@ __device__ inline int group_pairs(const FusedParams& p, GroupLds& g, PairGroup<T
     const int incl = wave_incl_scan(nblk);
     pg.excl[0] = incl - nblk;
     pg.nblk[0] = nblk;
-    return __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
+    return lane_value(incl, kWave - 1);
   }
   for (int i = t; i < kGroupHash; i += T) {
     g.key[i] = -1;
@@ -149,8 +149,8 @@ __device__ inline void group_block_wave(const FusedParams& p, const PairGroup<T>
   const int lane = lane_id();
   const uint64_t hit = __ballot(gi >= pg.excl[0] && gi < pg.excl[0] + pg.nblk[0]);
   const int src = hit ? __builtin_ctzll(hit) : 0;
-  const int key = __builtin_amdgcn_readfirstlane(__shfl(pg.key[0], src));
-  const int b = __builtin_amdgcn_readfirstlane(gi - __shfl(pg.excl[0], src));
+  const int key = lane_value(pg.key[0], src);
+  const int b = gi - lane_value(pg.excl[0], src);
   const bool match = pg.key[0] == key;
   const uint64_t m = __ballot(match);
   for (int i = lane; i < p.B; i += kWave) ids[i] = p.numel;
@@ -172,8 +172,8 @@ __device__ inline void group_block(const FusedParams& p, GroupLds& g, const Pair
     // the group leader whose block range holds gi, found in registers
     const uint64_t hit = __ballot(gi >= pg.excl[0] && gi < pg.excl[0] + pg.nblk[0]);
     const int src = hit ? __builtin_ctzll(hit) : 0;
-    const int key = __builtin_amdgcn_readfirstlane(__shfl(pg.key[0], src));
-    const int b = __builtin_amdgcn_readfirstlane(gi - __shfl(pg.excl[0], src));
+    const int key = lane_value(pg.key[0], src);
+    const int b = gi - lane_value(pg.excl[0], src);
     const bool match = pg.key[0] == key;
     const uint64_t m = __ballot(match);
     if (w == 0) {
