@@ -28,7 +28,7 @@
  *   - Calls on different streams may overlap if their outputs are disjoint.
  *
  * Limits: 1 <= E <= 1024 (the expert limit asked for in the review of PR
- * #29257), 1 <= L <= 1024, L*E <= 8192, block_m in {16, 32, 64, 128},
+ * #29257), 1 <= L <= 1024 (so L*E <= 2^20), block_m in {16, 32, 64, 128},
  * 1 <= r <= 128 (the one-shot kernel's compile-time rank bound in the prhub
  * summary of PR #42290, here an error code instead of an assert),
  * M*topk + min(E, M*topk)*(block_m-1) < 2^31 and L * capacity < 2^31.
@@ -105,7 +105,11 @@ MOE_LORA_API int64_t moe_lora_align_workspace_size(int64_t M, int32_t topk, int3
  *                       do not matter.
  * Pairs whose slot is outside [0, L) (including -1) or whose expert is
  * outside [0, E) are skipped; nothing traps on device.  The result does not
- * depend on thread timing: the same inputs give the same bytes.
+ * depend on thread timing: the same inputs give the same bytes.  When L*E is
+ * above 8192 (slot, expert) keys (and the call is not a one-wavefront one of
+ * at most 64 pairs and 64 slots), the work runs as several launches over
+ * ranges of 8192/E slots, each reading every pair, then one that lists the
+ * active slots; the workspace is sized for one range.
  */
 MOE_LORA_API int moe_lora_align(const int32_t *topk_ids, const int32_t *token_lora_mapping,
                    int64_t M, int32_t topk, int32_t E, int32_t L,

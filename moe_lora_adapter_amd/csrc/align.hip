@@ -32,7 +32,7 @@ constexpr int kLdsInts = 16384;  // 64 KiB of LDS per workgroup
 
 __device__ __forceinline__ int pair_key(const AlignParams& a, int p) {
   const int m = p / a.topk;
-  const int l = a.mapping[m];
+  const int l = int(unsigned(a.mapping[m]) - unsigned(a.l0));  // wraps: out of range stays out
   const int e = a.topk_ids[p];
   return (unsigned(l) < unsigned(a.L) && unsigned(e) < unsigned(a.E)) ? l * a.E + e : -1;
 }
@@ -185,7 +185,7 @@ __device__ __forceinline__ void load_keys(const AlignParams& a, int64_t base, in
   for (int i = 0; i < kKeyBatch; ++i) {
     const int p = int(min<int64_t>(base + i * kWave + lane, s1 - 1));
     e[i] = a.topk_ids[p];
-    l[i] = a.mapping[p / a.topk];
+    l[i] = int(unsigned(a.mapping[p / a.topk]) - unsigned(a.l0));
   }
 #pragma unroll
   for (int i = 0; i < kKeyBatch; ++i) {
@@ -457,11 +457,17 @@ constexpr int64_t kMinTile = MLR_ALIGN_MIN_TILE;
 AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   (void)B;
   AlignPlan pl{};
+  pl.pass_slots = L;
   if (numel <= kAlignWaveMaxPairs && L <= kAlignWaveMaxSlots) {
-    pl.wave = true;
+    pl.wave = true;   // keys are matched by votes: any key range in one pass
     pl.threads = kWave;
     return pl;
   }
+  // The LDS tables hold at most kAlignPassKeys (slot, expert) keys; more
+  // slots are taken in passes over slot ranges (each pass reads every pair
+  // and keeps those of its slots).
+  if (int64_t(L) * E > kAlignPassKeys) pl.pass_slots = std::max(1, kAlignPassKeys / E);
+  L = pl.pass_slots;
   const int64_t LE = int64_t(L) * E;
   const int64_t fixed = 2 * LE + L + 1 + 17 + numel;   // tot, off, sb, wtot, keys
   const int64_t wmax_single = (kLdsInts - fixed) / LE;
@@ -489,6 +495,29 @@ AlignPlan plan_align(int64_t numel, int E, int L, int B) {
   pl.lds_bytes = size_t(LE * 4);
   pl.ws_bytes = (int64_t(pl.ntiles) + 1) * LE * 4;   // tile counts, then key totals
   return pl;
+}
+
+// Active slots from num_tokens_post_padded (one wavefront): ascending, then -1.
+__global__ void __launch_bounds__(kWave) align_active_kernel(const int32_t* ntpp, int L,
+                                                             int32_t* lora_ids, int32_t* nact) {
+  const int lane = lane_id();
+  int run = 0;
+  for (int c0 = 0; c0 < L; c0 += kWave) {
+    const int l = c0 + lane;
+    const bool act = l < L && ntpp[l] > 0;
+    const uint64_t mk = __ballot(act);
+    if (act && lora_ids) lora_ids[run + __popcll(mk & lanes_below(lane))] = l;
+    run += __popcll(mk);
+  }
+  if (lora_ids)
+    for (int i = run + lane; i < L; i += kWave) lora_ids[i] = -1;
+  if (nact && lane == 0) *nact = run;
+}
+
+hipError_t launch_align_active(const int32_t* ntpp, int L, int32_t* lora_ids, int32_t* nact,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(align_active_kernel, dim3(1), dim3(kWave), 0, st, ntpp, L, lora_ids, nact);
+  return hipGetLastError();
 }
 
 hipError_t launch_align(const AlignPlan& pl, AlignParams a, hipStream_t st) {

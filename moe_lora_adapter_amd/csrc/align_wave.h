@@ -21,7 +21,7 @@ __device__ __forceinline__ void align_wave_body(const AlignParams& a) {
   const int lane = lane_id();
   int l = -1, e = -1;
   if (lane < a.numel) {  // both loads issued before either is used
-    l = a.mapping[lane / a.topk];
+    l = int(unsigned(a.mapping[lane / a.topk]) - unsigned(a.l0));
     e = a.topk_ids[lane];
   }
   const bool ok = (unsigned(l) < unsigned(a.L)) & (unsigned(e) < unsigned(a.E));

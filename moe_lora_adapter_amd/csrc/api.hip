@@ -16,7 +16,7 @@ namespace {
 
 constexpr int64_t kMaxE = 1024;
 constexpr int64_t kMaxL = 1024;
-constexpr int64_t kMaxLE = 8192;
+constexpr int64_t kMaxLE = int64_t(1) << 20;
 constexpr int64_t kMaxRank = 128;
 constexpr int64_t kInt32Max = 2147483647;
 
@@ -145,33 +145,42 @@ static int align_call(const int32_t* topk_ids, const int32_t* token_lora_mapping
   const AlignPlan plan = plan_align(numel, E, L, block_m);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return MOE_LORA_ERR_WORKSPACE;
-  AlignParams a{};
-  a.topk_ids = topk_ids;
-  a.mapping = token_lora_mapping;
-  a.sorted = sorted_token_ids;
-  a.eids = expert_ids;
-  a.ntpp = num_tokens_post_padded;
-  a.lora_ids = lora_ids;
-  a.nact = num_active_loras;
-  a.numel = int32_t(numel);
-  a.topk = topk;
-  a.E = E;
-  a.L = L;
-  a.LE = L * E;
-  a.B = block_m;
-  a.nbits = nbits_for(int64_t(L) * E);
-  a.cap = int32_t(cap);
-  a.nb = int32_t(cap / block_m);
-  a.W = plan.W;
-  a.seg = plan.seg;
-  a.ntiles = plan.ntiles;
-  if (!plan.single) {
-    int32_t* ws = static_cast<int32_t*>(workspace);
-    a.tile_cnt = ws;
-    a.key_tot = ws + int64_t(plan.ntiles) * a.LE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool passes = plan.pass_slots < L;  // slot ranges, one pass each
+  for (int32_t l0 = 0; l0 < L; l0 += plan.pass_slots) {
+    const int32_t Lp = std::min<int32_t>(plan.pass_slots, L - l0);
+    AlignParams a{};
+    a.topk_ids = topk_ids;
+    a.mapping = token_lora_mapping;
+    a.l0 = l0;
+    a.sorted = sorted_token_ids ? sorted_token_ids + int64_t(l0) * cap : nullptr;
+    a.eids = expert_ids ? expert_ids + int64_t(l0) * (cap / block_m) : nullptr;
+    a.ntpp = num_tokens_post_padded + l0;
+    a.lora_ids = passes ? nullptr : lora_ids;
+    a.nact = passes ? nullptr : num_active_loras;
+    a.numel = int32_t(numel);
+    a.topk = topk;
+    a.E = E;
+    a.L = Lp;
+    a.LE = Lp * E;
+    a.B = block_m;
+    a.nbits = nbits_for(int64_t(Lp) * E);
+    a.cap = int32_t(cap);
+    a.nb = int32_t(cap / block_m);
+    a.W = plan.W;
+    a.seg = plan.seg;
+    a.ntiles = plan.ntiles;
+    if (!plan.single && !plan.wave) {
+      int32_t* ws = static_cast<int32_t*>(workspace);
+      a.tile_cnt = ws;
+      a.key_tot = ws + int64_t(plan.ntiles) * a.LE;
+    }
+    if (launch_align(plan, a, st) != hipSuccess) return MOE_LORA_ERR_HIP;
   }
-  const hipError_t err = launch_align(plan, a, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP;
+  if (passes && (lora_ids || num_active_loras) &&
+      launch_align_active(num_tokens_post_padded, L, lora_ids, num_active_loras, st) != hipSuccess)
+    return MOE_LORA_ERR_HIP;
+  return MOE_LORA_OK;
 }
 
 extern "C" {

@@ -23,6 +23,8 @@ struct AlignParams {
   int32_t seg;     // single workgroup: pairs per wave; tiles: pairs per tile
   int32_t ntiles;  // workgroups of the tile kernels
   int32_t segw;    // tile scatter: pairs per wave (multiple of 64)
+  int32_t l0;      // first slot of this pass: slots [l0, l0 + L) of the call,
+                   // whose rows sorted / eids / ntpp point at
 };
 
 struct AlignPlan {
@@ -32,14 +34,22 @@ struct AlignPlan {
   int threads;       // block size of the single / tile count kernels
   size_t lds_bytes;  // dynamic LDS of the single / tile count kernels
   int64_t ws_bytes;  // device workspace (0 for the single path)
+  int pass_slots;    // slots per pass: the call's L, or fewer when L * E keys
+                     // exceed what the LDS tables of one pass hold
 };
 
 // The one-wavefront align (lane = pair, lane = slot) takes at most this many.
 constexpr int kAlignWaveMaxPairs = 64;
 constexpr int kAlignWaveMaxSlots = 64;
+// (slot, expert) keys one pass of the LDS-table align paths takes.
+constexpr int kAlignPassKeys = 8192;
 
 AlignPlan plan_align(int64_t numel, int E, int L, int B);
 hipError_t launch_align(const AlignPlan& plan, AlignParams a, hipStream_t st);
+// lora_ids / num_active from num_tokens_post_padded (after passes that
+// wrote them for slot ranges without those outputs).
+hipError_t launch_align_active(const int32_t* ntpp, int L, int32_t* lora_ids, int32_t* nact,
+                               hipStream_t st);
 
 // ---------------------------------------------------------------- fused
 struct FusedParams {

@@ -76,7 +76,6 @@ def align_call(**kw):
     (dict(L=0), mla.ERR_INVALID),
     (dict(E=1025), mla.ERR_UNSUPPORTED),
     (dict(L=1025, E=1), mla.ERR_UNSUPPORTED),
-    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
     (dict(B=8), mla.ERR_UNSUPPORTED),
     (dict(B=48), mla.ERR_UNSUPPORTED),
     (dict(M=2 ** 31, topk=1), mla.ERR_UNSUPPORTED),
@@ -105,7 +104,7 @@ def align_noalloc_call(**kw):
     (dict(M=-1), mla.ERR_INVALID),
     (dict(E=1025), mla.ERR_UNSUPPORTED),
     (dict(B=48), mla.ERR_UNSUPPORTED),
-    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
+    (dict(L=1025, E=1), mla.ERR_UNSUPPORTED),
 ])
 def test_align_noalloc_rejects(kw, status):
     assert align_noalloc_call(**kw) == status
@@ -117,8 +116,25 @@ def test_align_noalloc_scratch_covers_every_accepted_size():
     assert mla.ALIGN_NOALLOC_SCRATCH_BYTES == 8 * 1024 * 1024
     for M, topk, E, L, B in ((65536, 8, 256, 16, 64), (2 ** 22, 8, 1024, 8, 128),
                              (2 ** 20, 1, 1, 1024, 16), (10 ** 6, 1, 1024, 8, 16),
-                             (5000, 4, 2, 1, 16)):
+                             (5000, 4, 2, 1, 16), (8192, 8, 1024, 1024, 128),
+                             (65536, 8, 256, 64, 64)):
         assert mla.align_workspace_size(M, topk, E, L, B) <= mla.ALIGN_NOALLOC_SCRATCH_BYTES
+
+
+def test_align_takes_every_key_space_in_passes():
+    """Every L <= 1024 and E <= 1024 is accepted (up to 2^20 (slot, expert)
+    keys).  Key spaces beyond the 8192 keys of one pass's LDS tables are
+    aligned in passes over slot ranges, each sized like a call with that many
+    slots: the workspace of a call with L slots is that of a call with
+    8192 / E slots."""
+    ws = mla.align_workspace_size
+    assert ws(65536, 8, 256, 64, 64) == ws(65536, 8, 256, 32, 64)
+    assert ws(65536, 8, 1024, 1024, 64) == ws(65536, 8, 1024, 8, 64)
+    assert ws(8192, 8, 1024, 1024, 128) == ws(8192, 8, 1024, 8, 128)
+    # one pass up to 8192 keys: unchanged
+    assert ws(65536, 8, 256, 32, 64) == (128 + 1) * 8192 * 4   # 2^20 / 8192 tiles
+    # decode batches (at most 64 pairs and 64 slots) take the one-wavefront path at any E
+    assert ws(16, 4, 1024, 64, 16) == 0
 
 
 def fused_call(**kw):
@@ -218,7 +234,7 @@ def naive_call(**kw):
     (dict(topk=0), mla.ERR_INVALID),
     (dict(r=129), mla.ERR_UNSUPPORTED),
     (dict(E=1025), mla.ERR_UNSUPPORTED),
-    (dict(L=16, E=1024), mla.ERR_UNSUPPORTED),
+    (dict(L=1025, E=1), mla.ERR_UNSUPPORTED),
     # block sizes: powers of two from 1 to 128
     (dict(B=0), mla.ERR_UNSUPPORTED),
     (dict(B=3), mla.ERR_UNSUPPORTED),

@@ -88,6 +88,11 @@ NAIVE_EDGE = [
     # (L * E = 8192, the largest key space: 13-bit keys, a full hash table)
     dict(K=64, Ns=64, r=32, block_m=16, M=1024, E=1, topk=1, L=1, active=1, p_neg=0.0),
     dict(K=64, Ns=64, r=16, block_m=16, M=1024, E=1024, topk=1, L=8, active=8, p_neg=0.1),
+    # 2^20 and 65536 (slot, expert) keys: the align in passes over slot ranges,
+    # 20- and 16-bit keys in the grouping
+    # (K, Ns and r small: the weights of every slot are drawn, zero for inactive ones)
+    dict(K=8, Ns=8, r=2, block_m=16, M=256, E=1024, topk=2, L=1024, active=40, p_neg=0.1),
+    dict(K=8, Ns=16, r=4, block_m=16, M=128, E=1024, topk=4, L=64, active=64, p_neg=0.1),
     dict(K=64, Ns=64, r=64, block_m=1, M=256, E=64, topk=4, L=4, active=4, p_neg=0.1),
     # just past one wavefront of pairs, and a dense decode batch (MFMA by AUTO)
     dict(K=128, Ns=64, r=32, block_m=16, M=65, E=4, topk=1, L=2, active=2, p_neg=0.1),

@@ -65,16 +65,18 @@ def _random_align_case(rng):
     M = int(rng.choice([0, 1, 3, 64, 65, 1000, 4095, 4096, 4097, 9000, 20000]))
     topk = int(rng.integers(1, 9))
     E = int(rng.choice([1, 2, 7, 64, 129, 1024]))
-    L = int(rng.choice([1, 2, 5, 8]))
-    while L * E > 8192:
-        L //= 2
+    L = int(rng.choice([1, 2, 5, 8, 9, 64, 1024]))
     B = int(rng.choice([16, 32, 64, 128]))
+    # bounded output (L rows of capacity) for the oracle; past 8192 keys the
+    # library aligns in passes over slot ranges
+    while L > 1 and L * (M * topk + min(E, M * topk) * (B - 1)) > 1 << 23:
+        L //= 2
     topk_ids = rng.integers(-1, E + 1, size=(M, topk)).astype(np.int32)
     mapping = rng.integers(-2, L + 1, size=M).astype(np.int32)
     return topk_ids, mapping, E, L, B
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_align_edge_cases(orc, seed):
     rng = np.random.default_rng(100 + seed)
     topk_ids, mapping, E, L, B = _random_align_case(rng)
@@ -94,6 +96,35 @@ def test_align_max_experts_and_many_slots(orc):
         ref = orc.align(topk_ids, mapping, E, L, B)
         gpu = gh.align_to_host(gh.run_align(topk_ids, mapping, E, L, B))
         gh.assert_align_equal(gpu, ref, B)
+
+
+@pytest.mark.parametrize("M,topk,E,L,B,lo", [
+    (256, 8, 256, 64, 64, 0),      # 16384 keys: two passes of 32 slots (tile path)
+    (256, 8, 256, 64, 64, 40),     # every pair in the second pass's slots
+    (9000, 2, 100, 100, 32, 0),    # 10000 keys: passes of 81 and 19 slots
+    (512, 4, 1024, 1024, 16, 0),   # 2^20 keys: 128 passes of 8 slots
+    (512, 4, 1024, 1024, 16, 1000),
+    (0, 4, 1024, 64, 16, 0),       # no pairs: every slot empty, no active slot
+])
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_align_key_spaces_in_passes(orc, M, topk, E, L, B, lo, noalloc):
+    """Key spaces beyond one pass's 8192 (slot, expert) keys, up to 2^20:
+    bit-exact against the oracle, lora_ids and num_active_loras included,
+    through moe_lora_align and moe_lora_align_noalloc."""
+    rng = np.random.default_rng(M + 7 * L + lo)
+    topk_ids = rng.integers(-1, E + 1, size=(M, topk)).astype(np.int32)
+    topk_ids[::4] = rng.integers(0, max(1, E // 8), size=topk_ids[::4].shape)  # repeated keys
+    mapping = rng.integers(lo - 1, L + 1, size=M).astype(np.int32)
+    _log(f"align passes M={M} topk={topk} E={E} L={L} B={B} slots from {lo} noalloc={noalloc}")
+    ref = orc.align(topk_ids, mapping, E, L, B)
+    if noalloc:
+        import moe_lora_adapter_amd as mla
+        out = mla.alloc_align_output(M, topk, E, L, B, gh.DEV)
+        mla.moe_lora_align_noalloc(gh.i32_dev(topk_ids), gh.i32_dev(mapping), E, L, B, out=out)
+        torch.cuda.synchronize()
+    else:
+        out = gh.run_align(topk_ids, mapping, E, L, B)
+    gh.assert_align_equal(gh.align_to_host(out), ref, B)
 
 
 @pytest.mark.parametrize("M,topk,E,L,B", [
@@ -285,6 +316,10 @@ EDGE = [
     dict(K=328, Ns=88, r=32, block_m=64, M=24, E=2, topk=2, L=2, active=2),
     # ranks that are not a multiple of 16 / 32
     dict(K=320, Ns=96, r=96, block_m=32, M=64, E=2, topk=2, L=1, active=1, p_neg=0.0),
+    # key spaces beyond one align pass (8192 keys): 16384 and 2^20 (slot, expert) keys
+    # (K, Ns and r small: the weights of every slot are drawn, zero for inactive ones)
+    dict(K=64, Ns=64, r=16, block_m=16, M=96, E=1024, topk=4, L=16, active=12),
+    dict(K=8, Ns=8, r=2, block_m=32, M=40, E=1024, topk=2, L=1024, active=30),
     dict(K=128, Ns=48, r=120, block_m=64, M=100, E=2, topk=1, L=1, active=1, mul=True),
     dict(K=136, Ns=64, r=56, block_m=16, M=50, E=3, topk=2, L=2, active=2, x_per_pair=True),
     # K beyond what the decode stream kernel stages in LDS (4 rows x K):
