@@ -7,7 +7,9 @@
 // delta is added onto the base output.  This kernel is that addition:
 // y[i] = bf16(y[i] + delta[i]), the sum formed in fp32 and rounded to nearest
 // even once.  16-byte vector accesses, a grid-stride loop over the chunks and
-// an element loop for a tail shorter than eight values.
+// an element loop for a tail shorter than eight values.  Every byte is touched
+// once, so the chunk loads and stores are non-temporal (a cold 4096 x 12288
+// addition measured 56.1 us with the default policy, 49.3 us with this).
 #include <algorithm>
 
 #include "common.h"
@@ -17,14 +19,15 @@ namespace mlr {
 namespace {
 
 constexpr int kTA = 256;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(kTA) accumulate_kernel(uint16_t* __restrict__ y,
                                                          const uint16_t* __restrict__ d, int64_t n) {
   const int64_t chunks = n / 8;
   const int64_t stride = int64_t(gridDim.x) * kTA;
   for (int64_t c = int64_t(blockIdx.x) * kTA + threadIdx.x; c < chunks; c += stride) {
-    const uint4 yv = reinterpret_cast<const uint4*>(y)[c];
-    const uint4 dv = reinterpret_cast<const uint4*>(d)[c];
+    const u32x4_t yv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y) + c);
+    const u32x4_t dv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(d) + c);
     const uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w}, ds[4] = {dv.x, dv.y, dv.z, dv.w};
     uint32_t o[4];
 #pragma unroll
@@ -33,7 +36,8 @@ __global__ void __launch_bounds__(kTA) accumulate_kernel(uint16_t* __restrict__ 
       const float hi = bf16_hi(ys[i]) + bf16_hi(ds[i]);
       o[i] = pack_bf16x2(lo, hi);
     }
-    reinterpret_cast<uint4*>(y)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    const u32x4_t ov = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t*>(y) + c);
   }
   if (blockIdx.x == 0) {
     for (int64_t i = chunks * 8 + threadIdx.x; i < n; i += kTA)

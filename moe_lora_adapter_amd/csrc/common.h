@@ -165,15 +165,20 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
 }
+// Cache policy of a buffer access (the instruction's aux bits): 0 = default,
+// kNonTemporal = nt (evict-first, for data a kernel touches once).
+constexpr int kNonTemporal = 2;
+template <int AUX = 0>
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), AUX);
   return make_uint4(uint32_t(v.x), uint32_t(v.y), uint32_t(v.z), uint32_t(v.w));
 }
 
 // Stores past the range are dropped.
+template <int AUX = 0>
 __device__ __forceinline__ void buf_st16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const i32x4_t d = {int(v.x), int(v.y), int(v.z), int(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(d, r, int(voff), int(soff), 0);
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, int(voff), int(soff), AUX);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

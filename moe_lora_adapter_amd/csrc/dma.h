@@ -37,17 +37,30 @@ __device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
 // does not see an LDS store in flight; it would otherwise wait for every
 // outstanding stage before each LDS read.  The waits for these loads are the
 // explicit ones in stage_barrier.  M0 (the LDS base) is saved and restored.
+// NT: a non-temporal (evict-first) load, for bytes no other workgroup reads.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(i32x4_t r, uint32_t lds, uint32_t voff) {
   int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(r)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
 }
 
 // Wait until at most VM vector memory operations of this wavefront are

@@ -287,9 +287,12 @@ __device__ __forceinline__ void expand_load(const FusedParams& p, const PassCtx&
       r.b[i][ks] = buf_ld16(c.br, off, 0);
     }
   }
+  // Y is read once and written once: both accesses are non-temporal (loads
+  // and stores together measured 2-11 % faster on the prefill and dense
+  // shapes; either one alone, within 2 %)
   if (p.add) {
 #pragma unroll
-    for (int i = 0; i < X::YC; ++i) r.y[i] = buf_ld16(c.yr, ychunk_off(c, yc, i, nb), 0);
+    for (int i = 0; i < X::YC; ++i) r.y[i] = buf_ld16<kNonTemporal>(c.yr, ychunk_off(c, yc, i, nb), 0);
   }
 }
 
@@ -345,7 +348,7 @@ __device__ __forceinline__ void expand_store(const FusedParams& p, const PassCtx
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       ow[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-    buf_st16(make_uint4(ow[0], ow[1], ow[2], ow[3]), c.yr, ychunk_off(c, yc, i, nb), 0);
+    buf_st16<kNonTemporal>(make_uint4(ow[0], ow[1], ow[2], ow[3]), c.yr, ychunk_off(c, yc, i, nb), 0);
   }
 }
 
