@@ -66,12 +66,13 @@ constexpr int kMaxIds = 128;                // largest block_m
 constexpr int kMaxPeers = kXchPeers;       // most workgroups one K split spans
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
 
-// Ring depth: slots - 1 stages in flight per workgroup.  Three slots (32 KiB
-// in flight) measured fastest on MI355X: with 228 streaming workgroups,
-// deeper rings only add contention (20b-like decode a6: 3 slots 27.0 us,
-// 4 slots 27.3, 5 slots 28.4, 6 slots 29.3).
+// Ring depth: slots - 1 stages in flight per workgroup.  Four slots (48 KiB
+// in flight) measured fastest on MI355X with B non-temporal; deeper rings add
+// contention among the 228 streaming workgroups (20b-like decode a6, kernel
+// us with 3 / 4 / 5 / 6 slots: 22.5 / 22.2 / 23.1 / 23.8 one launch, 22.0 /
+// 21.5 / 22.3 / 23.0 sorted; w2 a6 18.1 / 17.6 / 19.0 / 19.8).
 #ifndef MLR_STREAM_SLOTS
-#define MLR_STREAM_SLOTS 3
+#define MLR_STREAM_SLOTS 4
 #endif
 constexpr int kSlots = MLR_STREAM_SLOTS;
 static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
@@ -306,6 +307,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // ring slots: kSlots, or with the K split a deeper ring that holds the B
   // stages loaded while the peers' partials are awaited
   constexpr int NS = XCH ? kSlotsXch<R>() : kSlots;
+  // slots the stream runs ahead through (with the K split, until the exchange)
+  constexpr int SA = NS < kSlots ? NS : kSlots;
   __shared__ __align__(16) uint8_t ring[NS * kStage];
   __shared__ __align__(16) uint8_t xs[kXBytes];
   __shared__ __align__(16) uint8_t ys[kYBytes];
@@ -529,9 +532,8 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
                                ? uint32_t(int64_t(pid) * p.N + 8 * c) * 2u : kOob;
       dma16(yr, ys_lds + q0 * 16, off);
     }
-    for (int t = g0 == 0 ? 1 : 0; t < kSlots - 1 && t < TA; ++t)
+    for (int t = g0 == 0 ? 1 : 0; t < SA - 1 && t < TA; ++t)
       issue_stage<R>(p, ar, br, t, nA, ka0, ncols, ring_lds + t * kStage);
-    static_assert(NS >= kSlots, "the first stages go to slots 0 .. kSlots - 2");
 
     // wavefront w: A rank tile rt and k-step ka of every A stage
     const int rt = w % G::RT, ka = w / G::RT;
@@ -548,13 +550,13 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       // (with the K split the A stages drain before the exchange)
       const int lim = t < nA ? TA : T;
       if constexpr (!XCH) {
-        wait_stage<kSlots - 2>(min(kSlots - 2, lim - 1 - t));
-        if (t + kSlots - 1 < lim)
-          issue_stage<R>(p, ar, br, t + kSlots - 1, nA, ka0, ncols,
-                         ring_lds + ((t + kSlots - 1) % kSlots) * kStage);
+        wait_stage<SA - 2>(min(SA - 2, lim - 1 - t));
+        if (t + SA - 1 < lim)
+          issue_stage<R>(p, ar, br, t + SA - 1, nA, ka0, ncols,
+                         ring_lds + ((t + SA - 1) % NS) * kStage);
       } else {
-        // stages issued ahead of t: kSlots - 1, or NS - 1 from the exchange on
-        const int ahead = (xch && t >= nA) ? NS - 1 : kSlots - 1;
+        // stages issued ahead of t: SA - 1, or NS - 1 from the exchange on
+        const int ahead = (xch && t >= nA) ? NS - 1 : SA - 1;
         wait_stage<NS - 2>(min(ahead - 1, lim - 1 - t));
         if (xch && t == nA && tid == 0) {
           // every read of the slot by this workgroup has returned (its values
