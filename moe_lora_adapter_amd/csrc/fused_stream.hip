@@ -60,8 +60,12 @@ constexpr int kStageChunks = kStage / 16;   // 1024
 constexpr int kIPS = kStageChunks / kST;    // DMA instructions per thread and stage
 static_assert(kIPS == 1, "a stage is one 16-byte chunk per thread");
 constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
+// Eight rows per pass where K allows (the K split keeps four: its exchange
+// slot holds four rows): a block of five to eight rows then streams its
+// weights once instead of twice.  X rows of such a pass: 8 * K * 2 bytes.
+constexpr int kRows8 = 8;
+constexpr int kXBytes8 = 49152;
 constexpr int kMaxCols = 2048;              // output columns per workgroup
-constexpr int kYBytes = kRows * kMaxCols * 2;
 constexpr int kMaxIds = 128;                // largest block_m
 constexpr int kMaxPeers = kXchPeers;       // most workgroups one K split spans
 constexpr int64_t kMaxBufBytes = int64_t(1) << 31;
@@ -84,6 +88,9 @@ static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
 template <int R>
 constexpr int kSlotsXch() { return R <= 64 ? 5 : 4; }
 
+#ifndef MLR_STREAM_ROWS8
+#define MLR_STREAM_ROWS8 1
+#endif
 #ifndef MLR_STREAM_MIN_COLS
 #define MLR_STREAM_MIN_COLS 256
 #endif
@@ -119,12 +126,13 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Lane i of every 16-lane row gets the value of lane i + kRows of the same
+// Lane i of every 16-lane row gets the value of lane i + ROWS of the same
 // row (DPP row shift left; lanes past the row's end get 0): a VALU lane move,
 // with no trip through the LDS crossbar.
+template <int ROWS>
 __device__ __forceinline__ float lane_plus_rows(float v) {
-  static_assert(kRows >= 1 && kRows <= 15, "DPP row shift distance");
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + kRows, 0xf, 0xf, true));
+  static_assert(ROWS >= 1 && ROWS <= 15, "DPP row shift distance");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + ROWS, 0xf, 0xf, true));
 }
 
 // Stage geometry for rank R (32, 64 or 128).
@@ -300,9 +308,12 @@ __device__ __forceinline__ void gather_partials(const FusedParams& p, const XchS
 // it keeps does not crowd the registers of the kernel without it (the
 // shared build spilled scalar registers into vector lanes on every stage:
 // +2 us on the 20b-like decode).
-template <int R, bool NAIVE, bool XCH>
+template <int R, bool NAIVE, bool XCH, int ROWS>
 __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   using G = Geo<R>;
+  static_assert(ROWS == kRows || (ROWS == kRows8 && !XCH), "rows per pass");
+  constexpr int XB = ROWS == kRows ? kXBytes : kXBytes8;  // X rows of a pass
+  constexpr int YB = ROWS * kMaxCols * 2;                 // the split's Y values of a pass
   constexpr int VP = 32 * G::KS + 8;  // bf16 pitch of the v rows
   // ring slots: kSlots, or with the K split a deeper ring that holds the B
   // stages loaded while the peers' partials are awaited
@@ -310,24 +321,24 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // slots the stream runs ahead through (with the K split, until the exchange)
   constexpr int SA = NS < kSlots ? NS : kSlots;
   __shared__ __align__(16) uint8_t ring[NS * kStage];
-  __shared__ __align__(16) uint8_t xs[kXBytes];
-  __shared__ __align__(16) uint8_t ys[kYBytes];
-  __shared__ __align__(16) uint16_t s_vb[kRows * VP];  // v, bf16 high part
-  __shared__ __align__(16) uint16_t s_vl[kRows * VP];  // v, bf16 low part
-  __shared__ int s_pair[kRows];
-  __shared__ int s_row[kRows];
-  __shared__ float s_w[kRows];
+  __shared__ __align__(16) uint8_t xs[XB];
+  __shared__ __align__(16) uint8_t ys[YB];
+  __shared__ __align__(16) uint16_t s_vb[ROWS * VP];  // v, bf16 high part
+  __shared__ __align__(16) uint16_t s_vl[ROWS * VP];  // v, bf16 low part
+  __shared__ int s_pair[ROWS];
+  __shared__ int s_row[ROWS];
+  __shared__ float s_w[ROWS];
   __shared__ int s_ids[NAIVE ? kMaxIds : 1];  // pair ids of the block (align-free path)
   __shared__ uint2 s_dummy[kWave];            // stores of lanes with no output
   __shared__ __align__(16) float s_part[XCH ? kST * 4 : 4];  // k-step partials (K split)
-  static_assert(kST * 4 * 4 <= kXBytes, "k-step partials fit the X buffer");
+  static_assert(kST * 4 * 4 <= XB, "k-step partials fit the X buffer");
   __shared__ int s_miss;                      // K split: peers whose partial did not arrive
-  __shared__ float s_peer[XCH ? kMaxPeers * kRows * R : 1];  // K split: the peers' partials
+  __shared__ float s_peer[XCH ? kMaxPeers * ROWS * R : 1];  // K split: the peers' partials
   __shared__ uint32_t s_tag;                  // K split: this call's tag in the pass's slot
   __shared__ __align__(16) uint32_t s_left[XCH ? kXchPeers : 1];  // K split: the slot's left words
   __shared__ int s_grp1[4];                   // one-wavefront grouping: blocks, slot, expert,
                                               // valid rows of the first pass
-  static_assert(2 * kRows <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
+  static_assert(2 * ROWS <= 16, "V_hi and V_lo share the 16 columns of one MFMA operand");
   static_assert(sizeof(GroupLds) <= sizeof(ring), "the grouping tables borrow the ring");
 
   // units = (block, slice); split count: a compute unit per working
@@ -377,22 +388,22 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   const int32_t* srow = nullptr;
   int id0 = p.numel;
   // The block's pair ids of the first pass -> the pass's rows, written to LDS
-  // (lanes < kRows of the calling wavefront); returns the valid rows.
+  // (lanes < ROWS of the calling wavefront); returns the valid rows.
   auto first_rows = [&](int id) {
     const int lane = lane_id();
     int pid = p.numel, xrow = -1;
     float wv = 1.f;
-    if (lane < kRows && lane < p.B && id < p.numel) {
+    if (lane < ROWS && lane < p.B && id < p.numel) {
       pid = id;
       xrow = p.x_per_pair ? id : id / p.topk;
       if (p.mul) wv = p.w[id];
     }
-    if (lane < kRows) {
+    if (lane < ROWS) {
       s_pair[lane] = pid;
       s_row[lane] = xrow;
       s_w[lane] = wv;
     }
-    return __popcll(__ballot(lane < kRows && xrow >= 0));
+    return __popcll(__ballot(lane < ROWS && xrow >= 0));
   };
   if constexpr (NAIVE) {
     if (rows_first) {
@@ -400,7 +411,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
         group_block_wave(p, pg, g, s_ids, l, e);
         // the first pass's rows too, so that one barrier publishes both
         const int lane = lane_id();
-        const int nr0 = first_rows(lane < kRows && lane < p.B ? s_ids[lane] : p.numel);
+        const int nr0 = first_rows(lane < ROWS && lane < p.B ? s_ids[lane] : p.numel);
         if (lane == 0) {
           s_grp1[1] = l;
           s_grp1[2] = e;
@@ -421,7 +432,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       find_block(p, sc, g, l, b);
       srow = p.sorted + l * p.cap + b * p.B;
       const int lane = lane_id();
-      const int id = (lane < kRows && lane < p.B) ? srow[lane] : p.numel;
+      const int id = (lane < ROWS && lane < p.B) ? srow[lane] : p.numel;
       e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
       const int nr0 = first_rows(id);
       if (lane == 0) {
@@ -438,7 +449,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     find_block(p, sc, g, l, b);
     // the first pass's pair ids are loaded before the expert id is waited for
     srow = p.sorted + l * p.cap + b * p.B;
-    id0 = (threadIdx.x < kRows && int(threadIdx.x) < p.B) ? srow[threadIdx.x] : p.numel;
+    id0 = (threadIdx.x < ROWS && int(threadIdx.x) < p.B) ? srow[threadIdx.x] : p.numel;
     e = __builtin_amdgcn_readfirstlane(p.eids[l * p.nb + b]);
   }
   const int64_t wsel = (int64_t(s) * p.L + l) * p.E + e;
@@ -476,9 +487,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
   // exactly one stage issued after the one it waits for.
   if (TA > 0) issue_stage<R>(p, ar, br, 0, nA, ka0, ncols, ring_lds);
 
-  for (int g0 = 0; g0 < p.B; g0 += kRows) {
+  for (int g0 = 0; g0 < p.B; g0 += ROWS) {
     // K split: the pass's slot
-    const XchSlot xs_slot = xch ? xch_slot(p.xch, p.xch_nslot, unit * p.xch_passes + g0 / kRows) : XchSlot{};
+    const XchSlot xs_slot = xch ? xch_slot(p.xch, p.xch_nslot, unit * p.xch_passes + g0 / ROWS) : XchSlot{};
     // K split: the slot's `left` words go to LDS by a direct load issued now
     // (two lanes of wavefront 0, after the pass's first stage): no register
     // holds them and nothing waits for them before the exchange, which reads
@@ -488,7 +499,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       dma16(lr4, lds_address(s_left), uint32_t(16 * lane));
     }
     const bool rows_set = rows_first && g0 == 0;  // set with the block, before its barrier
-    if (!rows_set && tid < kRows) {
+    if (!rows_set && tid < ROWS) {
       int pid = p.numel, xrow = -1;
       float wv = 1.f;
       if (g0 + tid < p.B) {
@@ -503,11 +514,11 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       s_row[tid] = xrow;
       s_w[tid] = wv;
     }
-    for (int i = tid; i < kRows * VP; i += kST) s_vb[i] = s_vl[i] = 0;
+    for (int i = tid; i < ROWS * VP; i += kST) s_vb[i] = s_vl[i] = 0;
     // valid rows are a prefix of the block (sentinels only pad a group's end)
     const int nr = rows_set ? __builtin_amdgcn_readfirstlane(s_grp1[3])
                             : __builtin_amdgcn_readfirstlane(
-                                  __syncthreads_count(tid < kRows && s_row[tid] >= 0));
+                                  __syncthreads_count(tid < ROWS && s_row[tid] >= 0));
     if (nr == 0) {  // (a block's first pass always has a row: only later passes end here)
       stage_barrier<0>();
       break;
@@ -519,16 +530,19 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     // of 64 chunks, so a last partial instruction still fits).  (Loading Y
     // after the first stage instead, since the expand is the first to need
     // it, measured 4 us slower on the 20b-like decode.)
-    for (int q0 = w * kWave; q0 < kRows * K8; q0 += kST) {
+    // Only the pass's nr valid rows are staged.  The rows past them keep what
+    // the buffers held: each row of the products depends on its own X row
+    // and v row only, and rows past nr are never stored.
+    for (int q0 = w * kWave; q0 < nr * K8; q0 += kST) {
       const int q = q0 + lane, i = q / K8, c = q % K8;
-      const int xrow = i < kRows ? s_row[i] : -1;
-      const uint32_t off = (q < kRows * K8 && xrow >= 0) ? uint32_t(xrow * p.K + 8 * c) * 2u : kOob;
+      const int xrow = i < ROWS ? s_row[i] : -1;
+      const uint32_t off = (q < nr * K8 && xrow >= 0) ? uint32_t(xrow * p.K + 8 * c) * 2u : kOob;
       dma16(xr, xs_lds + q0 * 16, off);
     }
-    for (int q0 = w * kWave; q0 < kRows * c8; q0 += kST) {
+    for (int q0 = w * kWave; q0 < nr * c8; q0 += kST) {
       const int q = q0 + lane, i = q / c8, c = q % c8;
-      const int pid = i < kRows ? s_pair[i] : p.numel;
-      const uint32_t off = (q < kRows * c8 && p.add && pid < p.numel)
+      const int pid = i < ROWS ? s_pair[i] : p.numel;
+      const uint32_t off = (q < nr * c8 && p.add && pid < p.numel)
                                ? uint32_t(int64_t(pid) * p.N + 8 * c) * 2u : kOob;
       dma16(yr, ys_lds + q0 * 16, off);
     }
@@ -541,7 +555,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
     uint4 vop[G::KS];
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) vop[ks] = zero4;
-    const float wrow = lr < kRows ? s_w[lr] : 0.f;
+    const float wrow = lr < ROWS ? s_w[lr] : 0.f;
 
     // stage t's wait and the next stage's issue (the ring's step)
     auto ring_step = [&](int t) {
@@ -576,12 +590,12 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       const int xc = (ka0 + t) * (G::KT / 8) + c;
       // one 16-byte read at a clamped index, then the select (a read
       // guarded by the condition became four masked 4-byte reads)
-      const uint4 xv = reinterpret_cast<const uint4*>(xs)[min(lr, kRows - 1) * K8 + min(xc, K8 - 1)];
-      const uint4 x = (lr < kRows && xc < K8) ? xv : zero4;
+      const uint4 xv = reinterpret_cast<const uint4*>(xs)[min(lr, ROWS - 1) * K8 + min(xc, K8 - 1)];
+      const uint4 x = (lr < ROWS && xc < K8) ? xv : zero4;
       acc = mfma16(a, x, acc);
     }
     {
-      // the A stages are multiplied: v for rows < kRows into s_vb / s_vl
+      // the A stages are multiplied: v for rows < ROWS into s_vb / s_vl
       // (the k-step partials go through the X buffer, which only the K
       // split's fallback still reads)
       if (xch && tid == 0) {
@@ -603,7 +617,7 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
         gather_partials<R>(p, xs_slot, acc, s_part, s_peer, &s_miss, xs, a_rsrc, split, C, nA_all, tag);
       }
       // lane (lr, lq) of wavefront w < RT holds v[row lr][16 w + 4 lq + i]
-      if (w < G::RT && lr < kRows) {
+      if (w < G::RT && lr < ROWS) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint16_t hi = f32_to_bf16(acc[i]);
@@ -620,14 +634,14 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
       const uint4* st = reinterpret_cast<const uint4*>(ring + (t % NS) * kStage);
       const int u = t - nA;
       if (u == 0) {
-        // operand column lr: V_hi of row lr (lr < kRows), V_lo of row
-        // lr - kRows (kRows <= lr < 2 kRows), else zero
+        // operand column lr: V_hi of row lr (lr < ROWS), V_lo of row
+        // lr - ROWS (ROWS <= lr < 2 ROWS), else zero
 #pragma unroll
         for (int ks = 0; ks < G::KS; ++ks) {
-          const int row = lr < kRows ? lr : (lr < 2 * kRows ? lr - kRows : 0);
-          const uint16_t* src = lr < kRows ? s_vb : s_vl;
+          const int row = lr < ROWS ? lr : (lr < 2 * ROWS ? lr - ROWS : 0);
+          const uint16_t* src = lr < ROWS ? s_vb : s_vl;
           const uint4 vv = *reinterpret_cast<const uint4*>(src + row * VP + 32 * ks + 8 * lq);
-          vop[ks] = lr < 2 * kRows ? vv : zero4;
+          vop[ks] = lr < 2 * ROWS ? vv : zero4;
         }
       }
       for (int ct = w; ct < G::CT; ct += kST / kWave) {
@@ -648,9 +662,9 @@ __global__ void __launch_bounds__(kST) fused_stream_kernel(FusedParams p) {
           const uint4 bb = jc < G::CPR ? st[col * G::CPR + (jc ^ (col & (G::SW - 1)))] : zero4;
           dt = mfma16(bb, vop[ks], dt);
         }
-        // lane (lr, lq) adds the V_lo product of its row, held kRows lanes up
+        // lane (lr, lq) adds the V_lo product of its row, held ROWS lanes up
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dt[i] += lane_plus_rows(dt[i]);
+        for (int i = 0; i < 4; ++i) dt[i] += lane_plus_rows<ROWS>(dt[i]);
         // every lane forms and stores its result -- lanes with nothing to
         // write into a dummy LDS slot -- so no branch exists that the Y read
         // and the arithmetic could be sunk into (below the products)
@@ -693,11 +707,15 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t need = (p.Ns + kMaxCols - 1) / kMaxCols;
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
   const dim3 grid(unsigned(kXcds * slots));
+  // eight rows per pass where the X rows fit (not with the K split)
+  const bool rows8 = MLR_STREAM_ROWS8 && !p.xch && int64_t(kRows8) * p.K * 2 <= kXBytes8;
 #define MLR_STREAM_CASE(R_)                                                                  \
   case R_:                                                                                   \
-    if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false>), grid, dim3(kST), 0, st, p); \
-    else if (p.xch) hipLaunchKernelGGL((fused_stream_kernel<R_, false, true>), grid, dim3(kST), 0, st, p); \
-    else hipLaunchKernelGGL((fused_stream_kernel<R_, false, false>), grid, dim3(kST), 0, st, p);       \
+    if (p.xch) hipLaunchKernelGGL((fused_stream_kernel<R_, false, true, kRows>), grid, dim3(kST), 0, st, p); \
+    else if (p.naive && rows8) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false, kRows8>), grid, dim3(kST), 0, st, p); \
+    else if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false, kRows>), grid, dim3(kST), 0, st, p); \
+    else if (rows8) hipLaunchKernelGGL((fused_stream_kernel<R_, false, false, kRows8>), grid, dim3(kST), 0, st, p); \
+    else hipLaunchKernelGGL((fused_stream_kernel<R_, false, false, kRows>), grid, dim3(kST), 0, st, p); \
     break;
   switch (p.r) {
     MLR_STREAM_CASE(32)
