@@ -1,7 +1,7 @@
 // Fused shrink + expand for decode-sized blocks as one continuous stream.
 //
 // One 1024-thread workgroup handles one (block, slice, column split) and up
-// to four rows at a time.  Its whole weight traffic -- the A matrix (r x K),
+// to ROWS rows at a time (8, or 4 with the K split or K > 3072).  Its whole weight traffic -- the A matrix (r x K),
 // then the split's B columns (cols x r) -- flows through one ring of LDS
 // slots filled by direct-to-LDS buffer loads, 16 KiB per stage, NS - 1 stages
 // in flight.  The B stages start loading while the last A stages are being
@@ -12,18 +12,20 @@
 // same loop with v_dot2 products was bound by their issue).
 //
 //   before the ring  X rows (rows x K) and the Y values of the split
-//                    (rows x cols) are loaded into LDS the same way.
+//                    (rows x cols) are loaded into LDS the same way, only
+//                    the pass's valid rows.
 //   A stage          K range [t KT, (t+1) KT) of all r rows: 16 (rank tile,
 //                    k-step) products, one per wavefront, V^T[16 ranks x 16
-//                    rows] += A[16 x 32] X^T[32 x 16] (rows >= 4 are zero).
+//                    rows] += A[16 x 32] X^T[32 x 16] (rows >= ROWS zero;
+//                    valid rows < row < ROWS stale and never stored).
 //   after A          the k-step partials of each rank tile are added through
 //                    LDS and v goes to LDS as two bf16 parts, v = hi + lo
 //                    (hi = bf16(v), lo = bf16(v - hi)); never to memory.
 //   B stage          NCS consecutive columns of B: D^T[16 cols x 16 cols'] =
 //                    B[16 x 32 ranks] W^T, where the 16 MFMA columns of W
-//                    carry V_hi of the pass rows in columns 0..3 and V_lo of
-//                    the same rows in columns 4..7 (the rest zero).  Adding
-//                    column i + 4 of the result onto column i (one lane
+//                    carry V_hi of the pass rows in columns 0..ROWS-1 and
+//                    V_lo of the same rows in columns ROWS..2 ROWS-1.  Adding
+//                    column i + ROWS of the result onto column i (one lane
 //                    shuffle) gives B (V_hi + V_lo)^T: v enters with about 16
 //                    significant bits instead of bf16's 8, at no extra MFMA.
 //                    A lane then ends with four
@@ -59,7 +61,7 @@ constexpr int kStage = 16384;               // bytes per ring stage
 constexpr int kStageChunks = kStage / 16;   // 1024
 constexpr int kIPS = kStageChunks / kST;    // DMA instructions per thread and stage
 static_assert(kIPS == 1, "a stage is one 16-byte chunk per thread");
-constexpr int kXBytes = 32768;              // X rows of a pass: kRows * K * 2
+constexpr int kXBytes = 32768;              // X rows of a four-row pass: kRows * K * 2
 // Eight rows per pass where K allows (the K split keeps four: its exchange
 // slot holds four rows): a block of five to eight rows then streams its
 // weights once instead of twice.  X rows of such a pass: 8 * K * 2 bytes.
