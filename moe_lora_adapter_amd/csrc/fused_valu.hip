@@ -71,7 +71,8 @@ namespace valu512 {
 
 // r = 16 stays here: the stream has few stages per workgroup and the
 // register-batch kernel was measured faster (gpt-oss-120b-like decode w13
-// 12.4 vs 13.4 us); from r = 32 on the stream kernel is (20b-like a2..a4:
+// 12.4 vs 13.4 us; re-measured later, 7.5 vs 13.3 one launch and 7.2 vs
+// 12.7 sorted); from r = 32 on the stream kernel is (20b-like a2..a4:
 // 27.8 vs 33.8 us).  stream_supported() admits r in {32, 64, 128}.
 bool valu_takes_stream(int64_t M, int64_t numel, int64_t K, int64_t N, int r, int x_per_pair) {
   return MLR_VALU_STREAM && stream_supported(M, numel, K, N, r, x_per_pair);
