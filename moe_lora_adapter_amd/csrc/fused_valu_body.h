@@ -458,7 +458,12 @@ __global__ void __launch_bounds__(kThreads, MLR_VALU_OCC * kThreads / 256) fused
   const uint16_t* A = p.a + wsel * p.r * p.K;
   const uint16_t* Bm = p.b + wsel * p.Ns * p.r;
 
-  if (nv <= 2)
+  // one-row blocks (most of a decode batch's) get their own instantiation:
+  // a two-row group would repeat the row's loads and products (120b-like
+  // decode, kernel us: w13 7.5 -> 7.3, w2 7.5 -> 6.8 one launch)
+  if (nv <= 1)
+    valu_rows<1, JW, CPR>(p, A, Bm, s_row, s_pair, nv, sh, s_part, s_v, s_d, s, n0, n1);
+  else if (nv <= 2)
     valu_rows<2, JW, CPR>(p, A, Bm, s_row, s_pair, nv, sh, s_part, s_v, s_d, s, n0, n1);
   else
     valu_rows<4, JW, CPR>(p, A, Bm, s_row, s_pair, nv, sh, s_part, s_v, s_d, s, n0, n1);
