@@ -1,7 +1,8 @@
 // Fused shrink + expand for decode-sized blocks as one continuous stream.
 //
 // One 1024-thread workgroup handles one (block, slice, column split) and up
-// to ROWS rows at a time (8, or 4 with the K split or K > 3072).  Its whole weight traffic -- the A matrix (r x K),
+// to ROWS rows at a time (4; 8 as a build option where K <= 3072, not with
+// the K split).  Its whole weight traffic -- the A matrix (r x K),
 // then the split's B columns (cols x r) -- flows through one ring of LDS
 // slots filled by direct-to-LDS buffer loads, 16 KiB per stage, NS - 1 stages
 // in flight.  The B stages start loading while the last A stages are being
@@ -62,9 +63,10 @@ constexpr int kStageChunks = kStage / 16;   // 1024
 constexpr int kIPS = kStageChunks / kST;    // DMA instructions per thread and stage
 static_assert(kIPS == 1, "a stage is one 16-byte chunk per thread");
 constexpr int kXBytes = 32768;              // X rows of a four-row pass: kRows * K * 2
-// Eight rows per pass where K allows (the K split keeps four: its exchange
-// slot holds four rows): a block of five to eight rows then streams its
-// weights once instead of twice.  X rows of such a pass: 8 * K * 2 bytes.
+// Eight rows per pass (MLR_STREAM_ROWS8) where K allows (the K split keeps
+// four: its exchange slot holds four rows): a block of five to eight rows
+// then streams its weights once instead of twice.  X rows of such a pass:
+// 8 * K * 2 bytes.
 constexpr int kRows8 = 8;
 constexpr int kXBytes8 = 49152;
 constexpr int kMaxCols = 2048;              // output columns per workgroup
@@ -90,8 +92,12 @@ static_assert(kSlots >= 3 && kSlots <= 8, "ring slots");
 template <int R>
 constexpr int kSlotsXch() { return R <= 64 ? 5 : 4; }
 
+// Eight rows per pass (build option, off by default): it removes the second
+// pass of blocks with five to eight rows and measured faster alone, but a
+// captured dual-stream layer whose base branch (base align, then the base
+// GEMM) ran beside the LoRA branch took 880 instead of 520 us with it.
 #ifndef MLR_STREAM_ROWS8
-#define MLR_STREAM_ROWS8 1
+#define MLR_STREAM_ROWS8 0
 #endif
 #ifndef MLR_STREAM_MIN_COLS
 #define MLR_STREAM_MIN_COLS 256
@@ -710,7 +716,9 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
   const int64_t slots = std::max<int64_t>(per_xcd * need, p.xcd_cus);
   const dim3 grid(unsigned(kXcds * slots));
   // eight rows per pass where the X rows fit (not with the K split)
-  const bool rows8 = MLR_STREAM_ROWS8 && !p.xch && int64_t(kRows8) * p.K * 2 <= kXBytes8;
+#if MLR_STREAM_ROWS8
+  // eight rows per pass where the X rows fit (not with the K split)
+  const bool rows8 = !p.xch && int64_t(kRows8) * p.K * 2 <= kXBytes8;
 #define MLR_STREAM_CASE(R_)                                                                  \
   case R_:                                                                                   \
     if (p.xch) hipLaunchKernelGGL((fused_stream_kernel<R_, false, true, kRows>), grid, dim3(kST), 0, st, p); \
@@ -719,6 +727,14 @@ hipError_t launch_fused_stream(FusedParams p, hipStream_t st) {
     else if (rows8) hipLaunchKernelGGL((fused_stream_kernel<R_, false, false, kRows8>), grid, dim3(kST), 0, st, p); \
     else hipLaunchKernelGGL((fused_stream_kernel<R_, false, false, kRows>), grid, dim3(kST), 0, st, p); \
     break;
+#else
+#define MLR_STREAM_CASE(R_)                                                                  \
+  case R_:                                                                                   \
+    if (p.xch) hipLaunchKernelGGL((fused_stream_kernel<R_, false, true, kRows>), grid, dim3(kST), 0, st, p); \
+    else if (p.naive) hipLaunchKernelGGL((fused_stream_kernel<R_, true, false, kRows>), grid, dim3(kST), 0, st, p); \
+    else hipLaunchKernelGGL((fused_stream_kernel<R_, false, false, kRows>), grid, dim3(kST), 0, st, p); \
+    break;
+#endif
   switch (p.r) {
     MLR_STREAM_CASE(32)
     MLR_STREAM_CASE(64)
