@@ -90,7 +90,7 @@ NAIVE_EDGE = [
     dict(K=64, Ns=64, r=16, block_m=16, M=1024, E=1024, topk=1, L=8, active=8, p_neg=0.1),
     # 2^20 and 65536 (slot, expert) keys: the align in passes over slot ranges,
     # 20- and 16-bit keys in the grouping
-    # eight rows per pass at the largest K that allows it, 17- and 21-row groups
+    # K = 3072 (the eight-row build option's largest), 17- and 21-row groups
     dict(K=3072, Ns=520, r=64, block_m=16, M=38, E=2, topk=1, L=1, active=1, p_neg=0.0),
     # (K, Ns and r small: the weights of every slot are drawn, zero for inactive ones)
     dict(K=8, Ns=8, r=2, block_m=16, M=256, E=1024, topk=2, L=1024, active=40, p_neg=0.1),

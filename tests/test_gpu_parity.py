@@ -329,10 +329,10 @@ EDGE = [
     # 128, and enough units that the split count is the fewest that keep a
     # workgroup's columns within its Y buffer (4096 columns: two of 2048)
     dict(K=4096, Ns=4096, S=2, r=128, block_m=16, M=160, E=16, topk=4, L=2, active=2),
-    # the stream kernel's largest blocks: 128 rows in 16 passes of 8
+    # the stream kernel's largest blocks: 128 rows in 32 passes of 4
     dict(K=1024, Ns=1024, r=64, block_m=128, M=200, E=2, topk=1, L=1, active=1, p_neg=0.0),
-    # eight rows per pass up to K = 3072 (its X rows fill the buffer), four beyond;
-    # full 16-row blocks and tail blocks of 1 and 5 rows in both
+    # around K = 3072, the largest K of the eight-row build option; full 16-row
+    # blocks and tail blocks of 1 and 5 rows (several passes per block)
     dict(K=3072, Ns=520, r=64, block_m=16, M=38, E=2, topk=1, L=1, active=1, p_neg=0.0),
     dict(K=3080, Ns=520, r=32, block_m=16, M=38, E=2, topk=1, L=1, active=1, p_neg=0.0),
     # the block lookup on either side of 64 slots (one wavefront up to 64,
