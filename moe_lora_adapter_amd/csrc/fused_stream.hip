@@ -93,9 +93,9 @@ template <int R>
 constexpr int kSlotsXch() { return R <= 64 ? 5 : 4; }
 
 // Eight rows per pass (build option, off by default): it removes the second
-// pass of blocks with five to eight rows and measured faster alone, but a
-// captured dual-stream layer whose base branch (base align, then the base
-// GEMM) ran beside the LoRA branch took 880 instead of 520 us with it.
+// pass of blocks with five to eight rows, but gained nothing clear on the
+// default decode step and made a captured dual-stream decode layer slower
+// (421 against 409 us; 880 against 520 with the LoRA side enqueued first).
 #ifndef MLR_STREAM_ROWS8
 #define MLR_STREAM_ROWS8 0
 #endif
